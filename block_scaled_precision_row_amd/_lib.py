@@ -1,0 +1,198 @@
+"""Thin ctypes binding of libbsq.so, with the C entry points' names.
+
+Two layers:
+  * ``lib`` -- the loaded library with argument / return types declared for
+    every symbol of include/bsq.h (raw pointers and sizes);
+  * functions named like the C entry points that take torch tensors, check
+    dtype / shape / device, allocate outputs and workspaces with torch when
+    the caller passes none, and call the library on the current stream.
+No arithmetic of the method happens here. Importing this module raises if
+the library has not been built (there is no fallback path).
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsq.so")
+
+BSQ_FMT_FP8R = 1
+BSQ_FMT_NVFP4 = 2
+BSQ_WEIGHT_ONLY = 0x1
+
+STATUS = {0: "BSQ_OK", 1: "BSQ_ERR_NULL", 2: "BSQ_ERR_SHAPE", 3: "BSQ_ERR_ALIGN", 4: "BSQ_ERR_WORKSPACE",
+          5: "BSQ_ERR_DEVICE", 6: "BSQ_ERR_HIP", 7: "BSQ_ERR_ARG"}
+
+_p, _i64, _u32, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_int
+
+# symbol -> (restype, argtypes); mirrors include/bsq.h
+SIGNATURES = {
+    "bsq_abi_version": (_int, []),
+    "bsq_status_string": (ctypes.c_char_p, [_int]),
+    "bsq_last_hip_error": (ctypes.c_char_p, []),
+    "bsq_quantize_act_fp8r": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
+    "bsq_quantize_act_nvfp4": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "bsq_calibrate_workspace_bytes": (_sz, [_i64, _i64]),
+    "bsq_calibrate_global_scale": (_int, [_p, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "bsq_gemm_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _u32]),
+    "bsq_gemm_fp8r": (_int, [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz, _p]),
+    "bsq_gemm_nvfp4": (_int, [_p, _i64, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz, _p]),
+    "bsq_dequant_to_bf16": (_int, [_int, _p, _p, _p, _i64, _i64, _p, _p]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbsq.so is not built at %s; run `python -m block_scaled_precision_row_amd.build`"
+                          % LIB_PATH)
+    so = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(so, name)
+        fn.restype = res
+        fn.argtypes = args
+    return so
+
+
+lib = _load()
+
+
+class BsqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = "%s returned %s (%s)" % (fn, STATUS.get(status, status), lib.bsq_status_string(status).decode())
+        if status == 6:
+            msg += ": " + lib.bsq_last_hip_error().decode()
+        super().__init__(msg)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise BsqError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _rows(x, dtype, name):
+    if x.dtype != dtype or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("%s must be a 2-D %s tensor on the GPU" % (name, dtype))
+    if x.stride(1) != 1:
+        raise ValueError("%s must have unit stride along its last dimension" % name)
+    return x.shape[0], x.shape[1], (x.stride(0) if x.shape[0] > 1 else x.shape[1])
+
+
+def _dense(x, dtype, shape, name):
+    if x.dtype != dtype or tuple(x.shape) != tuple(shape) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on the GPU" % (name, dtype, tuple(shape)))
+
+
+def _scalar(t, name):
+    if t is None:
+        return None
+    _dense(t, torch.float32, (1,), name)
+    return t
+
+
+# ---- entry points -------------------------------------------------------------
+
+def bsq_quantize_act_fp8r(x, xq=None, x_scale=None):
+    """bf16 x [M, K] -> (E4M3 codes uint8 [M, K], fp32 row scales [M])."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device) if xq is None else xq
+    x_scale = torch.empty((M,), dtype=torch.float32, device=x.device) if x_scale is None else x_scale
+    _dense(xq, torch.uint8, (M, K), "xq")
+    _dense(x_scale, torch.float32, (M,), "x_scale")
+    _check("bsq_quantize_act_fp8r", lib.bsq_quantize_act_fp8r(_ptr(x), M, K, ldx, _ptr(xq), _ptr(x_scale), _stream()))
+    return xq, x_scale
+
+
+def bsq_quantize_act_nvfp4(x, global_scale, xq=None, x_bscale=None):
+    """bf16 x [M, K], fp32 global scale [1] -> (packed E2M1 uint8 [M, K/2], E4M3 block scales uint8 [M, K/16])."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    _scalar(global_scale, "global_scale")
+    xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device) if xq is None else xq
+    x_bscale = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device) if x_bscale is None else x_bscale
+    _dense(xq, torch.uint8, (M, K // 2), "xq")
+    _dense(x_bscale, torch.uint8, (M, K // 16), "x_bscale")
+    _check("bsq_quantize_act_nvfp4", lib.bsq_quantize_act_nvfp4(_ptr(x), M, K, ldx, _ptr(global_scale), _ptr(xq),
+                                                                _ptr(x_bscale), _stream()))
+    return xq, x_bscale
+
+
+def bsq_calibrate_global_scale(x, out=None, workspace=None):
+    """bf16 x [M, K] -> fp32 [1] holding amax(x) / 2688 (1.0 for an all-zero x)."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    out = torch.empty((1,), dtype=torch.float32, device=x.device) if out is None else out
+    _scalar(out, "out")
+    nbytes = lib.bsq_calibrate_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=x.device)
+    _check("bsq_calibrate_global_scale", lib.bsq_calibrate_global_scale(
+        _ptr(x), M, K, ldx, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def bsq_gemm_workspace_bytes(fmt, M, N, K, flags=0):
+    return lib.bsq_gemm_workspace_bytes(fmt, M, N, K, flags)
+
+
+def _workspace(fmt, M, N, K, flags, workspace, device):
+    nbytes = lib.bsq_gemm_workspace_bytes(fmt, M, N, K, flags)
+    if workspace is None and nbytes:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    return workspace, (0 if workspace is None else workspace.numel())
+
+
+def bsq_gemm_fp8r(x, w, w_scale, flags=0, y=None, workspace=None):
+    """bf16 x [M, K], E4M3 w [N, K], fp32 w_scale [N] -> bf16 y [M, N]."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N = w.shape[0]
+    _dense(w, torch.uint8, (N, K), "w")
+    _dense(w_scale, torch.float32, (N,), "w_scale")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    ws, nbytes = _workspace(BSQ_FMT_FP8R, M, N, K, flags, workspace, x.device)
+    _check("bsq_gemm_fp8r", lib.bsq_gemm_fp8r(_ptr(x), ldx, _ptr(w), _ptr(w_scale), _ptr(y), ldy, M, N, K, flags,
+                                              _ptr(ws), nbytes, _stream()))
+    return y
+
+
+def bsq_gemm_nvfp4(x, w, w_bscale, w_scale2, input_scale=None, flags=0, y=None, workspace=None):
+    """bf16 x [M, K], packed E2M1 w [N, K/2], E4M3 w_bscale [N, K/16], fp32 w_scale2 [1],
+    fp32 input_scale [1] (None with BSQ_WEIGHT_ONLY) -> bf16 y [M, N]."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N = w.shape[0]
+    _dense(w, torch.uint8, (N, K // 2), "w")
+    _dense(w_bscale, torch.uint8, (N, K // 16), "w_bscale")
+    _scalar(w_scale2, "w_scale2")
+    _scalar(input_scale, "input_scale")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    ws, nbytes = _workspace(BSQ_FMT_NVFP4, M, N, K, flags, workspace, x.device)
+    _check("bsq_gemm_nvfp4", lib.bsq_gemm_nvfp4(_ptr(x), ldx, _ptr(w), _ptr(w_bscale), _ptr(w_scale2),
+                                                _ptr(input_scale), _ptr(y), ldy, M, N, K, flags, _ptr(ws), nbytes,
+                                                _stream()))
+    return y
+
+
+def bsq_dequant_to_bf16(fmt, w, w_scale, w_scale2=None, out=None):
+    """Dequantize fp8r (w [N, K], w_scale fp32 [N]) or nvfp4 (w [N, K/2], w_scale uint8 [N, K/16],
+    w_scale2 fp32 [1]) weights to bf16 [N, K]."""
+    N = w.shape[0]
+    K = w.shape[1] * (2 if fmt == BSQ_FMT_NVFP4 else 1)
+    _dense(w, torch.uint8, tuple(w.shape), "w")
+    if fmt == BSQ_FMT_NVFP4:
+        _dense(w_scale, torch.uint8, (N, K // 16), "w_scale")
+        _scalar(w_scale2, "w_scale2")
+    else:
+        _dense(w_scale, torch.float32, (N,), "w_scale")
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=w.device) if out is None else out
+    _dense(out, torch.bfloat16, (N, K), "out")
+    _check("bsq_dequant_to_bf16", lib.bsq_dequant_to_bf16(fmt, _ptr(w), _ptr(w_scale), _ptr(w_scale2), N, K,
+                                                          _ptr(out), _stream()))
+    return out

@@ -1,0 +1,231 @@
+// C ABI of the block-scaled quantized linear layer (declared in include/bsq.h).
+//
+// Every entry point validates all of its arguments on the host before any
+// HIP call, then checks (once per device) that the current device is gfx950,
+// then enqueues its kernels on the caller's stream. Nothing here allocates,
+// frees or synchronizes device memory.
+#include "bsq.h"
+
+#include <atomic>
+#include <cstring>
+#include <string>
+
+#include "bsq_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxThreads = (int64_t)1 << 31;  // bound on work-items of any single launch
+constexpr int kMaxDevices = 64;
+
+thread_local std::string g_last_hip;
+
+bsq_status hip_fail(hipError_t e) {
+  g_last_hip = hipGetErrorString(e);
+  return BSQ_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+bsq_status check_device() {
+  static std::atomic<int> state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return BSQ_ERR_DEVICE;
+  }
+  int st = state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return BSQ_ERR_DEVICE;
+    }
+    st = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? BSQ_OK : BSQ_ERR_DEVICE;
+}
+
+// shape rules shared by every entry point: K > 0, K % 32 == 0, rows >= 0,
+// ld >= K and ld % 8 == 0
+bsq_status check_rows(int64_t rows, int64_t K, int64_t ld) {
+  if (rows < 0 || K <= 0 || K % 32 != 0 || K > (int64_t)1 << 30) return BSQ_ERR_SHAPE;
+  if (ld < K || ld % 8 != 0) return BSQ_ERR_SHAPE;
+  if (rows > 0 && rows > ((int64_t)1 << 62) / ld) return BSQ_ERR_SHAPE;
+  return BSQ_OK;
+}
+
+size_t ws_fp8r(int64_t M, int64_t K) { return pad256((size_t)(M * K)) + pad256((size_t)(4 * M)); }
+size_t ws_nvfp4(int64_t M, int64_t K) { return pad256((size_t)(M * K / 2)) + pad256((size_t)(M * K / 16)); }
+
+bsq_status check_gemm_common(const uint16_t* x, int64_t ldx, const void* w, uint16_t* y, int64_t ldy,
+                             int64_t M, int64_t N, int64_t K, uint32_t flags) {
+  if (flags & ~BSQ_WEIGHT_ONLY) return BSQ_ERR_ARG;
+  bsq_status st = check_rows(M, K, ldx);
+  if (st != BSQ_OK) return st;
+  if (N < 0 || N > ((int64_t)1 << 30) || M > ((int64_t)1 << 30)) return BSQ_ERR_SHAPE;
+  if (ldy < N || (M > 0 && M > ((int64_t)1 << 62) / (ldy > 0 ? ldy : 1))) return BSQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!x || !w || !y) return BSQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return BSQ_ERR_ALIGN;
+  if (M * (K / 16) >= kMaxThreads || N * (K / 16) >= kMaxThreads) return BSQ_ERR_SHAPE;
+  return BSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsq_abi_version(void) { return BSQ_ABI_VERSION; }
+
+const char* bsq_status_string(bsq_status s) {
+  switch (s) {
+    case BSQ_OK: return "ok";
+    case BSQ_ERR_NULL: return "null pointer";
+    case BSQ_ERR_SHAPE: return "invalid shape or leading dimension";
+    case BSQ_ERR_ALIGN: return "misaligned pointer";
+    case BSQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case BSQ_ERR_DEVICE: return "no gfx950 device is current";
+    case BSQ_ERR_HIP: return "HIP launch failed";
+    case BSQ_ERR_ARG: return "invalid format or flags";
+  }
+  return "unknown status";
+}
+
+const char* bsq_last_hip_error(void) { return g_last_hip.c_str(); }
+
+bsq_status bsq_quantize_act_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                                 float* x_scale, hipStream_t stream) {
+  bsq_status st = check_rows(M, K, ldx);
+  if (st != BSQ_OK) return st;
+  if (M == 0) return BSQ_OK;
+  if (!x || !xq || !x_scale) return BSQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4)) return BSQ_ERR_ALIGN;
+  if (M * 64 >= kMaxThreads) return BSQ_ERR_SHAPE;
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e = bsq::launch_quant_fp8r(x, M, K, ldx, xq, x_scale, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_quantize_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  const float* global_scale, uint8_t* xq, uint8_t* x_bscale,
+                                  hipStream_t stream) {
+  bsq_status st = check_rows(M, K, ldx);
+  if (st != BSQ_OK) return st;
+  if (M == 0) return BSQ_OK;
+  if (!x || !global_scale || !xq || !x_bscale) return BSQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(global_scale, 4) || !aligned(xq, 16) || !aligned(x_bscale, 4))
+    return BSQ_ERR_ALIGN;
+  if (M * (K / 16) >= kMaxThreads) return BSQ_ERR_SHAPE;
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e = bsq::launch_quant_nvfp4(x, M, K, ldx, global_scale, xq, x_bscale, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+size_t bsq_calibrate_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return pad256(4 * (size_t)bsq::calibrate_partials(M));
+}
+
+bsq_status bsq_calibrate_global_scale(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float* out_scale,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bsq_status st = check_rows(M, K, ldx);
+  if (st != BSQ_OK) return st;
+  if (M == 0) return BSQ_ERR_SHAPE;
+  if (!x || !out_scale) return BSQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out_scale, 4)) return BSQ_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bsq_calibrate_workspace_bytes(M, K) || !aligned(workspace, 4))
+    return BSQ_ERR_WORKSPACE;
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e = bsq::launch_calibrate(x, M, K, ldx, out_scale, static_cast<float*>(workspace), stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+size_t bsq_gemm_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, uint32_t flags) {
+  (void)N;
+  if ((flags & BSQ_WEIGHT_ONLY) || M <= 0 || K <= 0) return 0;
+  if (f == BSQ_FMT_FP8R) return ws_fp8r(M, K);
+  if (f == BSQ_FMT_NVFP4) return ws_nvfp4(M, K);
+  return 0;
+}
+
+bsq_status bsq_gemm_fp8r(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* w_scale, uint16_t* y,
+                         int64_t ldy, int64_t M, int64_t N, int64_t K, uint32_t flags, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  bsq_status st = check_gemm_common(x, ldx, w, y, ldy, M, N, K, flags);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!w_scale) return BSQ_ERR_NULL;
+  if (!aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
+  const bool weight_only = flags & BSQ_WEIGHT_ONLY;
+  if (!weight_only) {
+    if (!workspace || workspace_bytes < ws_fp8r(M, K)) return BSQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BSQ_ERR_ALIGN;
+  }
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e;
+  if (weight_only) {
+    bsq::DecArgs a{};
+    a.x = x; a.ldx = ldx; a.w = w; a.sw = w_scale; a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
+    e = bsq::launch_gemm_dec(bsq::kW8A16, a, stream);
+  } else {
+    uint8_t* xq = static_cast<uint8_t*>(workspace);
+    float* sx = reinterpret_cast<float*>(xq + pad256((size_t)(M * K)));
+    e = bsq::launch_quant_fp8r(x, M, K, ldx, xq, sx, stream);
+    if (e == hipSuccess) e = bsq::launch_gemm_fp8(xq, sx, w, w_scale, y, ldy, M, N, K, stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* w_bscale,
+                          const float* w_scale2, const float* input_scale, uint16_t* y, int64_t ldy, int64_t M,
+                          int64_t N, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  bsq_status st = check_gemm_common(x, ldx, w, y, ldy, M, N, K, flags);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  const bool weight_only = flags & BSQ_WEIGHT_ONLY;
+  if (!w_bscale || !w_scale2 || (!weight_only && !input_scale)) return BSQ_ERR_NULL;
+  if (!aligned(w_bscale, 4) || !aligned(w_scale2, 4) || (input_scale && !aligned(input_scale, 4)))
+    return BSQ_ERR_ALIGN;
+  if (!weight_only) {
+    if (!workspace || workspace_bytes < ws_nvfp4(M, K)) return BSQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BSQ_ERR_ALIGN;
+  }
+  if ((st = check_device()) != BSQ_OK) return st;
+  bsq::DecArgs a{};
+  a.x = x; a.ldx = ldx; a.w = w; a.ws = w_bscale; a.gw = w_scale2; a.y = y; a.ldy = ldy;
+  a.M = M; a.N = N; a.K = K;
+  hipError_t e;
+  if (weight_only) {
+    e = bsq::launch_gemm_dec(bsq::kW4A16, a, stream);
+  } else {
+    uint8_t* xq = static_cast<uint8_t*>(workspace);
+    uint8_t* xs = xq + pad256((size_t)(M * K / 2));
+    a.xq = xq; a.xs = xs; a.gx = input_scale;
+    e = bsq::launch_quant_nvfp4(x, M, K, ldx, input_scale, xq, xs, stream);
+    if (e == hipSuccess) e = bsq::launch_gemm_dec(bsq::kW4A4, a, stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_dequant_to_bf16(bsq_format f, const uint8_t* w, const void* w_scale, const float* w_scale2,
+                               int64_t N, int64_t K, uint16_t* w_bf16, hipStream_t stream) {
+  if (f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;
+  if (f == BSQ_FMT_FP8R && w_scale2) return BSQ_ERR_ARG;
+  bsq_status st = check_rows(N, K, K);
+  if (st != BSQ_OK) return st;
+  if (N == 0) return BSQ_OK;
+  if (!w || !w_scale || !w_bf16 || (f == BSQ_FMT_NVFP4 && !w_scale2)) return BSQ_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w_scale, 4) || !aligned(w_bf16, 16) || (w_scale2 && !aligned(w_scale2, 4)))
+    return BSQ_ERR_ALIGN;
+  if (N * (K / 16) >= kMaxThreads) return BSQ_ERR_SHAPE;
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e = f == BSQ_FMT_NVFP4
+                     ? bsq::launch_dequant_nvfp4(w, static_cast<const uint8_t*>(w_scale), w_scale2, N, K, w_bf16,
+                                                 stream)
+                     : bsq::launch_dequant_fp8r(w, static_cast<const float*>(w_scale), N, K, w_bf16, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device-side helpers shared by the bsq kernels (gfx950 / CDNA4 only).
+//
+// Number formats ("BFL (fp8r / nvfp4)", scheme list): E4M3 (OCP "FN": bias 7,
+// max 448, S.1111.111 = NaN, no Inf) for fp8r values and nvfp4 block scales;
+// E2M1 (bias 1, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) for nvfp4 values,
+// packed two per byte with the even element in the low nibble.
+//
+// Conversions use the gfx950 hardware instructions. Their behaviour was
+// checked on MI355X against bit-level round-to-nearest-even encoders over
+// every finite fp32 input:
+//   v_cvt_pk_fp8_f32          : RNE to E4M3FN, subnormals kept, sign of zero
+//                               kept; inputs above 448 must be clamped first
+//                               (the clamp gives the saturating encoding).
+//   v_cvt_scalef32_pk_fp4_f32 : RNE to E2M1 with saturation at +-6 (scale 1).
+//   v_cvt_pk_bf16_f32         : RNE to bf16.
+//   v_cvt_f32_fp8             : exact E4M3 decode.
+//   v_cvt_scalef32_pk_*_fp4   : exact E2M1 decode times 2^exponent(scale) --
+//                               only the scale's exponent is applied, so an
+//                               E4M3 block scale (4 significant bits) is
+//                               multiplied in separately.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+
+// ---- bf16 ---------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16 pair (round to nearest even), lo in bits 15:0
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  union { v2bf v; uint32_t u; } r;
+  r.v = v2bf{(__bf16)lo, (__bf16)hi};
+  return r.u;
+}
+
+// ---- E4M3 ---------------------------------------------------------------------
+// Encode into byte `byte_sel` (0..3) of `old`: two values at a time go into a
+// 16-bit half; callers build whole words with enc_e4m3x4.
+__device__ __forceinline__ uint32_t enc_e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+  c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+  d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+__device__ __forceinline__ uint32_t enc_e4m3(float a) {
+  a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0u, false) & 0xFFu;
+}
+// decode byte `sel` of w
+template <int sel>
+__device__ __forceinline__ float dec_e4m3(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, sel); }
+// decode two E4M3 bytes (word half `hi`) to two fp32
+template <bool hi>
+__device__ __forceinline__ v2f dec_e4m3x2(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, hi); }
+
+// ---- E2M1 ---------------------------------------------------------------------
+// Encode eight fp32 values into one word of packed E2M1 (element 0 in the low
+// nibble). Hardware saturates at +-6; scale 1.0 applies no exponent shift.
+__device__ __forceinline__ uint32_t enc_e2m1x8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+// byte `sel` of w -> two fp32 E2M1 values (exact)
+template <int sel>
+__device__ __forceinline__ v2f dec_e2m1x2_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
+}
+template <int sel>
+__device__ __forceinline__ v2h dec_e2m1x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, sel);
+}
+
+// ---- wave reductions ----------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// ---- launch geometry ----------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Remap the linear id so that each XCD receives a contiguous range of
+// tiles; the range is then walked in groups of `group_m` tile-rows so that
+// concurrently running tiles share operand rows in that XCD's L2.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_contiguous_id(int pid, int total) {
+  const int xcd = pid % kNumXcd, slot = pid / kNumXcd;
+  const int base = total / kNumXcd, rem = total % kNumXcd;
+  return xcd * base + (xcd < rem ? xcd : rem) + slot;
+}
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = id / per_group, first_m = g * group_m;
+  const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int in = id - g * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+}  // namespace bsq

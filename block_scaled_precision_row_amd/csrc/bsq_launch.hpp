@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI (bsq_api.cpp) and the kernels.
+// Arguments are already validated by the caller; each function enqueues its
+// kernels on `s` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsq {
+
+hipError_t launch_quant_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                             float* sx, hipStream_t s);
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* g,
+                              uint8_t* xq, uint8_t* xs, hipStream_t s);
+int calibrate_partials(int64_t M);
+hipError_t launch_calibrate(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float* out,
+                            float* partials, hipStream_t s);
+hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* sf, const float* g, int64_t N,
+                                int64_t K, uint16_t* out, hipStream_t s);
+hipError_t launch_dequant_fp8r(const uint8_t* w, const float* sw, int64_t N, int64_t K,
+                               uint16_t* out, hipStream_t s);
+
+// W8A8: y = bf16((sum e4m3(xq) e4m3(w)) * sx[m] * sw[n])
+hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+// Decode-to-16-bit GEMMs on the bf16 / f16 matrix cores.
+enum DecMode : int {
+  kW4A4 = 0,   // X nvfp4 (xq, xs, *gx), W nvfp4 (w, ws, *gw); f16 MFMA; alpha = gx * gw
+  kW4A16 = 1,  // X bf16, W nvfp4; bf16 MFMA; alpha = gw
+  kW8A16 = 2,  // X bf16, W E4M3 with per-row scale sw[n]; bf16 MFMA
+};
+struct DecArgs {
+  const uint16_t* x;   // bf16 activations (A16 modes)
+  int64_t ldx;
+  const uint8_t* xq;   // packed E2M1 activations [M][K/2] (W4A4)
+  const uint8_t* xs;   // E4M3 activation block scales [M][K/16] (W4A4)
+  const float* gx;     // activation global scale (W4A4)
+  const uint8_t* w;    // packed E2M1 [N][K/2] or E4M3 [N][K]
+  const uint8_t* ws;   // E4M3 weight block scales [N][K/16] (nvfp4)
+  const float* gw;     // weight global scale (nvfp4)
+  const float* sw;     // per-row weight scales [N] (W8A16)
+  uint16_t* y;
+  int64_t ldy;
+  int64_t M, N, K;
+};
+hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
+
+}  // namespace bsq
+
+#include <atomic>
+
+namespace bsq {
+// Raise a kernel's dynamic-LDS limit once per device (the GEMMs use more than
+// the 64 KB default; gfx950 has 160 KB per workgroup).
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+}  // namespace bsq

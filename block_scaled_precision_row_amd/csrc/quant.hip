@@ -1,0 +1,166 @@
+// Activation / weight quantizers and global-scale calibration.
+//
+// fp8r ("BFL (fp8r / nvfp4)", fp8r bullet): one E4M3 scale per row,
+//   d = fp32(amax / 448), r = fp32(1 / d), q = E4M3(fp32(x * r)).
+// nvfp4 (same page, nvfp4 bullet): E4M3 scale per 16 elements times an fp32
+//   global g, G = fp32(1 / g), sf = E4M3(fp32(fp32(a_b / 6) * G)),
+//   r_b = fp32(G / sf), q = E2M1(fp32(x * r_b)).
+// Every fp32 step is a single IEEE-rounded operation: this file is built
+// with -ffp-contract=off and correctly rounded division.
+#include "bsq_device.hpp"
+#include "bsq_launch.hpp"
+
+namespace bsq {
+
+// ---- fp8r: one wave per row ---------------------------------------------------
+// Each lane owns the 16-byte chunks (8 bf16) c = lane + 64 i of the row. The
+// first NCH of them stay in registers between the amax pass and the encode
+// pass; chunks beyond 64 * NCH (rows longer than 512 * NCH) are read twice.
+__device__ __forceinline__ float absmax8(uint4 v) {
+  return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                     fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
+               fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                     fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+}
+__device__ __forceinline__ uint2 encode8_fp8(uint4 v, float r) {
+  uint2 o;
+  o.x = enc_e4m3x4(bf16_lo(v.x) * r, bf16_hi(v.x) * r, bf16_lo(v.y) * r, bf16_hi(v.y) * r);
+  o.y = enc_e4m3x4(bf16_lo(v.z) * r, bf16_hi(v.z) * r, bf16_lo(v.w) * r, bf16_hi(v.w) * r);
+  return o;
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void quant_fp8r_rows(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                        int64_t ldx, uint8_t* __restrict__ xq,
+                                                        float* __restrict__ sx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = xq + row * (int64_t)K;
+  const int nch = K >> 3;
+  uint4 buf[NCH];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      buf[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
+      amax = fmaxf(amax, absmax8(buf[i]));
+    }
+  }
+  for (int c = lane + 64 * NCH; c < nch; c += 64)
+    amax = fmaxf(amax, absmax8(*reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)));
+  amax = wave_max(amax);
+  const float d = amax / kE4M3Max;
+  const float r = d > 0.0f ? 1.0f / d : 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) = encode8_fp8(buf[i], r);
+  }
+  for (int c = lane + 64 * NCH; c < nch; c += 64)
+    *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) =
+        encode8_fp8(*reinterpret_cast<const uint4*>(xr + (int64_t)c * 8), r);
+  if (lane == 0) sx[row] = d;
+}
+
+hipError_t launch_quant_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                             float* sx, hipStream_t s) {
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+  if (K <= 512 * 8)
+    hipLaunchKernelGGL(quant_fp8r_rows<8>, grid, block, 0, s, x, M, (int)K, ldx, xq, sx);
+  else
+    hipLaunchKernelGGL(quant_fp8r_rows<24>, grid, block, 0, s, x, M, (int)K, ldx, xq, sx);
+  return hipGetLastError();
+}
+
+// ---- nvfp4: one thread per 16-element block ---------------------------------
+__global__ __launch_bounds__(256) void quant_nvfp4_blocks(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                           int64_t ldx, const float* __restrict__ gptr,
+                                                           uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  const int nb = K >> 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= M * nb) return;
+  const int64_t row = t / nb;
+  const int b = (int)(t - row * nb);
+  const uint16_t* p = x + row * ldx + (int64_t)b * 16;
+  const uint4 v0 = *reinterpret_cast<const uint4*>(p);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
+  float f[16] = {bf16_lo(v0.x), bf16_hi(v0.x), bf16_lo(v0.y), bf16_hi(v0.y),
+                 bf16_lo(v0.z), bf16_hi(v0.z), bf16_lo(v0.w), bf16_hi(v0.w),
+                 bf16_lo(v1.x), bf16_hi(v1.x), bf16_lo(v1.y), bf16_hi(v1.y),
+                 bf16_lo(v1.z), bf16_hi(v1.z), bf16_lo(v1.w), bf16_hi(v1.w)};
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
+  const float G = 1.0f / gptr[0];
+  const float u = (a / kE2M1Max) * G;
+  const uint32_t sf = enc_e4m3(u);
+  const float sfv = dec_e4m3<0>(sf);
+  const float r = sfv > 0.0f ? G / sfv : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = f[i] * r;
+  uint2 o;
+  o.x = enc_e2m1x8(f);
+  o.y = enc_e2m1x8(f + 8);
+  *reinterpret_cast<uint2*>(xq + row * (int64_t)(K >> 1) + (int64_t)b * 8) = o;
+  xs[row * (int64_t)nb + b] = (uint8_t)sf;
+}
+
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* g,
+                              uint8_t* xq, uint8_t* xs, hipStream_t s) {
+  const int64_t total = M * (K >> 4);
+  hipLaunchKernelGGL(quant_nvfp4_blocks, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, x, M,
+                     (int)K, ldx, g, xq, xs);
+  return hipGetLastError();
+}
+
+// ---- calibration: amax over the tensor, two deterministic passes -------------
+constexpr int kCalibMaxBlocks = 1024;
+int calibrate_partials(int64_t M) {
+  const int64_t b = (M + 3) / 4;
+  return (int)(b < kCalibMaxBlocks ? b : kCalibMaxBlocks);
+}
+
+__global__ __launch_bounds__(256) void amax_partial(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                     int64_t ldx, float* __restrict__ partials) {
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float a = 0.0f;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < M; row += (int64_t)gridDim.x * 4) {
+    const uint16_t* xr = x + row * ldx;
+    for (int c = lane; c < (K >> 3); c += 64) {
+      a = fmaxf(a, absmax8(*reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)));
+    }
+  }
+  a = wave_max(a);
+  if (lane == 0) red[wv] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void amax_final(const float* __restrict__ partials, int n, float* out) {
+  __shared__ float red[4];
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) a = fmaxf(a, partials[i]);
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    out[0] = m > 0.0f ? m / (kE2M1Max * kE4M3Max) : 1.0f;
+  }
+}
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float* out,
+                            float* partials, hipStream_t s) {
+  const int nb = calibrate_partials(M);
+  hipLaunchKernelGGL(amax_partial, dim3(nb), dim3(256), 0, s, x, M, (int)K, ldx, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(amax_final, dim3(1), dim3(256), 0, s, partials, nb, out);
+  return hipGetLastError();
+}
+
+}  // namespace bsq

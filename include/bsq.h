@@ -1,0 +1,177 @@
+/*
+ * bsq.h -- block-scaled quantized linear layer (fp8r / nvfp4) on AMD gfx950.
+ *
+ * Computes bf16 Y = X W^T for a linear layer whose weights are stored in one
+ * of two block-scaled formats, as the "BFL (fp8r / nvfp4)" page of the
+ * diffusers quantization docs defines them (scheme list):
+ *
+ *   fp8r  : W is E4M3 [N][K] with one fp32 scale per row (output channel);
+ *           activations are quantized to E4M3 per row (token) at run time.
+ *   nvfp4 : W is E2M1 packed two per byte [N][K/2] with an E4M3 scale for
+ *           every 16 consecutive elements of a row [N][K/16], an fp32 global
+ *           scale (weight_scale_2) and a calibrated fp32 activation scale
+ *           (input_scale) used to quantize activations to nvfp4 at run time.
+ *
+ * The same page's "Kernels" section pairs an fp8 GEMM with row-wise scales
+ * (fp8r), runtime nvfp4 activation quantization before an fp4 GEMM (nvfp4),
+ * and a fallback that dequantizes the weights to the compute dtype (bf16)
+ * and runs a plain linear with unquantized activations.
+ *
+ * Conventions for every entry point:
+ *  - bf16 tensors are passed as uint16_t bit patterns. Every data pointer is
+ *    a DEVICE pointer (including the fp32 scalars global_scale, w_scale2 and
+ *    input_scale); the caller owns all memory. The library never allocates,
+ *    frees or synchronizes; work is enqueued on `stream` (NULL = default
+ *    stream) and the call returns once it is enqueued.
+ *  - Matrices are row-major. ldx / ldy are leading dimensions in elements;
+ *    all other operands are dense ([rows][cols] with no padding).
+ *  - Shapes: M, N >= 0 (0 means nothing to do and returns BSQ_OK without
+ *    touching any pointer); K > 0 and K % 32 == 0; ldx >= K with ldx a
+ *    multiple of 8; ldy >= N. M, N, K <= 2^30.
+ *  - Alignment: every data pointer 16-byte aligned, except fp32 scale
+ *    vectors and scalars (4-byte) and E4M3 block-scale arrays (4-byte).
+ *  - Outputs must not alias inputs.
+ *  - Errors: arguments are validated on the host, in full, before any HIP
+ *    call; a failed validation returns its status and enqueues nothing.
+ *    BSQ_ERR_DEVICE means the current device is not gfx950 (or there is
+ *    none); BSQ_ERR_HIP means a launch failed (bsq_last_hip_error() gives
+ *    the HIP message for the calling thread). No exception crosses the ABI.
+ *  - Determinism: the same inputs produce the same output bits; there are
+ *    no atomics in any reduction.
+ *  - Rounding: every fp32 step is IEEE round-to-nearest-even, with no
+ *    flush-to-zero; E4M3 / E2M1 encodings round to nearest with ties to the
+ *    even code, saturate at +-448 / +-6 and keep the sign of zero.
+ */
+#ifndef BSQ_H
+#define BSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSQ_ABI_VERSION 1
+
+typedef enum {
+  BSQ_OK = 0,
+  BSQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  BSQ_ERR_SHAPE = 2,     /* bad M/N/K/ld, or K % 32 != 0 */
+  BSQ_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  BSQ_ERR_WORKSPACE = 4, /* workspace NULL or smaller than bsq_gemm_workspace_bytes() */
+  BSQ_ERR_DEVICE = 5,    /* no device, or the current device is not gfx950 */
+  BSQ_ERR_HIP = 6,       /* a HIP launch failed */
+  BSQ_ERR_ARG = 7        /* an invalid enum or flag value */
+} bsq_status;
+
+typedef enum { BSQ_FMT_FP8R = 1, BSQ_FMT_NVFP4 = 2 } bsq_format;
+
+/* Keep activations in bf16 and dequantize only the weights inside the GEMM
+ * (the fallback's arithmetic: "BFL (fp8r / nvfp4)", last paragraph of
+ * "Kernels"), without rounding the weights to bf16 first. */
+#define BSQ_WEIGHT_ONLY 0x1u
+
+int bsq_abi_version(void);
+const char* bsq_status_string(bsq_status s);
+/* Message of the last HIP error seen by this thread ("" if none). */
+const char* bsq_last_hip_error(void);
+
+/*
+ * Per-row E4M3 quantization ("BFL (fp8r / nvfp4)", fp8r bullet: activations
+ * are quantized to E4M3 per row at run time). For each row m of X:
+ *   a = max_k |x|, d = fp32(a / 448), r = fp32(1 / d),
+ *   xq[m][k] = E4M3(fp32(x[m][k] * r)), x_scale[m] = d
+ * (a zero row gives d = 0 and signed-zero codes). Dequantized value:
+ * e4m3(xq) * d. Applied to a weight matrix W [N][K] this produces the fp8r
+ * weight and its per-row weight_scale.
+ *   x       [M][ldx] bf16        xq      [M][K] E4M3 codes
+ *   x_scale [M] fp32
+ */
+bsq_status bsq_quantize_act_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                 uint8_t* xq, float* x_scale, hipStream_t stream);
+
+/*
+ * nvfp4 quantization with a given global scale g = *global_scale
+ * ("BFL (fp8r / nvfp4)", nvfp4 bullet and "Kernels" table: activations are
+ * quantized to nvfp4 at run time with the calibrated input_scale):
+ *   G = fp32(1 / g); per 16-element block b of a row:
+ *   a_b = max |x|, sf_b = E4M3(fp32(fp32(a_b / 6) * G)),
+ *   r_b = sf_b == 0 ? 0 : fp32(G / e4m3(sf_b)), q = E2M1(fp32(x * r_b)).
+ * Dequantized value: e2m1(q) * e4m3(sf_b) * g. Values beyond the calibrated
+ * range saturate. g must be a positive normal fp32 with 1/g finite.
+ * Applied to W with g = weight_scale_2 it produces the nvfp4 weight tensors.
+ *   x        [M][ldx] bf16
+ *   xq       [M][K/2] packed E2M1, element 2j in the low nibble of byte j
+ *   x_bscale [M][K/16] E4M3 block scales
+ */
+bsq_status bsq_quantize_act_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  const float* global_scale, uint8_t* xq, uint8_t* x_bscale,
+                                  hipStream_t stream);
+
+/*
+ * Calibrate an nvfp4 global scale: *out_scale = fp32(amax(X) / (6 * 448)),
+ * or 1.0 when X is all zeros, so that the tensor maximum maps onto the
+ * largest nvfp4 magnitude (the calibrated input_scale / weight_scale_2 of
+ * the nvfp4 bullet). Needs a workspace of bsq_calibrate_workspace_bytes(M, K)
+ * bytes (4-byte aligned). M must be > 0.
+ */
+size_t bsq_calibrate_workspace_bytes(int64_t M, int64_t K);
+bsq_status bsq_calibrate_global_scale(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      float* out_scale, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Workspace the GEMM entry points need (quantized activations):
+ *   fp8r:  M*K + 4*M bytes, nvfp4: M*K/2 + M*K/16 bytes (each part padded
+ *   to 256 bytes); 0 with BSQ_WEIGHT_ONLY. */
+size_t bsq_gemm_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, uint32_t flags);
+
+/*
+ * fp8r linear ("BFL (fp8r / nvfp4)", fp8r bullet and "Kernels" table: fp8
+ * GEMM with row-wise scales). Default (W8A8): quantizes X per row into the
+ * workspace (as bsq_quantize_act_fp8r), then
+ *   y[m][n] = bf16( (sum_k e4m3(xq[m][k]) * e4m3(w[n][k])) * sx[m] * w_scale[n] )
+ * with fp32 accumulation. With BSQ_WEIGHT_ONLY (W8A16):
+ *   y[m][n] = bf16( (sum_k x[m][k] * e4m3(w[n][k])) * w_scale[n] ).
+ *   x [M][ldx] bf16, w [N][K] E4M3, w_scale [N] fp32, y [M][ldy] bf16
+ */
+bsq_status bsq_gemm_fp8r(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* w_scale,
+                         uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4 linear ("BFL (fp8r / nvfp4)", nvfp4 bullet and "Kernels" table).
+ * Default (W4A4): quantizes X to nvfp4 with *input_scale into the workspace
+ * (as bsq_quantize_act_nvfp4), then
+ *   y[m][n] = bf16( (sum_k xh[m][k] * wh[n][k]) * (*input_scale) * (*w_scale2) )
+ * with xh = e2m1 * e4m3(block scale) (exact) for both operands and fp32
+ * accumulation. With BSQ_WEIGHT_ONLY (W4A16, input_scale may be NULL):
+ *   y[m][n] = bf16( (sum_k x[m][k] * wh[n][k]) * (*w_scale2) ).
+ *   x [M][ldx] bf16, w [N][K/2] packed E2M1, w_bscale [N][K/16] E4M3,
+ *   w_scale2 [1] fp32, input_scale [1] fp32, y [M][ldy] bf16
+ */
+bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* w_bscale,
+                          const float* w_scale2, const float* input_scale, uint16_t* y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Fallback dequantization to bf16 ("BFL (fp8r / nvfp4)", last paragraph of
+ * "Kernels": on other devices the weights are dequantized to the compute
+ * dtype every forward and the layer runs as a regular linear):
+ *   nvfp4: w_bf16[n][k] = bf16( fp32( (e2m1 * e4m3(sf)) * (*w_scale2) ) )
+ *          (w_scale is the [N][K/16] E4M3 block-scale array)
+ *   fp8r:  w_bf16[n][k] = bf16( fp32( e4m3(w) * w_scale[n] ) )
+ *          (w_scale is the [N] fp32 row-scale vector; w_scale2 must be NULL)
+ * Bit-exact: every step is one rounding as written.
+ */
+bsq_status bsq_dequant_to_bf16(bsq_format f, const uint8_t* w, const void* w_scale,
+                               const float* w_scale2, int64_t N, int64_t K, uint16_t* w_bf16,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSQ_H */

@@ -1,0 +1,55 @@
+"""Helpers shared by the GPU parity tests: device upload / download and the
+GEMM tolerance.
+
+Tolerance for bf16 GEMM outputs (fp32 accumulation, bf16 rounding of Y):
+both must hold
+  normwise   ||Y_gpu - Y_ref||_F / ||Y_ref||_F <= 1e-2
+  elementwise |y_gpu - y_ref| <= 1e-2 |y_ref| + 1e-3 rms(Y_ref)
+where Y_ref is the oracle's fp64 product of the exactly dequantized
+operands. The floor term covers outputs near zero under cancellation; the
+expected error is about 2^-9 normwise from the bf16 output rounding.
+"""
+import numpy as np
+import torch
+
+REL_TOL = 1e-2
+FLOOR = 1e-3
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def dev_scalar(v):
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device="cuda")
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def gemm_errors(y_gpu_bits, y_ref):
+    y = bf16_to_f64(y_gpu_bits)
+    diff = np.abs(y - y_ref)
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    norm = float(np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300))
+    excess = float(np.max(diff - (REL_TOL * np.abs(y_ref) + FLOOR * rms))) if y_ref.size else -1.0
+    return norm, excess, float(diff.max()) if diff.size else 0.0, rms
+
+
+def assert_gemm_close(y_gpu_bits, y_ref, what=""):
+    norm, excess, maxdiff, rms = gemm_errors(y_gpu_bits, y_ref)
+    print("%s normwise=%.3e maxabs=%.3e rms=%.3e" % (what, norm, maxdiff, rms), flush=True)
+    assert np.all(np.isfinite(bf16_to_f64(y_gpu_bits))), what
+    assert norm <= REL_TOL, (what, norm)
+    assert excess <= 0.0, (what, excess)

@@ -1,0 +1,114 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call.
+
+Pointers passed here are fake (never dereferenced): every call below fails
+validation before touching the device. The one call with valid arguments is
+only made when no GPU is present, where it must report BSQ_ERR_DEVICE.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from block_scaled_precision_row_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib
+P = ctypes.c_void_p
+A = P(1 << 20)       # fake, 16-byte aligned
+B = P((1 << 20) + 4096)
+C = P((1 << 20) + 8192)
+D = P((1 << 20) + 12288)
+ODD = P((1 << 20) + 2)
+OK, NULL, SHAPE, ALIGN, WS, DEV, HIP, ARG = range(8)
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "bsq.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(bsq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    syms = declared_symbols()
+    assert len(syms) == 11
+    so = ctypes.CDLL(_lib.LIB_PATH)
+    for s in syms:
+        assert hasattr(so, s), s
+        assert s in _lib.SIGNATURES, s
+    assert L.bsq_abi_version() == 1
+    assert L.bsq_status_string(SHAPE).decode().startswith("invalid shape")
+
+
+def test_workspace_sizes():
+    pad = lambda n: (n + 255) // 256 * 256
+    assert L.bsq_gemm_workspace_bytes(_lib.BSQ_FMT_FP8R, 4096, 3072, 3072, 0) == pad(4096 * 3072) + pad(4 * 4096)
+    assert L.bsq_gemm_workspace_bytes(_lib.BSQ_FMT_NVFP4, 4096, 12288, 3072, 0) == pad(4096 * 1536) + pad(4096 * 192)
+    assert L.bsq_gemm_workspace_bytes(_lib.BSQ_FMT_NVFP4, 4096, 12288, 3072, _lib.BSQ_WEIGHT_ONLY) == 0
+    assert L.bsq_gemm_workspace_bytes(_lib.BSQ_FMT_FP8R, 0, 1, 32, 0) == 0
+    assert L.bsq_calibrate_workspace_bytes(4096, 3072) == 4096
+
+
+def test_quantizer_validation():
+    q = L.bsq_quantize_act_fp8r
+    assert q(A, 4, 48, 48, B, C, None) == SHAPE          # K % 32
+    assert q(A, 4, 64, 32, B, C, None) == SHAPE          # ldx < K
+    assert q(A, 4, 64, 68, B, C, None) == SHAPE          # ldx % 8
+    assert q(A, -1, 64, 64, B, C, None) == SHAPE
+    assert q(A, 4, 0, 64, B, C, None) == SHAPE
+    assert q(None, 4, 64, 64, B, C, None) == NULL
+    assert q(ODD, 4, 64, 64, B, C, None) == ALIGN
+    assert q(None, 0, 64, 64, None, None, None) == OK    # empty: nothing to do
+    n = L.bsq_quantize_act_nvfp4
+    assert n(A, 4, 64, 64, None, B, C, None) == NULL
+    assert n(A, 4, 64, 64, D, ODD, C, None) == ALIGN
+    assert n(A, 4, 40, 64, D, B, C, None) == SHAPE
+    assert n(None, 0, 64, 64, None, None, None, None) == OK
+    c = L.bsq_calibrate_global_scale
+    assert c(A, 0, 64, 64, B, C, 4096, None) == SHAPE
+    assert c(A, 4, 64, 64, B, None, 4096, None) == WS
+    assert c(A, 4, 64, 64, B, C, 0, None) == WS
+
+
+def test_gemm_validation():
+    g = L.bsq_gemm_fp8r
+    ws = L.bsq_gemm_workspace_bytes(_lib.BSQ_FMT_FP8R, 64, 64, 64, 0)
+    assert g(A, 64, B, C, D, 64, 64, 64, 64, 0, None, 0, None) == WS
+    assert g(A, 64, B, C, D, 64, 64, 64, 64, 0, A, ws - 1, None) == WS
+    assert g(A, 64, B, C, D, 64, 64, 64, 64, 2, A, ws, None) == ARG
+    assert g(A, 64, B, None, D, 64, 64, 64, 64, 0, A, ws, None) == NULL
+    assert g(A, 64, B, C, D, 63, 64, 64, 64, 0, A, ws, None) == SHAPE   # ldy < N
+    assert g(A, 64, B, C, D, 64, 64, 64, 48, 0, A, ws, None) == SHAPE   # K % 32
+    assert g(A, 64, ODD, C, D, 64, 64, 64, 64, 0, A, ws, None) == ALIGN
+    assert g(None, 64, None, None, None, 64, 0, 64, 64, 0, None, 0, None) == OK
+    assert g(None, 64, None, None, None, 64, 64, 0, 64, 0, None, 0, None) == OK
+    n = L.bsq_gemm_nvfp4
+    assert n(A, 64, B, C, D, None, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == NULL       # W4A4 needs input_scale
+    assert n(A, 64, B, C, None, D, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == NULL       # w_scale2
+    assert n(A, 64, B, C, D, D, A, 64, 64, 64, 64, 0, None, 0, None) == WS
+    assert n(A, 64, B, ODD, D, D, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == ALIGN
+    assert n(A, 64, B, C, D, None, A, 64, 64, 64, 64, 4, None, 0, None) == ARG
+
+
+def test_dequant_validation():
+    d = L.bsq_dequant_to_bf16
+    assert d(3, A, B, C, 4, 64, D, None) == ARG
+    assert d(_lib.BSQ_FMT_FP8R, A, B, C, 4, 64, D, None) == ARG      # fp8r takes no global scale
+    assert d(_lib.BSQ_FMT_NVFP4, A, B, None, 4, 64, D, None) == NULL
+    assert d(_lib.BSQ_FMT_NVFP4, A, B, C, 4, 40, D, None) == SHAPE
+    assert d(_lib.BSQ_FMT_NVFP4, A, B, C, 4, 64, ODD, None) == ALIGN
+    assert d(_lib.BSQ_FMT_FP8R, None, None, None, 0, 64, None, None) == OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_valid_call_without_gpu_reports_device_error():
+    assert L.bsq_quantize_act_fp8r(A, 4, 64, 64, B, C, None) == DEV
+    assert L.bsq_dequant_to_bf16(_lib.BSQ_FMT_FP8R, A, B, None, 4, 64, D, None) == DEV
+
+
+def test_binding_checks_tensors_before_calling():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.bsq_quantize_act_fp8r(x)          # CPU tensor is rejected by the binding

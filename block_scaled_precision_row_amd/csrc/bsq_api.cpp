@@ -51,7 +51,7 @@ bsq_status check_device() {
 // shape rules shared by every entry point: K > 0, K % 32 == 0, rows >= 0,
 // ld >= K and ld % 8 == 0
 bsq_status check_rows(int64_t rows, int64_t K, int64_t ld) {
-  if (rows < 0 || K <= 0 || K % 32 != 0 || K > (int64_t)1 << 30) return BSQ_ERR_SHAPE;
+  if (rows < 0 || K <= 0 || K % 32 != 0 || K > (int64_t)1 << 20) return BSQ_ERR_SHAPE;
   if (ld < K || ld % 8 != 0) return BSQ_ERR_SHAPE;
   if (rows > 0 && rows > ((int64_t)1 << 62) / ld) return BSQ_ERR_SHAPE;
   return BSQ_OK;

@@ -118,3 +118,49 @@ __device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, i
 }
 
 }  // namespace bsq
+
+namespace bsq {
+
+// ---- LDS staging ----------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle); out-of-range loads return zeros
+constexpr int kBufferConfig = 0x00020000;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource for `bytes` bytes at `base` (stride 0); reads at or
+// past `bytes` return zeros.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, kBufferConfig};
+}
+
+// LDS byte offset of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)(p));
+}
+
+// global -> LDS copy of 16 bytes per lane: lane l's bytes at rsrc + voff + soff
+// land at LDS [lds + 16 l, lds + 16 l + 16). Written as inline asm so that the
+// compiler does not serialize unrelated LDS reads behind it; the caller
+// waits for completion (wait_vmem) before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
+}
+
+// 128-byte LDS rows, 16-byte chunks XOR-swizzled by ((row >> 1) & 7): a
+// ds_read_b128 serves 16 lanes per 256-byte window of the 64-bank LDS, and
+// 16 consecutive rows reading the same logical chunk then touch 16 distinct
+// 16-byte slots
+__device__ __forceinline__ int lds_swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// s_waitcnt encodings (gfx9): vmcnt[3:0]+[15:14], expcnt[6:4], lgkmcnt[11:8]
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until at most n (< 16) vector-memory operations are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vmem_upto_c() { __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15)); }
+#define wait_vmem_upto(n) wait_vmem_upto_c<((n) < 15 ? (n) : 15)>()
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+}  // namespace bsq

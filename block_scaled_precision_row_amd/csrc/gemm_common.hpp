@@ -1,0 +1,174 @@
+// Building blocks shared by the GEMM kernels: tile mapping, LDS swizzles,
+// the LDS-DMA stage loader and the bf16 epilogue.
+//
+// All GEMMs compute Y[m][n] = sum_k X[m][k] W[n][k] for row-major X [M][K]
+// and W [N][K] (both K-contiguous). A workgroup of 4 waves owns a BM x BN
+// tile of Y; each wave a (BM/2) x (BN/2) quadrant of 32x32 MFMA tiles. The
+// MFMA "A" operand is a 32-row slice of W and "B" a 32-row slice of X, so the
+// accumulator of a lane holds one token m (lane % 32) and, per 4-register
+// group g, the four consecutive outputs n = 8 g + 4 (lane / 32) + (0..3).
+//
+// K is walked in stages of 64 values. Every stage of every operand lands in
+// LDS untouched (packed codes stay packed) through buffer_load ... lds, in a
+// ring of NSTAGE buffers so that several stages are in flight while the
+// MFMAs work on an older one. Operands are read from LDS into registers one
+// stage ahead and, where needed, decoded there right before the MFMA.
+#pragma once
+
+#include "bsq_device.hpp"
+
+namespace bsq {
+namespace gemm {
+
+constexpr int kThreads = 256;
+constexpr int kKS = 64;                  // K values per stage
+constexpr int kOutOfRange = 0x40000000;  // buffer offset beyond any tile's records
+
+// s_waitcnt with vmcnt <= n (n in 0..63), lgkmcnt and expcnt unconstrained (gfx9 encoding)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS rows of R bytes hold R/16 chunks of 16 bytes. A ds_read_b128 serves 16
+// lanes per 256-byte LDS window; 16 consecutive rows reading the same logical
+// chunk must land on 16 distinct 16-byte slots of the window, so the physical
+// chunk is the logical one XOR-ed with (row / rows-per-window) mod chunks.
+template <int R>
+__device__ __forceinline__ int swz_chunk(int row, int c) {
+  constexpr int C = R / 16, RPW = 16 / C;
+  return c ^ ((row / RPW) % C);
+}
+template <int R>
+__device__ __forceinline__ int swz_off(int row, int c) {
+  return row * R + (swz_chunk<R>(row, c) << 4);
+}
+
+// One operand region of a stage: ROWS rows of R bytes each (R = 64 values at
+// the operand's width: 128 for bf16, 64 for E4M3, 32 for packed E2M1). A 1 KB
+// DMA load covers 1024 / R rows; lane l writes physical chunk l % C of row
+// l / C, so it fetches the logical chunk that the swizzle places there.
+// Loads are spread round-robin over the 4 waves.
+template <int R, int ROWS>
+struct Region {
+  static constexpr int C = R / 16;
+  static constexpr int RPL = 1024 / R;            // rows per load
+  static constexpr int LOADS = ROWS / RPL;        // loads per stage
+  static constexpr int MIN_PER_WAVE = LOADS / 4;  // loads issued by every wave
+  static constexpr int MAX_PER_WAVE = (LOADS + 3) / 4;
+  static_assert(ROWS % RPL == 0, "region rows must fill whole loads");
+  static constexpr int VPC = 16 * 64 / R;         // K values per 16-byte chunk
+};
+
+// Issue this wave's loads of region `Rg` for the stage starting at K value kb.
+// rsrc covers the tile's rows (rows past the matrix read as zeros), `stride`
+// is the row pitch in bytes, `kbyte` the byte offset of the stage in a row.
+template <class Rg>
+__device__ __forceinline__ void dma_region(const v4i& rsrc, uint32_t lds_base, int wave, int lane, int stride,
+                                           int kbyte, int kb, int K) {
+  const int lrow = lane / Rg::C, phys = lane % Rg::C;
+#pragma unroll
+  for (int i = 0; i < Rg::MAX_PER_WAVE; ++i) {
+    const int ld = wave + 4 * i;
+    if (i >= Rg::MIN_PER_WAVE && ld >= Rg::LOADS) break;  // wave-uniform
+    const int row = ld * Rg::RPL + lrow;
+    const int c = swz_chunk<Rg::C * 16>(row, phys);  // the swizzle is an involution
+    const int voff = (kb + c * Rg::VPC < K) ? lrow * stride + (c << 4) : kOutOfRange;
+    dma16(rsrc, lds_base + ld * 1024, voff, ld * Rg::RPL * stride + kbyte);
+  }
+}
+
+// E4M3 block scales of a stage: 4 bytes (4 blocks of 16) per row, 64 rows per
+// 4-byte-per-lane DMA load.
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
+}
+template <int ROWS>
+struct ScaleRegion {
+  static constexpr int LOADS = (ROWS + 63) / 64;
+  static constexpr int MIN_PER_WAVE = LOADS / 4;
+  static constexpr int MAX_PER_WAVE = (LOADS + 3) / 4;
+  static_assert(ROWS % 64 == 0, "scale rows must fill whole loads");
+};
+template <class Sg>
+__device__ __forceinline__ void dma_scales(const v4i& rsrc, uint32_t lds_base, int wave, int lane, int kstride,
+                                           int kb) {
+#pragma unroll
+  for (int i = 0; i < Sg::MAX_PER_WAVE; ++i) {
+    const int ld = wave + 4 * i;
+    if (i >= Sg::MIN_PER_WAVE && ld >= Sg::LOADS) break;
+    dma4(rsrc, lds_base + ld * 256, lane * kstride, ld * 64 * kstride + (kb >> 4));
+  }
+}
+
+// ---- bf16 epilogue --------------------------------------------------------------
+// acc[i][j] is the 32x32 tile (n-tile i, m-tile j) of this wave; `scale(n)`
+// gives the per-output factor (row scales and global scales folded in by the
+// caller: y = bf16(acc * rowscale(m) * scale(n))).
+template <int TN, int TM, class RowScale, class ColScale>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[TN][TM], uint16_t* __restrict__ y, int64_t ldy, int M,
+                                           int N, int mw0, int nw0, int lane, RowScale rs, ColScale cs) {
+  const int lr = lane & 31, lh = lane >> 5;
+  const bool vec_ok = (ldy & 3) == 0;  // 8-byte stores need 4-element aligned rows
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = mw0 + j * 32 + lr;
+    if (m >= M) continue;
+    const float xs = rs(m);
+    uint16_t* yr = y + (int64_t)m * ldy;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nw0 + i * 32 + 8 * g + 4 * lh;
+        const v16f& A = acc[i][j];
+        if (n + 3 < N && vec_ok) {
+          const float v0 = A[4 * g + 0] * xs * cs(n + 0), v1 = A[4 * g + 1] * xs * cs(n + 1);
+          const float v2 = A[4 * g + 2] * xs * cs(n + 2), v3 = A[4 * g + 3] * xs * cs(n + 3);
+          *reinterpret_cast<uint2*>(yr + n) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yr[n + e] = (uint16_t)(pack_bf16x2(A[4 * g + e] * xs * cs(n + e), 0.0f) & 0xFFFFu);
+        }
+      }
+    }
+  }
+}
+
+// Copy a bf16 output tile [BM][BN] (rows TROW bytes apart in LDS) to Y in
+// 16-byte row chunks: consecutive threads write consecutive chunks of a row.
+template <int BM, int BN, int TROW>
+__device__ __forceinline__ void store_tile_rows(const uint8_t* tile, uint16_t* __restrict__ y, int64_t ldy, int M,
+                                                int N, int m0, int n0, int tid) {
+  constexpr int CPR = BN / 8;  // 16-byte chunks per row
+  const bool vec_ok = (ldy & 7) == 0;
+  for (int idx = tid; idx < BM * CPR; idx += kThreads) {
+    const int ml = idx / CPR, c = idx - ml * CPR;
+    const int m = m0 + ml, n = n0 + 8 * c;
+    if (m >= M) break;  // rows only grow with idx
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * TROW + c * 16);
+    uint16_t* dst = y + (int64_t)m * ldy + n;
+    if (n + 8 <= N && vec_ok) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// tile index of this workgroup (XCD-contiguous, grouped along M)
+__device__ __forceinline__ void tile_of_block(int M, int N, int BM, int BN, int& m0, int& n0) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  grouped_tile(xcd_contiguous_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
+  m0 = tm * BM;
+  n0 = tn * BN;
+}
+
+}  // namespace gemm
+}  // namespace bsq

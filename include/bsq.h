@@ -27,7 +27,7 @@
  *    all other operands are dense ([rows][cols] with no padding).
  *  - Shapes: M, N >= 0 (0 means nothing to do and returns BSQ_OK without
  *    touching any pointer); K > 0 and K % 32 == 0; ldx >= K with ldx a
- *    multiple of 8; ldy >= N. M, N, K <= 2^30.
+ *    multiple of 8; ldy >= N. M, N <= 2^30 and K <= 2^20.
  *  - Alignment: every data pointer 16-byte aligned, except fp32 scale
  *    vectors and scalars (4-byte) and E4M3 block-scale arrays (4-byte).
  *  - Outputs must not alias inputs.

@@ -46,7 +46,7 @@ struct DecArgs {
   int64_t M, N, K;
 };
 hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
-// W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 64 == 0
+// W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0
 bool gemm_w4a4_supported(const DecArgs& a);
 hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s);
 

@@ -45,12 +45,13 @@ __device__ __forceinline__ int swz_off(int row, int c) {
   return row * R + (swz_chunk<R>(row, c) << 4);
 }
 
-// One operand region of a stage: ROWS rows of R bytes each (R = 64 values at
-// the operand's width: 128 for bf16, 64 for E4M3, 32 for packed E2M1). A 1 KB
+// One operand region of a stage: ROWS rows of R bytes each, holding KSTAGE K
+// values per row (for a 64-deep stage: 128 bytes of bf16, 64 of E4M3, 32 of
+// packed E2M1, 4 of E4M3 block scales). A 1 KB
 // DMA load covers 1024 / R rows; lane l writes physical chunk l % C of row
 // l / C, so it fetches the logical chunk that the swizzle places there.
 // Loads are spread round-robin over the 4 waves.
-template <int R, int ROWS>
+template <int R, int ROWS, int KSTAGE = kKS>
 struct Region {
   static constexpr int C = R / 16;
   static constexpr int RPL = 1024 / R;            // rows per load
@@ -58,7 +59,7 @@ struct Region {
   static constexpr int MIN_PER_WAVE = LOADS / 4;  // loads issued by every wave
   static constexpr int MAX_PER_WAVE = (LOADS + 3) / 4;
   static_assert(ROWS % RPL == 0, "region rows must fill whole loads");
-  static constexpr int VPC = 16 * 64 / R;         // K values per 16-byte chunk
+  static constexpr int VPC = 16 * KSTAGE / R;     // K values per 16-byte chunk
 };
 
 // Issue this wave's loads of region `Rg` for the stage starting at K value kb.

@@ -12,18 +12,23 @@
 // block-scaled FP4 MFMA applies power-of-two scales per 32 elements, which
 // cannot carry an E4M3 scale per 16.)
 //
-// Data movement (conventions in gemm_common.hpp): each 64-deep K stage of
-// every W and Xq row -- 32 bytes of packed codes plus 4 block-scale bytes --
-// is copied to LDS as stored, by LDS DMA, into a ring of NS stage buffers.
-// Every wave reads its operands' packed bytes from LDS one stage ahead and
-// decodes them in registers right before the MFMAs of each 16-deep K step:
-// per byte one v_cvt_scalef32_pk_f16_fp4 (exact E2M1 -> f16 pair) and one
-// v_pk_mul_f16 by the block scale. LDS traffic stays at the packed size; the
-// decode work (about 4 VALU per MFMA) issues under the MFMAs.
+// Data movement (conventions in gemm_common.hpp): a stage is 256 K values
+// of every W and Xq row -- 128 bytes of packed codes (one full cache line)
+// plus 16 block-scale bytes -- copied to LDS as stored by LDS DMA into one of
+// two stage buffers while the other is multiplied. Long stages keep the
+// number of memory requests low (small per-row segments would cost one
+// request each). Every wave reads its operands' packed bytes from LDS one
+// 64-deep K group ahead and decodes them in registers right before the MFMAs
+// of each 16-deep K step: per byte one v_cvt_scalef32_pk_f16_fp4 (exact
+// E2M1 -> f16 pair) and one v_pk_mul_f16 by the block scale. LDS traffic
+// stays at the packed size; the decode work (about 4 VALU per MFMA) issues
+// under the MFMAs.
 //
-// K permutation: within a stage, lane half h of an MFMA operand covers K
-// values [32 h, 32 h + 32) of the stage, one 8-value group per K step, for
-// both operands alike, so every product pairs equal K indices.
+// K permutation: lane half h of an MFMA operand covers K values
+// [128 h, 128 h + 128) of a stage -- 32 of them per 64-deep K group q, at
+// [128 h + 32 q, 128 h + 32 q + 32), one 8-value group per K step -- for both
+// operands alike, so every product pairs equal K indices. A lane's 8 block
+// scales of a stage are then 8 consecutive bytes, read once per stage.
 #include "gemm_common.hpp"
 #include "bsq_launch.hpp"
 
@@ -33,51 +38,55 @@ namespace {
 
 using namespace gemm;
 
-template <int BM, int BN, int NS>
+constexpr int kStageK = 256;  // K values per stage
+
+template <int BM, int BN>
 struct W4Cfg {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  using RA = Region<32, BN>;  // packed W rows, 32 bytes per stage
-  using RB = Region<32, BM>;  // packed Xq rows
-  using SA = ScaleRegion<BN>;
-  using SB = ScaleRegion<BM>;
-  static constexpr int A_OFF = 0, B_OFF = BN * 32, SA_OFF = (BN + BM) * 32, SB_OFF = SA_OFF + BN * 4;
-  static constexpr int STAGE = (BN + BM) * 36;
-  static constexpr int LOADS_MIN = RA::MIN_PER_WAVE + RB::MIN_PER_WAVE + SA::MIN_PER_WAVE + SB::MIN_PER_WAVE;
+  using RA = Region<128, BN, kStageK>;  // packed W rows, 128 bytes per stage
+  using RB = Region<128, BM, kStageK>;  // packed Xq rows
+  using SA = Region<16, BN, kStageK>;   // W block scales, 16 bytes per stage
+  using SB = Region<16, BM, kStageK>;   // Xq block scales
+  static constexpr int A_OFF = 0, B_OFF = BN * 128, SA_OFF = (BN + BM) * 128, SB_OFF = SA_OFF + BN * 16;
+  static constexpr int STAGE = (BN + BM) * 144;
+  static constexpr int LOADS = RA::MAX_PER_WAVE + RB::MAX_PER_WAVE + SA::MAX_PER_WAVE + SB::MAX_PER_WAVE;
   static constexpr int TROW = BN * 2 + 16;  // bytes per row of the bf16 output tile in LDS
-  static constexpr int LDS = NS * STAGE > BM * TROW ? NS * STAGE : BM * TROW;
-  static_assert(NS >= 3, "at least one stage in flight behind the next");
-  static_assert((NS - 3) * LOADS_MIN < 64, "vmcnt range");
+  static constexpr int LDS = 2 * STAGE > BM * TROW ? 2 * STAGE : BM * TROW;
+  static_assert(LOADS < 64, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// packed operand bytes of one stage for one lane: 32 E2M1 values (4 dwords)
-// and the two E4M3 scales of its two 16-value blocks as f16 pairs
+// packed operand bytes of one K group for one lane: 32 E2M1 values (4 dwords)
 struct Raw {
   uint4 q;
-  uint32_t s;  // two scale bytes in bits 15:0
 };
 
+// packed bytes of K group q (0..3) of a stage for this lane: chunk 4h + q of the row
 template <int TN, int TM>
-__device__ __forceinline__ void read_raw(const uint8_t* st, int a_off, int b_off, int sa_off, int sb_off, int rowa,
-                                         int rowb, int lh, Raw (&ra)[TN], Raw (&rb)[TM]) {
+__device__ __forceinline__ void read_raw(const uint8_t* st, int a_off, int b_off, int rowa, int rowb, int lh, int q,
+                                         Raw (&ra)[TN], Raw (&rb)[TM]) {
 #pragma unroll
-  for (int i = 0; i < TN; ++i) {
-    const int row = rowa + i * 32;
-    ra[i].q = *reinterpret_cast<const uint4*>(st + a_off + swz_off<32>(row, lh));
-    ra[i].s = *reinterpret_cast<const uint16_t*>(st + sa_off + row * 4 + 2 * lh);
-  }
+  for (int i = 0; i < TN; ++i)
+    ra[i].q = *reinterpret_cast<const uint4*>(st + a_off + swz_off<128>(rowa + i * 32, 4 * lh + q));
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int row = rowb + j * 32;
-    rb[j].q = *reinterpret_cast<const uint4*>(st + b_off + swz_off<32>(row, lh));
-    rb[j].s = *reinterpret_cast<const uint16_t*>(st + sb_off + row * 4 + 2 * lh);
-  }
+  for (int j = 0; j < TM; ++j)
+    rb[j].q = *reinterpret_cast<const uint4*>(st + b_off + swz_off<128>(rowb + j * 32, 4 * lh + q));
 }
 
-// block scale byte b (0 or 1) of `s` as an f16 pair (E4M3 -> f16 is exact)
+// this lane's 8 block scales of a stage (blocks 8h .. 8h + 7 of the row)
+template <int TN, int TM>
+__device__ __forceinline__ void read_scales(const uint8_t* st, int sa_off, int sb_off, int rowa, int rowb, int lh,
+                                            uint2 (&sa)[TN], uint2 (&sb)[TM]) {
+#pragma unroll
+  for (int i = 0; i < TN; ++i) sa[i] = *reinterpret_cast<const uint2*>(st + sa_off + (rowa + i * 32) * 16 + 8 * lh);
+#pragma unroll
+  for (int j = 0; j < TM; ++j) sb[j] = *reinterpret_cast<const uint2*>(st + sb_off + (rowb + j * 32) * 16 + 8 * lh);
+}
+
+// block scale byte b (0..3) of `s` as an f16 pair (E4M3 -> f16 is exact)
 __device__ __forceinline__ v2h scale_pair(uint32_t s, int b) {
-  const uint32_t dup = __builtin_amdgcn_perm(s, s, b ? 0x01010101u : 0x00000000u);
+  const uint32_t dup = __builtin_amdgcn_perm(s, s, 0x01010101u * (uint32_t)b);
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dup, 1.0f, false);
 }
 
@@ -100,10 +109,10 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q) {
   return T == 0 ? q.x : T == 1 ? q.y : T == 2 ? q.z : q.w;
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4a4_kernel(DecArgs a) {
-  using C = W4Cfg<BM, BN, NS>;
+  using C = W4Cfg<BM, BN>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
@@ -122,13 +131,14 @@ void gemm_w4a4_kernel(DecArgs a) {
   const v4i rws = buffer_rsrc(a.ws + (int64_t)n0 * ks, (uint32_t)(rows_w * ks));
   const uint32_t lds0 = lds_offset(smem);
 
+  // fetch stage kt into buffer kt % 2 (stages past K read as zeros)
   auto issue_stage = [&](int kt) {
-    const int kb = kt * kKS;
-    const uint32_t base = lds0 + (uint32_t)((kt % NS) * C::STAGE);
+    const int kb = kt * kStageK;
+    const uint32_t base = lds0 + (uint32_t)((kt & 1) * C::STAGE);
     dma_region<typename C::RA>(rwq, base + C::A_OFF, wave, lane, kp, kb >> 1, kb, K);
     dma_region<typename C::RB>(rxq, base + C::B_OFF, wave, lane, kp, kb >> 1, kb, K);
-    dma_scales<typename C::SA>(rws, base + C::SA_OFF, wave, lane, ks, kb < K ? kb : kOutOfRange);
-    dma_scales<typename C::SB>(rxs, base + C::SB_OFF, wave, lane, ks, kb < K ? kb : kOutOfRange);
+    dma_region<typename C::SA>(rws, base + C::SA_OFF, wave, lane, ks, kb >> 4, kb, K);
+    dma_region<typename C::SB>(rxs, base + C::SB_OFF, wave, lane, ks, kb >> 4, kb, K);
   };
 
   v16f acc[TN][TM];
@@ -139,22 +149,27 @@ void gemm_w4a4_kernel(DecArgs a) {
 
   const int lr = lane & 31, lh = lane >> 5;
   const int rowa = wn * C::WN + lr, rowb = wm * C::WM + lr;  // region-local rows
-  const int nk = K / kKS;
+  const int nk = K / kStageK;
 
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue_stage(p);
-  wait_vmcnt<(NS - 2) * C::LOADS_MIN>();
-  __syncthreads();
-
-  Raw r0a[TN], r0b[TM], r1a[TN], r1b[TM];  // packed operands of the current / next stage
+  Raw r0a[TN], r0b[TM], r1a[TN], r1b[TM];  // packed operands of the current / next K group
+  uint2 s0a[TN], s0b[TM], s1a[TN], s1b[TM];  // block scales of the current / next stage
   v8h d0a[TN], d0b[TM], d1a[TN], d1b[TM];  // decoded operands of two consecutive K steps
-  v2h spa[TN][2], spb[TM][2];              // block-scale pairs of the stage being decoded
+  v2h spa[TN][2], spb[TM][2];              // block-scale pairs of the K group being decoded
 
-  auto scales_of = [&](const Raw (&ra)[TN], const Raw (&rb)[TM]) {
+  // scale pairs of K group q from the stage's scale bytes (bytes 2q, 2q + 1 of the lane's 8)
+  auto scales_of = [&](const uint2 (&sa)[TN], const uint2 (&sb)[TM], int q) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i) { spa[i][0] = scale_pair(ra[i].s, 0); spa[i][1] = scale_pair(ra[i].s, 1); }
+    for (int i = 0; i < TN; ++i) {
+      const uint32_t w = q < 2 ? sa[i].x : sa[i].y;
+      spa[i][0] = scale_pair(w, (2 * q) & 3);
+      spa[i][1] = scale_pair(w, (2 * q + 1) & 3);
+    }
 #pragma unroll
-    for (int j = 0; j < TM; ++j) { spb[j][0] = scale_pair(rb[j].s, 0); spb[j][1] = scale_pair(rb[j].s, 1); }
+    for (int j = 0; j < TM; ++j) {
+      const uint32_t w = q < 2 ? sb[j].x : sb[j].y;
+      spb[j][0] = scale_pair(w, (2 * q) & 3);
+      spb[j][1] = scale_pair(w, (2 * q + 1) & 3);
+    }
   };
   auto decode_step = [&](auto tc, const Raw (&ra)[TN], const Raw (&rb)[TM], v8h (&da)[TN], v8h (&db)[TM]) {
     constexpr int T = decltype(tc)::value;
@@ -170,7 +185,7 @@ void gemm_w4a4_kernel(DecArgs a) {
       for (int j = 0; j < TM; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[i], db[j], acc[i][j], 0, 0, 0);
   };
-  // one K step's MFMAs with the next step's decode (VALU) and reads (LDS) issued between them
+  // one K step's MFMAs with the next step's decode (VALU) and LDS reads issued between them
   auto pipeline = [&](auto vc, auto dc) {
     constexpr int NV = decltype(vc)::value, ND = decltype(dc)::value;
 #pragma unroll
@@ -185,43 +200,61 @@ void gemm_w4a4_kernel(DecArgs a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  constexpr int DEC_VALU = 8 * (TN + TM) / (TN * TM) + 1;  // decode VALU per MFMA (rounded up)
+  using NV = std::integral_constant<int, 8 * (TN + TM) / (TN * TM) + 1>;  // decode VALU per MFMA
+  using NV2 = std::integral_constant<int, 8 * (TN + TM) / (TN * TM) + 3>;
 
-  read_raw<TN, TM>(smem, C::A_OFF, C::B_OFF, C::SA_OFF, C::SB_OFF, rowa, rowb, lh, r0a, r0b);
-  scales_of(r0a, r0b);
-  decode_step(I0{}, r0a, r0b, d0a, d0b);
-
-  // stage s: its packed operands in ca/cb, K step 0 already decoded in d0; stage s + 1 is read
-  // into na/nb and its K step 0 decoded into d0 at the end. Past the last stage this reads a
-  // buffer of zeros (stages beyond K are fetched as zeros) and the result goes unused.
-  auto iteration = [&](int s, const Raw (&ca)[TN], const Raw (&cb)[TM], Raw (&na)[TN], Raw (&nb)[TM]) {
-    {
-      wait_vmcnt<(NS - 3) * C::LOADS_MIN>();  // this wave's share of stage s + 1 has landed
-      __syncthreads();                         // everybody's has; nobody reads stage s - 1 any more
-      issue_stage(s + NS - 1);
-      const uint8_t* st = smem + ((s + 1) % NS) * C::STAGE;
-      read_raw<TN, TM>(st, C::A_OFF, C::B_OFF, C::SA_OFF, C::SB_OFF, rowa, rowb, lh, na, nb);
-    }
+  // K group q of a stage: operands in ca/cb (K step 0 decoded in d0, scale pairs of the group
+  // in spa/spb); the next group's packed bytes are read into na/nb from `nst` (group nq, whose
+  // scales are in nsa/nsb) and its K step 0 decoded into d0
+  auto group = [&](const Raw (&ca)[TN], const Raw (&cb)[TM], Raw (&na)[TN], Raw (&nb)[TM], const uint8_t* nst,
+                   int nq, const uint2 (&nsa)[TN], const uint2 (&nsb)[TM]) {
+    read_raw<TN, TM>(nst, C::A_OFF, C::B_OFF, rowa, rowb, lh, nq, na, nb);
     decode_step(I1{}, ca, cb, d1a, d1b);
     mfmas(d0a, d0b);
-    pipeline(std::integral_constant<int, DEC_VALU>{}, std::integral_constant<int, 2>{});
+    pipeline(NV{}, std::integral_constant<int, 1>{});
     decode_step(I2{}, ca, cb, d0a, d0b);
     mfmas(d1a, d1b);
-    pipeline(std::integral_constant<int, DEC_VALU>{}, I0{});
+    pipeline(NV{}, I0{});
     decode_step(I3{}, ca, cb, d1a, d1b);
+    scales_of(nsa, nsb, nq);
     mfmas(d0a, d0b);
-    pipeline(std::integral_constant<int, DEC_VALU>{}, I0{});
-    scales_of(na, nb);
+    pipeline(NV2{}, I0{});
     decode_step(I0{}, na, nb, d0a, d0b);
     mfmas(d1a, d1b);
-    pipeline(std::integral_constant<int, DEC_VALU + 2>{}, I0{});
+    pipeline(NV{}, I0{});
+  };
+
+  issue_stage(0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  issue_stage(1);
+  read_raw<TN, TM>(smem, C::A_OFF, C::B_OFF, rowa, rowb, lh, 0, r0a, r0b);
+  read_scales<TN, TM>(smem, C::SA_OFF, C::SB_OFF, rowa, rowb, lh, s0a, s0b);
+  scales_of(s0a, s0b, 0);
+  decode_step(I0{}, r0a, r0b, d0a, d0b);
+
+  // Stage s sits in buffer s % 2 and stage s + 1 is in flight into the other one. Before the
+  // last K group reads ahead into stage s + 1, every wave waits for its share of stage s + 1,
+  // the barrier publishes it (and ends all reads of stage s), and stage s + 2 is fetched into
+  // buffer s % 2. Past the last stage the read-ahead sees a buffer of zeros and goes unused.
+  auto stage = [&](int s, const uint2 (&csa)[TN], const uint2 (&csb)[TM], uint2 (&nsa)[TN], uint2 (&nsb)[TM]) {
+    const uint8_t* cur = smem + (s & 1) * C::STAGE;
+    const uint8_t* nxt = smem + ((s + 1) & 1) * C::STAGE;
+    group(r0a, r0b, r1a, r1b, cur, 1, csa, csb);
+    group(r1a, r1b, r0a, r0b, cur, 2, csa, csb);
+    group(r0a, r0b, r1a, r1b, cur, 3, csa, csb);
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue_stage(s + 2);
+    read_scales<TN, TM>(nxt, C::SA_OFF, C::SB_OFF, rowa, rowb, lh, nsa, nsb);
+    group(r1a, r1b, r0a, r0b, nxt, 0, nsa, nsb);
   };
   int s = 0;
   for (; s + 1 < nk; s += 2) {
-    iteration(s, r0a, r0b, r1a, r1b);
-    iteration(s + 1, r1a, r1b, r0a, r0b);
+    stage(s, s0a, s0b, s1a, s1b);
+    stage(s + 1, s1a, s1b, s0a, s0b);
   }
-  if (s < nk) iteration(s, r0a, r0b, r1a, r1b);
+  if (s < nk) stage(s, s0a, s0b, s1a, s1b);
 
   // ---- epilogue: y = bf16(acc * gx * gw) via an LDS copy of the tile [BM][BN]
   const float alpha = a.gx[0] * a.gw[0];
@@ -246,21 +279,21 @@ void gemm_w4a4_kernel(DecArgs a) {
   store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid);
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN>
 hipError_t run(const DecArgs& a, hipStream_t s) {
   const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, NS>), dim3(tiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN>), dim3(tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kKS == 0; }
+bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kStageK == 0; }
 
 hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s) {
   const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (t256 >= 192) return run<256, 256, 4>(a, s);
-  return run<128, 128, 6>(a, s);
+  if (t256 >= 192) return run<256, 256>(a, s);
+  return run<128, 128>(a, s);
 }
 
 }  // namespace bsq

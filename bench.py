@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the block-scaled quantized linear layer on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic,
+seeded input, all inputs resident in HBM before the timed region:
+
+  * fp8r linear, 4096 tokens, K = 3072, N = 3072 (1 % outlier input channels):
+    per-row E4M3 activation quantization + FP8 GEMM with row-wise scales;
+  * nvfp4 linear, 4096 tokens, K = 3072, N = 12288 (MLP-up shape):
+    runtime nvfp4 activation quantization with the calibrated input_scale +
+    W4A4 GEMM on decoded operands;
+  * the fallback path: dequantization of both weight matrices to bf16.
+
+Weights are generated in bf16 and quantized (and their global scale
+calibrated) by the library itself before timing. `value` is the step's GEMM
+work (2 M N K for both GEMMs) divided by the step time. The dominant kernel's
+roofline entry uses per-launch durations measured with HIP events on the
+launch stream; its HBM traffic comes from the rocprofv3 counter summary in
+profiles/ when that summary was taken on the current kernel source.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + % MFMA peak for nvfp4/fp8r GEMM at M=4096,K=3072; HBM GB/s"
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+M, K, N_FP8, N_FP4 = 4096, 3072, 3072, 12288
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_4096x12288x3072_traffic.json")
+DOMINANT_SRC = os.path.join(ROOT, "block_scaled_precision_row_amd", "csrc", "gemm_w4a4.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash(DOMINANT_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(rows=64, reps=2):
+    """The CPU oracle on a bounded sample of the same step: `rows` tokens of each linear.
+
+    Per repetition the oracle quantizes the sampled activations, dequantizes
+    both weight matrices (exact values and the bf16 fallback copies) and forms
+    the fp64 products. The value is the sampled GEMM work (2 rows N K summed
+    over both linears) per second, in TFLOP/s.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from block_scaled_precision_row_amd import synthetic as syn
+    from oracle import dequant, gemm, quant
+
+    x2 = syn.activations(syn.FP8R_4096, M, K)[:rows]
+    x3 = syn.activations(syn.NVFP4_UP, M, K)[:rows]
+    w2 = syn.weights(syn.FP8R_4096, N_FP8, K)
+    w3 = syn.weights(syn.NVFP4_UP, N_FP4, K)
+    w2q, w2s = quant.quantize_fp8r(w2)
+    g3 = quant.calibrate_global_scale(w3)
+    w3q, w3s = quant.quantize_nvfp4(w3, g3)
+    gx3 = quant.calibrate_global_scale(syn.activations(syn.NVFP4_UP, M, K))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        xq, sx = quant.quantize_fp8r(x2)
+        gemm.gemm_fp8r(xq, sx, w2q, w2s)
+        xq3, sx3 = quant.quantize_nvfp4(x3, gx3)
+        gemm.gemm_nvfp4(xq3, sx3, gx3, w3q, w3s, g3)
+        dequant.dequant_fp8r_bf16(w2q, w2s)
+        dequant.dequant_nvfp4_bf16(w3q, w3s, g3)
+    dt = (time.perf_counter() - t0) / reps
+    flops = 2.0 * rows * K * (N_FP8 + N_FP4)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of %d tokens of both linears per step (weights dequantized in full), %d steps, %.2f s/step"
+                      % (rows, M, reps, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (requested %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_scaled_precision_row_amd import _lib as L
+    from block_scaled_precision_row_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up_bf16(bits):
+        return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
+
+    log("generating inputs")
+    x2 = up_bf16(syn.activations(syn.FP8R_4096, M, K))
+    x3 = up_bf16(syn.activations(syn.NVFP4_UP, M, K))
+    w2 = up_bf16(syn.weights(syn.FP8R_4096, N_FP8, K))
+    w3 = up_bf16(syn.weights(syn.NVFP4_UP, N_FP4, K))
+    # weights to their storage formats, global scales calibrated, by the library
+    w2q, w2s = L.bsq_quantize_act_fp8r(w2)
+    g3 = L.bsq_calibrate_global_scale(w3)
+    w3q, w3s = L.bsq_quantize_act_nvfp4(w3, g3)
+    gx3 = L.bsq_calibrate_global_scale(x3)
+    del w2, w3
+    x2q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    x2s = torch.empty((M,), dtype=torch.float32, device=dev)
+    x3q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    x3s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    y2 = torch.empty((M, N_FP8), dtype=torch.bfloat16, device=dev)
+    y3 = torch.empty((M, N_FP4), dtype=torch.bfloat16, device=dev)
+    wd2 = torch.empty((N_FP8, K), dtype=torch.bfloat16, device=dev)
+    wd3 = torch.empty((N_FP4, K), dtype=torch.bfloat16, device=dev)
+
+    # the timed loop calls the C entry points directly (argument tuples built once) so that host
+    # overhead stays far below the GPU time of a step
+    P = lambda t: t.data_ptr()
+    lib = L.lib
+    parts = ["quant_fp8r", "gemm_fp8r", "quant_nvfp4", "gemm_nvfp4", "dequant_fp8r", "dequant_nvfp4"]
+
+    def calls(stream):
+        return [
+            (lib.bsq_quantize_act_fp8r, (P(x2), M, K, K, P(x2q), P(x2s), stream)),
+            (lib.bsq_gemm_fp8r_q, (P(x2q), P(x2s), P(w2q), P(w2s), P(y2), N_FP8, M, N_FP8, K, stream)),
+            (lib.bsq_quantize_act_nvfp4, (P(x3), M, K, K, P(gx3), P(x3q), P(x3s), stream)),
+            (lib.bsq_gemm_nvfp4_q, (P(x3q), P(x3s), P(gx3), P(w3q), P(w3s), P(g3), P(y3), N_FP4, M, N_FP4, K, stream)),
+            (lib.bsq_dequant_to_bf16, (L.BSQ_FMT_FP8R, P(w2q), P(w2s), None, N_FP8, K, P(wd2), stream)),
+            (lib.bsq_dequant_to_bf16, (L.BSQ_FMT_NVFP4, P(w3q), P(w3s), P(g3), N_FP4, K, P(wd3), stream)),
+        ]
+    stream = torch.cuda.current_stream().cuda_stream
+    seq = calls(stream)
+    DOM = parts.index("gemm_nvfp4")
+
+    def step(ev=None):
+        for i, (fn, a) in enumerate(seq):
+            if ev is not None and i == DOM:
+                ev[0].record()
+            st = fn(*a)
+            if st != 0:
+                raise L.BsqError(fn.__name__, st)
+            if ev is not None and i == DOM:
+                ev[1].record()
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log("timing %d steps" % args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+
+    # per-kernel averages (outside the timed region): each call back to back between two events
+    per_kernel = {}
+    for i, p in enumerate(parts):
+        fn, a = seq[i]
+        reps = 5 if i == DOM else 40
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn(*a)
+        e0.record()
+        for _ in range(reps):
+            fn(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        per_kernel[p] = e0.elapsed_time(e1) / reps  # ms
+    per_kernel["gemm_nvfp4"] = dom_ms
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.0 * M * K * (N_FP8 + N_FP4)
+    value = flops * args.steps / wall / 1e12
+
+    g4_us = per_kernel["gemm_nvfp4"] * 1e3
+    g4_tflops = 2.0 * M * N_FP4 * K / (g4_us * 1e-6) / 1e12
+    g8_us = per_kernel["gemm_fp8r"] * 1e3
+    g8_tflops = 2.0 * M * N_FP8 * K / (g8_us * 1e-6) / 1e12
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    hbm = {
+        "quant_fp8r": gbs(M * K * 2 + M * K + 4 * M, per_kernel["quant_fp8r"]),
+        "quant_nvfp4": gbs(M * K * 2 + M * K // 2 + M * K // 16, per_kernel["quant_nvfp4"]),
+        "dequant_fp8r": gbs(N_FP8 * K + 4 * N_FP8 + N_FP8 * K * 2, per_kernel["dequant_fp8r"]),
+        "dequant_nvfp4": gbs(N_FP4 * K // 2 + N_FP4 * K // 16 + 4 + N_FP4 * K * 2, per_kernel["dequant_nvfp4"]),
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8,f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fp8r W8A8 linear 4096x3072x3072 (1% outlier channels) + nvfp4 W4A4 linear "
+                        "4096x12288x3072 (MLP-up) + bf16 dequant fallback of both weights, one GPU",
+            "tokens": M, "K": K, "N_fp8r": N_FP8, "N_nvfp4": N_FP4,
+        },
+        "roofline": {
+            "kernel": "gemm_w4a4 (nvfp4 W4A4 GEMM, 4096x12288x3072, f16 MFMA on decoded operands)",
+            "bound": "mfma",
+            "achieved": round(g4_tflops, 1),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(g4_tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": measured_traffic(),
+        },
+        "kernels_us": {p: round(v * 1e3, 2) for p, v in per_kernel.items()},
+        "kernels_us_note": "gemm_nvfp4: HIP events around each launch in the timed steps; others: back-to-back "
+                           "launches between two events after the timed region",
+        "gemm_fp8r": {"tflops": round(g8_tflops, 1), "frac_fp8_peak": round(g8_tflops / PEAK_FP8_TFLOPS, 4)},
+        "gemm_nvfp4": {"tflops": round(g4_tflops, 1), "frac_f16_peak": round(g4_tflops / PEAK_F16_TFLOPS, 4),
+                       "frac_fp4_peak": round(g4_tflops / 10100.0, 4)},
+        "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
+        "hbm_frac": {k: round(v / PEAK_HBM_GBS, 4) for k, v in hbm.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline()
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

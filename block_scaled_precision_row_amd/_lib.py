@@ -38,6 +38,8 @@ SIGNATURES = {
     "bsq_gemm_fp8r": (_int, [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz, _p]),
     "bsq_gemm_nvfp4": (_int, [_p, _i64, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz, _p]),
     "bsq_dequant_to_bf16": (_int, [_int, _p, _p, _p, _i64, _i64, _p, _p]),
+    "bsq_gemm_fp8r_q": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
+    "bsq_gemm_nvfp4_q": (_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
 }
 
 
@@ -177,6 +179,39 @@ def bsq_gemm_nvfp4(x, w, w_bscale, w_scale2, input_scale=None, flags=0, y=None, 
     _check("bsq_gemm_nvfp4", lib.bsq_gemm_nvfp4(_ptr(x), ldx, _ptr(w), _ptr(w_bscale), _ptr(w_scale2),
                                                 _ptr(input_scale), _ptr(y), ldy, M, N, K, flags, _ptr(ws), nbytes,
                                                 _stream()))
+    return y
+
+
+def bsq_gemm_fp8r_q(xq, x_scale, w, w_scale, y=None):
+    """E4M3 xq [M, K] with fp32 row scales [M], E4M3 w [N, K], fp32 w_scale [N] -> bf16 y [M, N]."""
+    M, K = xq.shape
+    N = w.shape[0]
+    _dense(xq, torch.uint8, (M, K), "xq")
+    _dense(x_scale, torch.float32, (M,), "x_scale")
+    _dense(w, torch.uint8, (N, K), "w")
+    _dense(w_scale, torch.float32, (N,), "w_scale")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    _check("bsq_gemm_fp8r_q", lib.bsq_gemm_fp8r_q(_ptr(xq), _ptr(x_scale), _ptr(w), _ptr(w_scale), _ptr(y), ldy,
+                                                  M, N, K, _stream()))
+    return y
+
+
+def bsq_gemm_nvfp4_q(xq, x_bscale, input_scale, w, w_bscale, w_scale2, y=None):
+    """packed E2M1 xq [M, K/2] + E4M3 x_bscale [M, K/16] + input_scale [1], nvfp4 weights -> bf16 y [M, N]."""
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = w.shape[0]
+    _dense(xq, torch.uint8, (M, K // 2), "xq")
+    _dense(x_bscale, torch.uint8, (M, K // 16), "x_bscale")
+    _scalar(input_scale, "input_scale")
+    _dense(w, torch.uint8, (N, K // 2), "w")
+    _dense(w_bscale, torch.uint8, (N, K // 16), "w_bscale")
+    _scalar(w_scale2, "w_scale2")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    _check("bsq_gemm_nvfp4_q", lib.bsq_gemm_nvfp4_q(_ptr(xq), _ptr(x_bscale), _ptr(input_scale), _ptr(w),
+                                                    _ptr(w_bscale), _ptr(w_scale2), _ptr(y), ldy, M, N, K,
+                                                    _stream()))
     return y
 
 

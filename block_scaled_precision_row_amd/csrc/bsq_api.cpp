@@ -209,6 +209,34 @@ bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, cons
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
+bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  // xq rows are dense (ld = K); reuse the common checks with ldx = K
+  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w, y, ldy, M, N, K, 0);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!x_scale || !w_scale) return BSQ_ERR_NULL;
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e = bsq::launch_gemm_fp8(xq, x_scale, w, w_scale, y, ldy, M, N, K, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
+                            const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2, uint16_t* y,
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w, y, ldy, M, N, K, 0);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!x_bscale || !input_scale || !w_bscale || !w_scale2) return BSQ_ERR_NULL;
+  if (!aligned(x_bscale, 4) || !aligned(input_scale, 4) || !aligned(w_bscale, 4) || !aligned(w_scale2, 4))
+    return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  bsq::DecArgs a{};
+  a.xq = xq; a.xs = x_bscale; a.gx = input_scale; a.w = w; a.ws = w_bscale; a.gw = w_scale2;
+  a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
+  hipError_t e = bsq::launch_gemm_dec(bsq::kW4A4, a, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
 bsq_status bsq_dequant_to_bf16(bsq_format f, const uint8_t* w, const void* w_scale, const float* w_scale2,
                                int64_t N, int64_t K, uint16_t* w_bf16, hipStream_t stream) {
   if (f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;

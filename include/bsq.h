@@ -157,6 +157,22 @@ bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, cons
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same two GEMMs on activations that are already quantized (laid out as
+ * bsq_quantize_act_fp8r / bsq_quantize_act_nvfp4 write them), for callers
+ * that quantize X elsewhere -- e.g. once for several linears sharing an
+ * input. Arithmetic, layouts and rounding are those of the W8A8 and W4A4
+ * paths above; no workspace is needed.
+ *   bsq_gemm_fp8r_q : xq [M][K] E4M3, x_scale [M] fp32 (16-byte aligned xq)
+ *   bsq_gemm_nvfp4_q: xq [M][K/2] packed E2M1, x_bscale [M][K/16] E4M3,
+ *                     input_scale [1] fp32
+ */
+bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
+                            const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2, uint16_t* y,
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Fallback dequantization to bf16 ("BFL (fp8r / nvfp4)", last paragraph of
  * "Kernels": on other devices the weights are dequantized to the compute
  * dtype every forward and the layer runs as a regular linear):

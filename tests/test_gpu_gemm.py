@@ -164,3 +164,21 @@ def test_strided_activations_and_output():
     assert np.all(host(ybig)[:, N:] == 0)
     assert_gemm_close(host(ybig2)[:, :N], gemm.gemm_nvfp4_weight_only(x, p, s, gw), "strided w4a16")
     assert np.all(host(ybig2)[:, N:] == 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 12288, 3072), (77, 100, 96), (300, 520, 1056), (256, 256, 512)])
+def test_prequantized_activation_entry_points(M, N, K):
+    """GEMMs on oracle-quantized activations: the same bytes on both sides, so only the GEMM is under test."""
+    x = syn.normal_bf16((M, K), 53, M)
+    w = syn.normal_bf16((N, K), 53, N, sigma=0.02)
+    rows = _rows_subset(M, 256, 7)
+    gx, gw = quant.calibrate_global_scale(x), quant.calibrate_global_scale(w)
+    xq, sfx = quant.quantize_nvfp4(x, gx)
+    wq, sfw = quant.quantize_nvfp4(w, gw)
+    y = L.bsq_gemm_nvfp4_q(dev(xq), dev(sfx), dev_scalar(gx), dev(wq), dev(sfw), dev_scalar(gw))
+    x8, s8 = quant.quantize_fp8r(x)
+    w8, t8 = quant.quantize_fp8r(w)
+    y8 = L.bsq_gemm_fp8r_q(dev(x8), dev(s8), dev(w8), dev(t8))
+    torch.cuda.synchronize()
+    assert_gemm_close(host(y)[rows], gemm.gemm_nvfp4(xq[rows], sfx[rows], gx, wq, sfw, gw), "nvfp4_q %dx%dx%d" % (M, N, K))
+    assert_gemm_close(host(y8)[rows], gemm.gemm_fp8r(x8[rows], s8[rows], w8, t8), "fp8r_q %dx%dx%d" % (M, N, K))

@@ -8,12 +8,19 @@
 // epilogue; the K loop is a plain E4M3 x E4M3 -> fp32 contraction on
 // v_mfma_f32_32x32x64_f8f6f4 (no per-block scaling inside the loop).
 //
-// Pipeline (layout conventions in gemm_common.hpp): each stage is 64 K
-// values = 64 bytes of every W row and every Xq row, fetched by LDS DMA into
-// a ring of NS stage buffers. Iteration s waits until stage s + 1 has landed,
-// refills the buffer of stage s - 1 with stage s + NS - 1, reads the operands
-// of stage s + 1 into registers and runs the MFMAs of stage s, so NS - 2
-// stages of DMA are always in flight behind the one being multiplied.
+// Pipeline (layout conventions in gemm_common.hpp): each stage is 128 K
+// values = 128 bytes (one full cache line) of every W row and every Xq row,
+// fetched by LDS DMA into a ring of NS stage buffers; full-line rows halve
+// the number of memory requests against 64-byte stages. A stage is two
+// 64-deep MFMA K steps. Iteration s reads step 1 of stage s into registers
+// while the MFMAs of step 0 run, waits until stage s + 1 has landed, and at
+// the barrier that follows no wave reads stage s any more, so its buffer is
+// refilled with stage s + NS at once; step 0 of stage s + 1 is then read
+// while the MFMAs of step 1 run. NS - 1 stages are in flight behind the one
+// being multiplied.
+// K permutation: in step t of a stage, lane half h of an MFMA operand holds
+// the 32 bytes [64 h + 32 t, 64 h + 32 t + 32) of its row -- the same for W
+// and Xq, so every product pairs equal K indices.
 // The epilogue scales the accumulators, converts them to bf16 into an LDS
 // copy of the output tile, and writes the tile back in 16-byte row chunks.
 #include "gemm_common.hpp"
@@ -25,37 +32,42 @@ namespace {
 
 using namespace gemm;
 
+constexpr int kStageK = 128;  // K values (bytes) per row per stage
+
 template <int BM, int BN, int NS>
 struct Cfg {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  using RA = Region<64, BN>;  // W rows
-  using RB = Region<64, BM>;  // Xq rows
-  static constexpr int A_BYTES = BN * 64, STAGE = (BN + BM) * 64;
+  using RA = Region<128, BN, kStageK>;  // W rows
+  using RB = Region<128, BM, kStageK>;  // Xq rows
+  static constexpr int A_BYTES = BN * 128, STAGE = (BN + BM) * 128;
   static constexpr int LOADS_MIN = RA::MIN_PER_WAVE + RB::MIN_PER_WAVE;  // per wave per stage
   static constexpr int TROW = BN * 2 + 16;  // bytes per row of the bf16 output tile in LDS (padded)
   static constexpr int LDS = NS * STAGE > BM * TROW ? NS * STAGE : BM * TROW;
-  static_assert(NS >= 3, "at least one stage in flight behind the next");
-  static_assert((NS - 3) * LOADS_MIN < 64, "vmcnt range");
+  static_assert(NS >= 2, "one stage in flight behind the one being multiplied");
+  static_assert(RA::MIN_PER_WAVE == RA::MAX_PER_WAVE && RB::MIN_PER_WAVE == RB::MAX_PER_WAVE,
+                "every wave issues the same number of loads (exact vmcnt accounting)");
+  static_assert((NS - 1) * LOADS_MIN < 64, "vmcnt range");
   static_assert(LDS + 4 * (BM + BN) <= 160 * 1024, "LDS budget");
 };
 
-// operands of one 64-deep K step: W rows from region A at `base`, Xq rows from region B at `bbase`
+// operands of K step t (0 or 1) of a stage: W rows from region A at `base`, Xq rows from region B at `bbase`
 template <int TN, int TM>
-__device__ __forceinline__ void read_ops(const uint8_t* base, const uint8_t* bbase, int rowa, int rowb, int lh,
+__device__ __forceinline__ void read_ops(const uint8_t* base, const uint8_t* bbase, int rowa, int rowb, int lh, int t,
                                          v8i (&a)[TN], v8i (&b)[TM]) {
+  const int c = 4 * lh + 2 * t;
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
     const int row = rowa + i * 32;
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + swz_off<64>(row, 2 * lh));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + swz_off<64>(row, 2 * lh + 1));
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + swz_off<128>(row, c));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + swz_off<128>(row, c + 1));
     a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int row = rowb + j * 32;
-    const uint4 lo = *reinterpret_cast<const uint4*>(bbase + swz_off<64>(row, 2 * lh));
-    const uint4 hi = *reinterpret_cast<const uint4*>(bbase + swz_off<64>(row, 2 * lh + 1));
+    const uint4 lo = *reinterpret_cast<const uint4*>(bbase + swz_off<128>(row, c));
+    const uint4 hi = *reinterpret_cast<const uint4*>(bbase + swz_off<128>(row, c + 1));
     b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 }
@@ -92,7 +104,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   const uint32_t lds0 = lds_offset(smem);
 
   auto issue_stage = [&](int kt) {
-    const int kb = kt * kKS;
+    const int kb = kt * kStageK;
     const uint32_t base = lds0 + (uint32_t)((kt % NS) * C::STAGE);
     dma_region<typename C::RA>(rw, base, wave, lane, K, kb, kb, K);
     dma_region<typename C::RB>(rx, base + C::A_BYTES, wave, lane, K, kb, kb, K);
@@ -110,40 +122,38 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
 
   const int lr = lane & 31, lh = lane >> 5;
   const int rowa = wn * C::WN + lr, rowb = wm * C::WM + lr;  // region-local rows
-  const int nk = (K + kKS - 1) / kKS;
+  const int nk = (K + kStageK - 1) / kStageK;
 
-  // prologue: NS - 1 stages in flight, wait for the first
+  // prologue: NS stages in flight, wait for the first
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue_stage(p);
-  wait_vmcnt<(NS - 2) * C::LOADS_MIN>();
+  for (int p = 0; p < NS; ++p) issue_stage(p);
+  wait_vmcnt<(NS - 1) * C::LOADS_MIN>();
   __syncthreads();
   v8i a0[TN], b0[TM], a1[TN], b1[TM];
-  read_ops<TN, TM>(smem, smem + C::A_BYTES, rowa, rowb, lh, a0, b0);
+  read_ops<TN, TM>(smem, smem + C::A_BYTES, rowa, rowb, lh, 0, a0, b0);
 
-  // iteration s: MFMAs of stage s (operands in `ca`/`cb`) while stage s + 1 is read into `na`/`nb`
-  auto iteration = [&](int s, v8i (&ca)[TN], v8i (&cb)[TM], v8i (&na)[TN], v8i (&nb)[TM]) {
-    wait_vmcnt<(NS - 3) * C::LOADS_MIN>();  // this wave's share of stage s + 1 has landed
-    __syncthreads();                         // everybody's has; nobody reads stage s - 1 any more
-    issue_stage(s + NS - 1);                 // refill the buffer of stage s - 1 (zeros past K)
-    const uint8_t* nxt = smem + ((s + 1) % NS) * C::STAGE;
-    read_ops<TN, TM>(nxt, nxt + C::A_BYTES, rowa, rowb, lh, na, nb);
-    mfma_all<TN, TM>(acc, ca, cb);
+  // MFMAs of one K step with the LDS reads of the next one interleaved
+  auto sched = [&]() {
 #pragma unroll
     for (int i = 0; i < TN * TM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, (2 * (TN + TM) + TN * TM - 1) / (TN * TM), 0);  // LDS read
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  int s = 0;
-  for (; s + 2 < nk; s += 2) {
-    iteration(s, a0, b0, a1, b1);
-    iteration(s + 1, a1, b1, a0, b0);
-  }
-  if (s + 1 < nk) {
-    iteration(s, a0, b0, a1, b1);
-    mfma_all<TN, TM>(acc, a1, b1);
-  } else {
+  // stage s, its step 0 already in a0/b0. Stages past K read as zeros and go unused.
+  for (int s = 0; s < nk; ++s) {
+    const uint8_t* cur = smem + (s % NS) * C::STAGE;
+    const uint8_t* nxt = smem + ((s + 1) % NS) * C::STAGE;
+    read_ops<TN, TM>(cur, cur + C::A_BYTES, rowa, rowb, lh, 1, a1, b1);
     mfma_all<TN, TM>(acc, a0, b0);
+    sched();
+    wait_vmcnt<(NS - 2) * C::LOADS_MIN>();  // this wave's share of stage s + 1 has landed
+    __syncthreads();                         // everybody's has; nobody reads stage s any more
+    issue_stage(s + NS);                     // refill the buffer of stage s
+    read_ops<TN, TM>(nxt, nxt + C::A_BYTES, rowa, rowb, lh, 0, a0, b0);
+    mfma_all<TN, TM>(acc, a1, b1);
+    sched();
   }
 
   // ---- epilogue: y = bf16(acc * sx[m] * sw[n]) via an LDS copy of the tile [BM][BN]
@@ -185,8 +195,8 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w,
                            uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   // pick the tile whose grid best fills the 256 compute units
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
-  if (t192 >= 192) return run<256, 192, 5>(xq, sx, w, sw, y, ldy, M, N, K, s);
-  return run<128, 128, 6>(xq, sx, w, sw, y, ldy, M, N, K, s);
+  if (t192 >= 192) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, s);
+  return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, s);
 }
 
 }  // namespace bsq

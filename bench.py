@@ -21,7 +21,6 @@ profiles/ when that summary was taken on the current kernel source.
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,16 +35,10 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 M, K, N_FP8, N_FP4 = 4096, 3072, 3072, 12288
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_4096x12288x3072_traffic.json")
-DOMINANT_SRC = os.path.join(ROOT, "block_scaled_precision_row_amd", "csrc", "gemm_w4a4.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
 
 
 def measured_traffic():
@@ -55,7 +48,8 @@ def measured_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_hash(DOMINANT_SRC):
+    from block_scaled_precision_row_amd import traffic
+    if t.get("source_sha256") != traffic.source_hash():
         return None
     return t.get("bytes_per_launch")
 

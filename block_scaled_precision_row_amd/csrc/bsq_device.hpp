@@ -90,6 +90,14 @@ __device__ __forceinline__ v2h dec_e2m1x2_f16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, sel);
 }
 
+// ---- streaming stores ----------------------------------------------------------
+// 16-byte store with the non-temporal hint, for outputs that this kernel does
+// not read back (dequantized weights, GEMM results)
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
+}
+
 // ---- wave reductions ----------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -8,75 +8,104 @@
 
 namespace bsq {
 
-// one thread per 16 packed bytes = 32 values = two 16-element blocks
-template <int sel>
-__device__ __forceinline__ uint32_t nvfp4_pair_bf16(uint32_t w, float sf, float g) {
-  const v2f e = dec_e2m1x2_f32<sel>(w);
-  return pack_bf16x2((e.x * sf) * g, (e.y * sf) * g);
+// Both kernels walk their output in 8-value (16-byte) chunks with consecutive
+// lanes on consecutive chunks, so every store instruction of a wave writes one
+// contiguous kilobyte and every load instruction reads a contiguous span.
+// The output is written with non-temporal stores: it is not read again here,
+// and streaming it past the caches measured about 5 % faster than plain stores.
+
+// nvfp4: chunk c of the flattened [N][K] output takes packed bytes [4c, 4c + 4)
+// and block scale c / 2 (a row of K values has K / 8 chunks and K / 16
+// scales), so no row index is needed. A thread loads all CPT of its chunks
+// before converting any, to keep many loads in flight; small tensors use a
+// smaller CPT so that the grid still covers every compute unit.
+
+__device__ __forceinline__ uint4 nvfp4_chunk_bf16(uint32_t w, float sf, float g) {
+  uint4 o;
+  v2f e = dec_e2m1x2_f32<0>(w);
+  o.x = pack_bf16x2((e.x * sf) * g, (e.y * sf) * g);
+  e = dec_e2m1x2_f32<1>(w);
+  o.y = pack_bf16x2((e.x * sf) * g, (e.y * sf) * g);
+  e = dec_e2m1x2_f32<2>(w);
+  o.z = pack_bf16x2((e.x * sf) * g, (e.y * sf) * g);
+  e = dec_e2m1x2_f32<3>(w);
+  o.w = pack_bf16x2((e.x * sf) * g, (e.y * sf) * g);
+  return o;
 }
 
-__global__ __launch_bounds__(256) void dequant_nvfp4_kernel(const uint8_t* __restrict__ w,
+template <int CPT>
+__global__ __launch_bounds__(256) void dequant_nvfp4_kernel(const uint32_t* __restrict__ w,
                                                              const uint8_t* __restrict__ sf,
-                                                             const float* __restrict__ gptr, int64_t N,
-                                                             int K, uint16_t* __restrict__ out) {
-  const int per_row = K >> 5;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= N * per_row) return;
-  const int64_t row = t / per_row;
-  const int c = (int)(t - row * per_row);
-  const uint4 q = *reinterpret_cast<const uint4*>(w + row * (int64_t)(K >> 1) + (int64_t)c * 16);
-  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sf + row * (int64_t)(K >> 4) + (int64_t)c * 2);
-  const float s0 = dec_e4m3<0>(s2), s1 = dec_e4m3<1>(s2);
+                                                             const float* __restrict__ gptr, int64_t chunks,
+                                                             uint4* __restrict__ out) {
+  const int64_t c0 = (int64_t)blockIdx.x * (256 * CPT) + threadIdx.x;
   const float g = gptr[0];
-  uint4 o0, o1, o2, o3;
-  o0.x = nvfp4_pair_bf16<0>(q.x, s0, g); o0.y = nvfp4_pair_bf16<1>(q.x, s0, g);
-  o0.z = nvfp4_pair_bf16<2>(q.x, s0, g); o0.w = nvfp4_pair_bf16<3>(q.x, s0, g);
-  o1.x = nvfp4_pair_bf16<0>(q.y, s0, g); o1.y = nvfp4_pair_bf16<1>(q.y, s0, g);
-  o1.z = nvfp4_pair_bf16<2>(q.y, s0, g); o1.w = nvfp4_pair_bf16<3>(q.y, s0, g);
-  o2.x = nvfp4_pair_bf16<0>(q.z, s1, g); o2.y = nvfp4_pair_bf16<1>(q.z, s1, g);
-  o2.z = nvfp4_pair_bf16<2>(q.z, s1, g); o2.w = nvfp4_pair_bf16<3>(q.z, s1, g);
-  o3.x = nvfp4_pair_bf16<0>(q.w, s1, g); o3.y = nvfp4_pair_bf16<1>(q.w, s1, g);
-  o3.z = nvfp4_pair_bf16<2>(q.w, s1, g); o3.w = nvfp4_pair_bf16<3>(q.w, s1, g);
-  uint4* dst = reinterpret_cast<uint4*>(out + row * (int64_t)K + (int64_t)c * 32);
-  dst[0] = o0; dst[1] = o1; dst[2] = o2; dst[3] = o3;
+  uint32_t q[CPT];
+  uint32_t s[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int64_t c = c0 + 256 * i;
+    if (c < chunks) {
+      q[i] = w[c];
+      s[i] = sf[c >> 1];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int64_t c = c0 + 256 * i;
+    if (c < chunks) store_stream(out + c, nvfp4_chunk_bf16(q[i], dec_e4m3<0>(s[i]), g));
+  }
 }
 
 hipError_t launch_dequant_nvfp4(const uint8_t* w, const uint8_t* sf, const float* g, int64_t N,
                                 int64_t K, uint16_t* out, hipStream_t s) {
-  const int64_t total = N * (K >> 5);
-  hipLaunchKernelGGL(dequant_nvfp4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, sf,
-                     g, N, (int)K, out);
+  const int64_t chunks = N * (K >> 3);
+  const uint32_t* wq = reinterpret_cast<const uint32_t*>(w);
+  uint4* o = reinterpret_cast<uint4*>(out);
+  constexpr int64_t kBig = 256 * 16, kSmall = 256 * 4;  // chunks per block
+  if (chunks >= 1024 * kBig)
+    hipLaunchKernelGGL(dequant_nvfp4_kernel<16>, dim3((unsigned)((chunks + kBig - 1) / kBig)), dim3(256), 0, s, wq,
+                       sf, g, chunks, o);
+  else
+    hipLaunchKernelGGL(dequant_nvfp4_kernel<4>, dim3((unsigned)((chunks + kSmall - 1) / kSmall)), dim3(256), 0, s,
+                       wq, sf, g, chunks, o);
   return hipGetLastError();
 }
 
-// one thread per 16 E4M3 codes
-__device__ __forceinline__ uint2 fp8_quad_bf16(uint32_t w, float d) {
-  const v2f a = dec_e4m3x2<false>(w), b = dec_e4m3x2<true>(w);
-  return make_uint2(pack_bf16x2(a.x * d, a.y * d), pack_bf16x2(b.x * d, b.y * d));
+// fp8r: one wave per row (the row scale is loaded once); lane l takes the
+// 8-code chunks l, l + 64, ... of the row.
+__device__ __forceinline__ uint4 fp8_chunk_bf16(uint2 q, float d) {
+  const v2f a = dec_e4m3x2<false>(q.x), b = dec_e4m3x2<true>(q.x);
+  const v2f e = dec_e4m3x2<false>(q.y), f = dec_e4m3x2<true>(q.y);
+  return make_uint4(pack_bf16x2(a.x * d, a.y * d), pack_bf16x2(b.x * d, b.y * d), pack_bf16x2(e.x * d, e.y * d),
+                    pack_bf16x2(f.x * d, f.y * d));
 }
 
 __global__ __launch_bounds__(256) void dequant_fp8r_kernel(const uint8_t* __restrict__ w,
                                                             const float* __restrict__ sw, int64_t N, int K,
                                                             uint16_t* __restrict__ out) {
-  const int per_row = K >> 4;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= N * per_row) return;
-  const int64_t row = t / per_row;
-  const int c = (int)(t - row * per_row);
-  const uint4 q = *reinterpret_cast<const uint4*>(w + row * (int64_t)K + (int64_t)c * 16);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const uint2* src = reinterpret_cast<const uint2*>(w + row * (int64_t)K);
+  uint4* dst = reinterpret_cast<uint4*>(out + row * (int64_t)K);
   const float d = sw[row];
-  const uint2 a = fp8_quad_bf16(q.x, d), b = fp8_quad_bf16(q.y, d);
-  const uint2 e = fp8_quad_bf16(q.z, d), f = fp8_quad_bf16(q.w, d);
-  uint4* dst = reinterpret_cast<uint4*>(out + row * (int64_t)K + (int64_t)c * 16);
-  dst[0] = make_uint4(a.x, a.y, b.x, b.y);
-  dst[1] = make_uint4(e.x, e.y, f.x, f.y);
+  const int cpr = K >> 3;
+  constexpr int U = 8;
+  for (int c = lane; c < cpr; c += 64 * U) {
+    uint2 q[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (c + 64 * i < cpr) q[i] = src[c + 64 * i];
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (c + 64 * i < cpr) store_stream(dst + c + 64 * i, fp8_chunk_bf16(q[i], d));
+  }
 }
 
 hipError_t launch_dequant_fp8r(const uint8_t* w, const float* sw, int64_t N, int64_t K, uint16_t* out,
                                hipStream_t s) {
-  const int64_t total = N * (K >> 4);
-  hipLaunchKernelGGL(dequant_fp8r_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, sw,
-                     N, (int)K, out);
+  hipLaunchKernelGGL(dequant_fp8r_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, w, sw, N, (int)K, out);
   return hipGetLastError();
 }
 

@@ -152,7 +152,7 @@ __device__ __forceinline__ void store_tile_rows(const uint8_t* tile, uint16_t* _
     const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * TROW + c * 16);
     uint16_t* dst = y + (int64_t)m * ldy + n;
     if (n + 8 <= N && vec_ok) {
-      *reinterpret_cast<uint4*>(dst) = v;
+      store_stream(reinterpret_cast<uint4*>(dst), v);
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -12,7 +12,7 @@ Two steps, run on one MI355X:
          <d2>/run_counter_collection.csv
      scales each counter by COPY_BYTES / (the counter's reading for the copy kernel),
      takes the GEMM's mean per launch and writes
-     profiles/gemm_w4a4_4096x12288x3072_traffic.json with the hash of the kernel source.
+     profiles/gemm_w4a4_4096x12288x3072_traffic.json with the hash of the kernel's sources.
 """
 import csv
 import hashlib
@@ -21,7 +21,17 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "block_scaled_precision_row_amd", "csrc", "gemm_w4a4.hip")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# the W4A4 kernel and every header it includes: a change to any of them makes a stored count stale
+SOURCES = [os.path.join(CSRC, f) for f in ("gemm_w4a4.hip", "gemm_common.hpp", "bsq_device.hpp", "bsq_launch.hpp")]
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for path in SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 OUT = os.path.join(ROOT, "profiles", "gemm_w4a4_4096x12288x3072_traffic.json")
 COPY_BYTES = 256 << 20
 M, K, N = 4096, 3072, 12288
@@ -75,8 +85,7 @@ def summarize(fetch_csv, write_csv):
                      "gemm_reading_bytes": sum(gemm) / len(gemm), "gemm_bytes": factor * sum(gemm) / len(gemm)}
     total = out["FETCH_SIZE"]["gemm_bytes"] + out["WRITE_SIZE"]["gemm_bytes"]
     algorithmic = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + M * N * 2
-    with open(SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = source_hash()
     res = {"kernel": "gemm_w4a4_kernel<256, 256>", "shape": "4096x12288x3072", "bytes_per_launch": round(total),
            "algorithmic_bytes_per_launch": algorithmic, "counters": out, "source_sha256": sha,
            "copy_bytes": COPY_BYTES}

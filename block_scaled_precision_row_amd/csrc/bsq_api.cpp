@@ -74,6 +74,40 @@ bsq_status check_gemm_common(const uint16_t* x, int64_t ldx, const void* w, uint
   return BSQ_OK;
 }
 
+// Few tokens: the skinny kernel (32 weight rows per workgroup, K split over its waves) keeps
+// every compute unit streaming weights where the tiled kernels would leave most of them idle
+// and walk K serially; with more rows the tiled kernels' operand reuse wins. Per scheme: the
+// skinny kernel always runs up to `always` rows, and up to `most` rows while the tiled
+// kernel would have fewer than 64 tiles of 128 x 128 (crossovers measured on MI355X,
+// K = 3072, N = 3072 and 12288).
+struct SkinnyRule {
+  int64_t always, most;
+};
+SkinnyRule skinny_rule(bsq::DecMode mode) {
+  switch (mode) {
+    case bsq::kW4A4: return {32, 128};
+    case bsq::kW4A16: return {64, 256};
+    case bsq::kW8A8: return {32, 256};
+    default: return {128, 256};  // W8A16
+  }
+}
+bool route_skinny(bsq::DecMode mode, const bsq::DecArgs& a) {
+  const SkinnyRule r = skinny_rule(mode);
+  const int64_t tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  const bool pick = a.M <= r.always || (a.M <= r.most && tiles < 64);
+  return pick && bsq::gemm_skinny_supported(mode, a);
+}
+hipError_t launch_dec_or_skinny(bsq::DecMode mode, const bsq::DecArgs& a, hipStream_t s) {
+  return route_skinny(mode, a) ? bsq::launch_gemm_skinny(mode, a, s) : bsq::launch_gemm_dec(mode, a, s);
+}
+hipError_t launch_w8a8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw, uint16_t* y,
+                       int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  bsq::DecArgs a{};
+  a.xq = xq; a.sx = sx; a.w = w; a.sw = sw; a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
+  if (route_skinny(bsq::kW8A8, a)) return bsq::launch_gemm_skinny(bsq::kW8A8, a, s);
+  return bsq::launch_gemm_fp8(xq, sx, w, sw, y, ldy, M, N, K, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,12 +202,12 @@ bsq_status bsq_gemm_fp8r(const uint16_t* x, int64_t ldx, const uint8_t* w, const
   if (weight_only) {
     bsq::DecArgs a{};
     a.x = x; a.ldx = ldx; a.w = w; a.sw = w_scale; a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
-    e = bsq::launch_gemm_dec(bsq::kW8A16, a, stream);
+    e = launch_dec_or_skinny(bsq::kW8A16, a, stream);
   } else {
     uint8_t* xq = static_cast<uint8_t*>(workspace);
     float* sx = reinterpret_cast<float*>(xq + pad256((size_t)(M * K)));
     e = bsq::launch_quant_fp8r(x, M, K, ldx, xq, sx, stream);
-    if (e == hipSuccess) e = bsq::launch_gemm_fp8(xq, sx, w, w_scale, y, ldy, M, N, K, stream);
+    if (e == hipSuccess) e = launch_w8a8(xq, sx, w, w_scale, y, ldy, M, N, K, stream);
   }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
@@ -198,13 +232,13 @@ bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, cons
   a.M = M; a.N = N; a.K = K;
   hipError_t e;
   if (weight_only) {
-    e = bsq::launch_gemm_dec(bsq::kW4A16, a, stream);
+    e = launch_dec_or_skinny(bsq::kW4A16, a, stream);
   } else {
     uint8_t* xq = static_cast<uint8_t*>(workspace);
     uint8_t* xs = xq + pad256((size_t)(M * K / 2));
     a.xq = xq; a.xs = xs; a.gx = input_scale;
     e = bsq::launch_quant_nvfp4(x, M, K, ldx, input_scale, xq, xs, stream);
-    if (e == hipSuccess) e = bsq::launch_gemm_dec(bsq::kW4A4, a, stream);
+    if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
   }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
@@ -217,7 +251,7 @@ bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_
   if (!x_scale || !w_scale) return BSQ_ERR_NULL;
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
   if ((st = check_device()) != BSQ_OK) return st;
-  hipError_t e = bsq::launch_gemm_fp8(xq, x_scale, w, w_scale, y, ldy, M, N, K, stream);
+  hipError_t e = launch_w8a8(xq, x_scale, w, w_scale, y, ldy, M, N, K, stream);
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
@@ -233,7 +267,7 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
   bsq::DecArgs a{};
   a.xq = xq; a.xs = x_bscale; a.gx = input_scale; a.w = w; a.ws = w_bscale; a.gw = w_scale2;
   a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
-  hipError_t e = bsq::launch_gemm_dec(bsq::kW4A4, a, stream);
+  hipError_t e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 

@@ -30,6 +30,7 @@ enum DecMode : int {
   kW4A4 = 0,   // X nvfp4 (xq, xs, *gx), W nvfp4 (w, ws, *gw); f16 MFMA; alpha = gx * gw
   kW4A16 = 1,  // X bf16, W nvfp4; bf16 MFMA; alpha = gw
   kW8A16 = 2,  // X bf16, W E4M3 with per-row scale sw[n]; bf16 MFMA
+  kW8A8 = 3,   // X E4M3 (xq) with per-row scale sx[m], W E4M3 with sw[n]; fp8 MFMA (skinny kernel only)
 };
 struct DecArgs {
   const uint16_t* x;   // bf16 activations (A16 modes)
@@ -40,7 +41,8 @@ struct DecArgs {
   const uint8_t* w;    // packed E2M1 [N][K/2] or E4M3 [N][K]
   const uint8_t* ws;   // E4M3 weight block scales [N][K/16] (nvfp4)
   const float* gw;     // weight global scale (nvfp4)
-  const float* sw;     // per-row weight scales [N] (W8A16)
+  const float* sw;     // per-row weight scales [N] (W8A16, W8A8)
+  const float* sx;     // per-row activation scales [M] (W8A8)
   uint16_t* y;
   int64_t ldy;
   int64_t M, N, K;
@@ -49,6 +51,9 @@ hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
 // W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0
 bool gemm_w4a4_supported(const DecArgs& a);
 hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s);
+// Few-token GEMMs: 32 weight rows per workgroup, K split over its 8 waves
+bool gemm_skinny_supported(DecMode mode, const DecArgs& a);
+hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s);
 
 }  // namespace bsq
 

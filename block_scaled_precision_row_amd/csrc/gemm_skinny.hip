@@ -1,0 +1,526 @@
+// Skinny GEMMs for few tokens (small M), all four schemes of the linear layer.
+//
+// With few activation rows the layer is a stream over the weights ("BFL
+// (fp8r / nvfp4)", "Kernels" table: the weight is read once per call), and a
+// tiled GEMM with one workgroup per output tile leaves most compute units
+// idle and walks K serially. Here every workgroup owns one MFMA block of 32
+// weight rows (N) and MB blocks of 32 activation rows (M), and its waves
+// split K: wave w of NW takes the 128-deep K stages w, w + NW, w + 2 NW, ...
+// The NW partial tiles are summed through LDS in wave order, so the result
+// does not depend on timing, and the epilogue applies the scheme's scales:
+//   W4A4 : y = bf16(acc * gx * gw)          f16 MFMA on exact decoded nvfp4
+//   W4A16: y = bf16(acc * gw)               bf16 MFMA, X as given
+//   W8A8 : y = bf16(acc * sx[m] * sw[n])    fp8 MFMA on the E4M3 codes
+//   W8A16: y = bf16(acc * sw[n])            bf16 MFMA, W decoded exactly
+//
+// Operand fetch, two variants:
+//  - E4M3 weights (W8A8, W8A16): each wave streams its stages through a
+//    private ring of two LDS stage buffers with LDS DMA -- whole 128- or
+//    256-byte row segments per request, so a 1 KB request touches 4 to 8
+//    cache lines, where loading the MFMA operand layout directly (each lane
+//    its own row) touches 32 -- and reads its operands from there. A wave
+//    only reads what it fetched itself, so the K loop has no workgroup
+//    barrier.
+//  - nvfp4 weights (W4A4, W4A16): operands go from global memory straight
+//    into the MFMA operand registers with buffer loads, two stages in flight
+//    per wave (8 waves per workgroup).
+//
+// K layout of a stage (kb = first K value): lane half h of an MFMA operand
+// holds the 64 values [kb + 64 h, kb + 64 h + 64), in MFMA K steps of 8
+// (16-bit MFMAs) or 32 (fp8 MFMA) consecutive values -- the same for both
+// operands, so every product pairs equal K indices.
+#include "gemm_common.hpp"
+#include "bsq_launch.hpp"
+
+namespace bsq {
+
+namespace {
+
+using namespace gemm;
+
+constexpr int kSkK = 128;  // K values per stage
+constexpr int kSkRing = 2;  // stage buffers per wave
+
+// ---- operands of one stage for one lane -------------------------------------------
+// nvfp4: 64 values = 32 packed bytes (q[g] holds values 32 g .. 32 g + 31 of the lane's
+// window) and their 4 E4M3 block scales (byte b scales values 16 b .. 16 b + 15)
+struct OpNv {
+  uint4 q[2];
+  uint32_t s;
+};
+// fp8: 64 E4M3 codes
+struct OpF8 {
+  uint4 d[4];
+};
+// bf16: 64 values
+struct OpBf {
+  uint4 d[8];
+};
+
+// ---- decoders ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t h2u(v2h v) {
+  union { v2h h; uint32_t u; } c;
+  c.h = v;
+  return c.u;
+}
+// block scale byte b of s as an f16 pair / as fp32 (E4M3 is exact in both)
+__device__ __forceinline__ v2h scale_h2(uint32_t s, int b) {
+  const uint32_t dup = __builtin_amdgcn_perm(s, s, 0x01010101u * (uint32_t)b);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dup, 1.0f, false);
+}
+__device__ __forceinline__ float scale_f(uint32_t s, int b) {
+  switch (b) {
+    case 0: return dec_e4m3<0>(s);
+    case 1: return dec_e4m3<1>(s);
+    case 2: return dec_e4m3<2>(s);
+    default: return dec_e4m3<3>(s);
+  }
+}
+// 8 E2M1 values (one packed dword) times their block scale, as 8 f16 / 8 bf16; both exact
+__device__ __forceinline__ v8h nv8_f16(uint32_t w, v2h s) {
+  union { uint4 u; v8h h; } r;
+  r.u = make_uint4(h2u(dec_e2m1x2_f16<0>(w) * s), h2u(dec_e2m1x2_f16<1>(w) * s), h2u(dec_e2m1x2_f16<2>(w) * s),
+                   h2u(dec_e2m1x2_f16<3>(w) * s));
+  return r.h;
+}
+template <int sel>
+__device__ __forceinline__ uint32_t nv2_bf16(uint32_t w, float s) {
+  const v2f e = dec_e2m1x2_f32<sel>(w);
+  return pack_bf16x2(e.x * s, e.y * s);
+}
+__device__ __forceinline__ v8bf nv8_bf16(uint32_t w, float s) {
+  union { uint4 u; v8bf b; } r;
+  r.u = make_uint4(nv2_bf16<0>(w, s), nv2_bf16<1>(w, s), nv2_bf16<2>(w, s), nv2_bf16<3>(w, s));
+  return r.b;
+}
+// 8 E4M3 codes (two dwords) as 8 bf16 (exact)
+__device__ __forceinline__ v8bf f8x8_bf16(uint32_t lo, uint32_t hi) {
+  const v2f a = dec_e4m3x2<false>(lo), b = dec_e4m3x2<true>(lo), c = dec_e4m3x2<false>(hi), d = dec_e4m3x2<true>(hi);
+  union { uint4 u; v8bf b; } r;
+  r.u = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y), pack_bf16x2(d.x, d.y));
+  return r.b;
+}
+__device__ __forceinline__ v8bf as_bf(uint4 u) {
+  union { uint4 u; v8bf b; } r;
+  r.u = u;
+  return r.b;
+}
+__device__ __forceinline__ uint32_t dw(const uint4& q, int t) { return t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w; }
+
+// ---- per-scheme stage: operand types, loads and MFMAs ---------------------------------
+template <int MODE>
+struct Scheme;
+
+template <>
+struct Scheme<kW4A4> {
+  using WOp = OpNv;
+  using XOp = OpNv;
+  template <int MB>
+  __device__ static void mma(v16f (&acc)[MB], const WOp& w, const XOp (&x)[MB]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int b = 2 * g + (t >> 1);
+        const v8h a = nv8_f16(dw(w.q[g], t), scale_h2(w.s, b));
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, nv8_f16(dw(x[j].q[g], t), scale_h2(x[j].s, b)), acc[j],
+                                                          0, 0, 0);
+      }
+  }
+};
+template <>
+struct Scheme<kW4A16> {
+  using WOp = OpNv;
+  using XOp = OpBf;
+  template <int MB>
+  __device__ static void mma(v16f (&acc)[MB], const WOp& w, const XOp (&x)[MB]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v8bf a = nv8_bf16(dw(w.q[g], t), scale_f(w.s, 2 * g + (t >> 1)));
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf(x[j].d[4 * g + t]), acc[j], 0, 0, 0);
+      }
+  }
+};
+template <>
+struct Scheme<kW8A8> {
+  using WOp = OpF8;
+  using XOp = OpF8;
+  template <int MB>
+  __device__ static void mma(v16f (&acc)[MB], const WOp& w, const XOp (&x)[MB]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 l = w.d[2 * s], h = w.d[2 * s + 1];
+      const v8i a = v8i{(int)l.x, (int)l.y, (int)l.z, (int)l.w, (int)h.x, (int)h.y, (int)h.z, (int)h.w};
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const uint4 xl = x[j].d[2 * s], xh = x[j].d[2 * s + 1];
+        const v8i b = v8i{(int)xl.x, (int)xl.y, (int)xl.z, (int)xl.w, (int)xh.x, (int)xh.y, (int)xh.z, (int)xh.w};
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], 0, 0, 0, 0, 0, 0);
+      }
+    }
+  }
+};
+template <>
+struct Scheme<kW8A16> {
+  using WOp = OpF8;
+  using XOp = OpBf;
+  template <int MB>
+  __device__ static void mma(v16f (&acc)[MB], const WOp& w, const XOp (&x)[MB]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4& q = w.d[c >> 1];
+      const v8bf a = (c & 1) ? f8x8_bf16(q.z, q.w) : f8x8_bf16(q.x, q.y);
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf(x[j].d[c]), acc[j], 0, 0, 0);
+    }
+  }
+};
+
+// sum the NW partial tiles (red = [NW][MB][16 registers][64 lanes]) in wave order, scale,
+// convert and store the tile
+template <int MODE, int MB, int NW>
+__device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* red, int m0, int n0, int tid) {
+  const int M = (int)a.M, N = (int)a.N;
+  float alpha = 1.0f;
+  if constexpr (MODE == kW4A4) alpha = a.gx[0] * a.gw[0];
+  if constexpr (MODE == kW4A16) alpha = a.gw[0];
+  // thread -> (row ml of the tile, output pair p): consecutive threads write consecutive pairs
+  for (int idx = tid; idx < 32 * MB * 16; idx += 64 * NW) {
+    const int ml = idx >> 4, p = idx & 15;
+    const int m = m0 + ml;
+    if (m >= M) break;
+    const int j = ml >> 5, lm = ml & 31;
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int nl = 2 * p + e;  // n = 8 G + 4 H + q is held by lane lm + 32 H in register 4 G + q
+      const int r = 4 * (nl >> 3) + (nl & 3), ln = lm + 32 * ((nl >> 2) & 1);
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += red[((w * MB + j) * 16 + r) * 64 + ln];
+      v[e] = s;
+    }
+    const int n = n0 + 2 * p;
+    float s0 = alpha, s1 = alpha;
+    if constexpr (MODE == kW8A8 || MODE == kW8A16) {
+      s0 = n < N ? a.sw[n] : 0.0f;
+      s1 = n + 1 < N ? a.sw[n + 1] : 0.0f;
+    }
+    if constexpr (MODE == kW8A8) {
+      const float xs = a.sx[m];
+      v[0] = v[0] * xs;
+      v[1] = v[1] * xs;
+    }
+    const uint32_t pk = pack_bf16x2(v[0] * s0, v[1] * s1);
+    uint16_t* yr = a.y + (int64_t)m * a.ldy;
+    if (n + 1 < N) {
+      *reinterpret_cast<uint32_t*>(yr + n) = pk;
+    } else if (n < N) {
+      yr[n] = (uint16_t)(pk & 0xFFFFu);
+    }
+  }
+}
+
+// ---- direct operand loads (nvfp4 schemes) --------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kSkOut = 0x40000000u;  // buffer offset past every tile's records
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferConfig);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+// packed codes of the lane's window, and its 4 block scales as two 16-bit loads (scale
+// rows are K / 16 bytes, always even); chunks past K read as zeros
+__device__ __forceinline__ void load_nv(OpNv& o, rsrc_t rq, rsrc_t rs, int row, int kp, int ks, int kw, int K) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const bool ok = kw + 32 * g < K;
+    o.q[g] = bload16(rq, ok ? (uint32_t)(row * kp + (kw >> 1) + 16 * g) : kSkOut);
+  }
+  const uint32_t lo = bload2(rs, kw < K ? (uint32_t)(row * ks + (kw >> 4)) : kSkOut);
+  const uint32_t hi = bload2(rs, kw + 32 < K ? (uint32_t)(row * ks + (kw >> 4) + 2) : kSkOut);
+  o.s = (lo & 0xFFFFu) | (hi << 16);
+}
+__device__ __forceinline__ void load_bf(OpBf& o, rsrc_t r, int row, int pitch_bytes, int kw, int K) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    o.d[c] = bload16(r, kw + 8 * c < K ? (uint32_t)(row * pitch_bytes + 2 * (kw + 8 * c)) : kSkOut);
+}
+
+// nvfp4 weights: 8 waves, operands loaded straight into registers
+constexpr int kSkDirectWaves = 8;
+
+template <int MODE, int MB>
+__global__ __launch_bounds__(64 * kSkDirectWaves) void gemm_skinny_direct_kernel(DecArgs a) {
+  static_assert(MODE == kW4A4 || MODE == kW4A16, "nvfp4 weights only");
+  using S = Scheme<MODE>;
+  constexpr int NW = kSkDirectWaves;
+  __shared__ __attribute__((aligned(16))) float red[NW * MB * 16 * 64];
+
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  const int nblk = (N + 31) / 32;
+  const int n0 = (blockIdx.x % nblk) * 32, m0 = (blockIdx.x / nblk) * (32 * MB);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int rows_w = N - n0 < 32 ? N - n0 : 32, rows_x = M - m0 < 32 * MB ? M - m0 : 32 * MB;
+  const int kp = K >> 1, ks = K >> 4;
+
+  const rsrc_t wq = make_rsrc(a.w + (int64_t)n0 * kp, (uint32_t)(rows_w * kp));
+  const rsrc_t ws = make_rsrc(a.ws + (int64_t)n0 * ks, (uint32_t)(rows_w * ks));
+  rsrc_t xq, xs;
+  int xpitch = 0;
+  if constexpr (MODE == kW4A4) {
+    xq = make_rsrc(a.xq + (int64_t)m0 * kp, (uint32_t)(rows_x * kp));
+    xs = make_rsrc(a.xs + (int64_t)m0 * ks, (uint32_t)(rows_x * ks));
+  } else {
+    xpitch = (int)(a.ldx * 2);
+    xq = make_rsrc(a.x + (int64_t)m0 * a.ldx, (uint32_t)((rows_x - 1) * xpitch + 2 * K));
+    xs = xq;
+  }
+
+  v16f acc[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) acc[j] = v16f{};
+
+  const int nk = (K + kSkK - 1) / kSkK;
+  const int mine = nk > wave ? (nk - wave + NW - 1) / NW : 0;  // uniform per wave
+  typename S::WOp w0, w1;
+  typename S::XOp x0[MB], x1[MB];
+  auto load = [&](typename S::WOp& w, typename S::XOp (&x)[MB], int i) {
+    const int kw = (wave + NW * i) * kSkK + 64 * lh;
+    load_nv(w, wq, ws, lr, kp, ks, kw, K);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      if constexpr (MODE == kW4A4) load_nv(x[j], xq, xs, 32 * j + lr, kp, ks, kw, K);
+      else load_bf(x[j], xq, 32 * j + lr, xpitch, kw, K);
+    }
+  };
+  // Two stages in flight; a load for a stage past this wave's share addresses K values
+  // past the end and reads zeros, so the loop needs no guards around its loads.
+  load(w0, x0, 0);
+  load(w1, x1, 1);
+  for (int i = 0; i < mine; i += 2) {
+    S::template mma<MB>(acc, w0, x0);
+    load(w0, x0, i + 2);
+    if (i + 1 < mine) S::template mma<MB>(acc, w1, x1);
+    load(w1, x1, i + 3);
+  }
+
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
+  __syncthreads();
+  skinny_epilogue<MODE, MB, NW>(a, red, m0, n0, tid);
+}
+
+// ---- LDS-DMA variant (E4M3 weights): stage layout of one wave -----------------------
+// A code region holds 32 rows of R bytes (R = 128 for E4M3, 256 for bf16 at a 128-deep
+// stage), 16-byte chunks XOR-swizzled as in gemm_common.hpp.
+template <int R>
+struct CodeRegion {
+  static constexpr int C = R / 16, RPL = 1024 / R, LOADS = 32 / RPL, BYTES = 32 * R;
+};
+
+template <int MODE>
+struct Layout {
+  static_assert(MODE == kW8A8 || MODE == kW8A16, "E4M3 weights only");
+  static constexpr bool XBF = MODE == kW8A16;
+  using WC = CodeRegion<128>;
+  using XC = CodeRegion<XBF ? 256 : 128>;
+  static constexpr int W_BYTES = WC::BYTES, X_BYTES = XC::BYTES;  // X per M block
+  static constexpr int W_LOADS = WC::LOADS, X_LOADS = XC::LOADS;
+};
+
+// a buffer resource as the scalar operand the DMA instruction takes (the values are
+// wave-uniform; this keeps them in scalar registers when they come from an array)
+__device__ __forceinline__ v4i sgpr(const v4i& r) {
+  return v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+             __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+
+// DMA of one code region: load ld covers rows RPL * ld .. RPL * ld + RPL - 1; lane l writes
+// physical chunk l % C of its row, so it fetches the logical chunk the swizzle puts there.
+// `kv` is the first K value of the stage, `vpc` the K values per 16-byte chunk.
+template <int R>
+__device__ __forceinline__ void dma_codes(const v4i& r, uint32_t lds, int lane, int pitch, int kbyte, int kv, int vpc,
+                                          int K) {
+  using G = CodeRegion<R>;
+  const v4i rs = sgpr(r);
+  const int lrow = lane / G::C, phys = lane % G::C;
+#pragma unroll
+  for (int ld = 0; ld < G::LOADS; ++ld) {
+    const int row = ld * G::RPL + lrow;
+    const int c = swz_chunk<R>(row, phys);
+    const int voff = kv + c * vpc < K ? row * pitch + kbyte + 16 * c : kOutOfRange;
+    dma16(rs, lds + ld * 1024, voff, 0);
+  }
+}
+
+// s_waitcnt that the compiler may not move memory accesses across
+template <int n>
+__device__ __forceinline__ void wait_vm_fence() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  __asm__ volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds_fence() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// operand reads from a wave's stage buffer
+__device__ __forceinline__ void read_f8(OpF8& o, const uint8_t* codes, int lr, int lh) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<128>(lr, 4 * lh + c));
+}
+__device__ __forceinline__ void read_bf(OpBf& o, const uint8_t* codes, int lr, int lh) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
+}
+
+template <int MODE, int MB, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
+  using S = Scheme<MODE>;
+  using L = Layout<MODE>;
+  constexpr int STAGE = L::W_BYTES + MB * L::X_BYTES;
+  constexpr int WAVE = kSkRing * STAGE;
+  constexpr int LOADS = L::W_LOADS + MB * L::X_LOADS;  // DMA instructions per stage
+  constexpr int RED = NW * MB * 16 * 64 * 4;
+  constexpr int LDS = NW * WAVE > RED ? NW * WAVE : RED;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert((kSkRing - 1) * LOADS < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+
+  const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
+  const int nblk = (N + 31) / 32;
+  const int n0 = (blockIdx.x % nblk) * 32, m0 = (blockIdx.x / nblk) * (32 * MB);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int rows_w = N - n0 < 32 ? N - n0 : 32;
+
+  // buffer resources over this tile's rows: rows past the matrix read as zeros
+  const v4i rwq = buffer_rsrc(a.w + (int64_t)n0 * K, (uint32_t)(rows_w * K));
+  const int xpitch = L::XBF ? (int)(a.ldx * 2) : K;
+  v4i rxq[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int mj = m0 + 32 * j;
+    const int rows = M - mj <= 0 ? 0 : M - mj < 32 ? M - mj : 32;
+    if constexpr (L::XBF)
+      rxq[j] = buffer_rsrc(a.x + (int64_t)mj * a.ldx, rows ? (uint32_t)((rows - 1) * xpitch + 2 * K) : 0u);
+    else
+      rxq[j] = buffer_rsrc(a.xq + (int64_t)mj * K, (uint32_t)(rows * K));
+  }
+
+  const uint32_t wave_lds = lds_offset(smem) + (uint32_t)(wave * WAVE);
+  const uint8_t* wave_mem = smem + wave * WAVE;
+  // fetch this wave's i-th stage into ring buffer i % 2 (stages past K read as zeros)
+  auto issue = [&](int i) {
+    const int kv = (wave + NW * i) * kSkK;
+    const uint32_t base = wave_lds + (uint32_t)((i & 1) * STAGE);
+    dma_codes<128>(rwq, base, lane, K, kv, kv, 16, K);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const uint32_t xb = base + L::W_BYTES + j * L::X_BYTES;
+      if constexpr (L::XBF) dma_codes<256>(rxq[j], xb, lane, xpitch, 2 * kv, kv, 8, K);
+      else dma_codes<128>(rxq[j], xb, lane, xpitch, kv, kv, 16, K);
+    }
+  };
+
+  v16f acc[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) acc[j] = v16f{};
+
+  const int nk = (K + kSkK - 1) / kSkK;
+  const int mine = nk > wave ? (nk - wave + NW - 1) / NW : 0;  // uniform per wave
+  issue(0);
+  issue(1);
+  for (int i = 0; i < mine; ++i) {
+    wait_vm_fence<(kSkRing - 1) * LOADS>();  // this wave's stage i has landed
+    const uint8_t* st = wave_mem + (i & 1) * STAGE;
+    typename S::WOp w;
+    typename S::XOp x[MB];
+    read_f8(w, st, lr, lh);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const uint8_t* xb = st + L::W_BYTES + j * L::X_BYTES;
+      if constexpr (L::XBF) read_bf(x[j], xb, lr, lh);
+      else read_f8(x[j], xb, lr, lh);
+    }
+    wait_lds_fence();  // the buffer is free again
+    issue(i + 2);
+    S::template mma<MB>(acc, w, x);
+  }
+  wait_vm_fence<0>();
+  __syncthreads();  // every ring is idle: the LDS is reused for the reduction
+
+  // sum the NW partial tiles in wave order
+  float* red = reinterpret_cast<float*>(smem);  // [NW][MB][16][64]
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
+  __syncthreads();
+
+  skinny_epilogue<MODE, MB, NW>(a, red, m0, n0, tid);
+}
+
+template <int MODE, int MB, int NW>
+hipError_t run(const DecArgs& a, hipStream_t s) {
+  const int64_t blocks = ((a.N + 31) / 32) * ((a.M + 32 * MB - 1) / (32 * MB));
+  hipLaunchKernelGGL((gemm_skinny_kernel<MODE, MB, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+template <int MODE, int MB>
+hipError_t run_direct(const DecArgs& a, hipStream_t s) {
+  const int64_t blocks = ((a.N + 31) / 32) * ((a.M + 32 * MB - 1) / (32 * MB));
+  hipLaunchKernelGGL((gemm_skinny_direct_kernel<MODE, MB>), dim3((unsigned)blocks), dim3(64 * kSkDirectWaves), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t pick(const DecArgs& a, hipStream_t s) {
+  if constexpr (MODE == kW4A4 || MODE == kW4A16) {
+    if (a.M <= 32) return run_direct<MODE, 1>(a, s);
+    return run_direct<MODE, 2>(a, s);
+  } else if constexpr (MODE == kW8A16) {
+    // bf16 activations fill LDS fastest: one activation block per workgroup
+    return run<MODE, 1, 4>(a, s);
+  } else {
+    if (a.M <= 32) return run<MODE, 1, 4>(a, s);
+    return run<MODE, 2, 4>(a, s);
+  }
+}
+
+}  // namespace
+
+bool gemm_skinny_supported(DecMode mode, const DecArgs& a) {
+  // 32-bit buffer offsets: every operand tile (up to 64 rows) stays below the out-of-range offset
+  const int64_t xpitch = (mode == kW4A16 || mode == kW8A16) ? 2 * a.ldx : a.K;
+  return 64 * a.K < kOutOfRange && 64 * xpitch < (int64_t)kOutOfRange;
+}
+
+hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s) {
+  switch (mode) {
+    case kW4A4: return pick<kW4A4>(a, s);
+    case kW4A16: return pick<kW4A16>(a, s);
+    case kW8A8: return pick<kW8A8>(a, s);
+    default: return pick<kW8A16>(a, s);
+  }
+}
+
+}  // namespace bsq

@@ -182,3 +182,21 @@ def test_prequantized_activation_entry_points(M, N, K):
     torch.cuda.synchronize()
     assert_gemm_close(host(y)[rows], gemm.gemm_nvfp4(xq[rows], sfx[rows], gx, wq, sfw, gw), "nvfp4_q %dx%dx%d" % (M, N, K))
     assert_gemm_close(host(y8)[rows], gemm.gemm_fp8r(x8[rows], s8[rows], w8, t8), "fp8r_q %dx%dx%d" % (M, N, K))
+
+
+# Few tokens: these shapes run on the skinny kernel (K split over the waves of a workgroup);
+# K values chosen so that stages end inside a lane's window (544 = 4 * 128 + 32) and waves
+# without any stage exist (K = 96, 224).
+SKINNY_SHAPES = [(16, 3072, 3072), (33, 1000, 544), (64, 3072, 3072), (96, 520, 224), (160, 3072, 3072),
+                 (256, 1056, 96), (5, 12288, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_all_schemes(M, N, K):
+    x = syn.normal_bf16((M, K), 52, M, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 52, 2000 + N + K, sigma=0.02)
+    tag = "%dx%dx%d" % (M, N, K)
+    run_fp8r(x, w, what="fp8r " + tag)
+    run_fp8r(x, w, weight_only=True, what="fp8r-w8a16 " + tag)
+    run_nvfp4(x, w, what="nvfp4 " + tag)
+    run_nvfp4(x, w, weight_only=True, what="nvfp4-w4a16 " + tag)

@@ -28,7 +28,8 @@
 // K layout of a stage (kb = first K value): lane half h of an MFMA operand
 // holds the 64 values [kb + 64 h, kb + 64 h + 64), in MFMA K steps of 8
 // (16-bit MFMAs) or 32 (fp8 MFMA) consecutive values -- the same for both
-// operands, so every product pairs equal K indices.
+// operands, so every product pairs equal K indices. Workgroups start their walk over K at
+// different stages (see stage_k).
 #include "gemm_common.hpp"
 #include "bsq_launch.hpp"
 
@@ -242,33 +243,105 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
-// packed codes of the lane's window, and its 4 block scales as two 16-bit loads (scale
-// rows are K / 16 bytes, always even); chunks past K read as zeros
-__device__ __forceinline__ void load_nv(OpNv& o, rsrc_t rq, rsrc_t rs, int row, int kp, int ks, int kw, int K) {
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const bool ok = kw + 32 * g < K;
-    o.q[g] = bload16(rq, ok ? (uint32_t)(row * kp + (kw >> 1) + 16 * g) : kSkOut);
-  }
-  const uint32_t lo = bload2(rs, kw < K ? (uint32_t)(row * ks + (kw >> 4)) : kSkOut);
-  const uint32_t hi = bload2(rs, kw + 32 < K ? (uint32_t)(row * ks + (kw >> 4) + 2) : kSkOut);
-  o.s = (lo & 0xFFFFu) | (hi << 16);
-}
-__device__ __forceinline__ void load_bf(OpBf& o, rsrc_t r, int row, int pitch_bytes, int kw, int K) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    o.d[c] = bload16(r, kw + 8 * c < K ? (uint32_t)(row * pitch_bytes + 2 * (kw + 8 * c)) : kSkOut);
+// K offset of a wave's i-th stage. Every workgroup reads the same activation rows; starting
+// the walk over K at a different stage per workgroup spreads those reads over the cache
+// channels instead of having all workgroups hit the same lines at once. Stages past the
+// wave's share return K (their loads read zeros).
+__device__ __forceinline__ int stage_k(int wave, int nw, int i, int nk, int rot, int K) {
+  const int v = wave + nw * i;
+  if (v >= nk) return K;
+  const int s = v + rot < nk ? v + rot : v + rot - nk;
+  return s * kSkK;
 }
 
-// nvfp4 weights: 8 waves, operands loaded straight into registers
-constexpr int kSkDirectWaves = 8;
+// ---- register-staged variant (nvfp4 weights) -------------------------------------------
+// A wave's share of one 128-deep stage is fetched with row-contiguous buffer loads (4 or 16
+// lanes per row segment), so one 1 KB load touches 8 cache lines; it lands in registers, is
+// written to the wave's LDS stage buffer in the MFMA operand layout, and read back as in the
+// DMA variant. Three stages of loads are in flight per wave.
+constexpr int kSkStagedWaves = 8;
+
+// nvfp4 operand of a stage: 32 rows x 64 packed bytes (2 loads of 16 rows) + 32 rows x 8 scale
+// bytes (lane l: dword l % 2 of row l / 2)
+struct RawNv {
+  uint4 c[2];
+  uint32_t s;
+};
+// `rows` = rows of the tile inside the matrix: a load that would only cover rows past it is
+// skipped (those rows only feed outputs that are never stored)
+__device__ __forceinline__ void fetch_nv(RawNv& r, rsrc_t rq, rsrc_t rs, int lane, int kp, int ks, int kv, int K,
+                                         bool dword_scales, int rows) {
+#pragma unroll
+  for (int ld = 0; ld < 2; ++ld) {
+    const int row = 16 * ld + (lane >> 2), c = lane & 3;
+    r.c[ld] = 16 * ld < rows ? bload16(rq, kv + 32 * c < K ? (uint32_t)(row * kp + (kv >> 1) + 16 * c) : kSkOut)
+                             : make_uint4(0, 0, 0, 0);
+  }
+  const int row = lane >> 1, d = lane & 1;
+  const bool ok = kv + 64 * d < K;
+  const uint32_t off = (uint32_t)(row * ks + (kv >> 4) + 4 * d);
+  if (dword_scales) {  // K % 64 == 0: the dword is 4-byte aligned
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? (int)off : (int)kSkOut, 0, 0);
+  } else {
+    const uint32_t lo = bload2(rs, ok ? off : kSkOut), hi = bload2(rs, ok ? off + 2 : kSkOut);
+    r.s = (lo & 0xFFFFu) | (hi << 16);
+  }
+}
+__device__ __forceinline__ void stash_nv(const RawNv& r, uint8_t* codes, uint8_t* scales, int lane) {
+#pragma unroll
+  for (int ld = 0; ld < 2; ++ld) {
+    const int row = 16 * ld + (lane >> 2), c = lane & 3;
+    *reinterpret_cast<uint4*>(codes + swz_off<64>(row, c)) = r.c[ld];
+  }
+  *reinterpret_cast<uint32_t*>(scales + 4 * lane) = r.s;  // row lane / 2, dword lane % 2
+}
+// bf16 operand of a stage: 32 rows x 256 bytes (8 loads of 4 rows)
+struct RawBf {
+  uint4 c[8];
+};
+__device__ __forceinline__ void fetch_bf(RawBf& r, rsrc_t rx, int lane, int pitch, int kv, int K, int rows) {
+#pragma unroll
+  for (int ld = 0; ld < 8; ++ld) {
+    const int row = 4 * ld + (lane >> 4), c = lane & 15;
+    r.c[ld] = 4 * ld < rows ? bload16(rx, kv + 8 * c < K ? (uint32_t)(row * pitch + 2 * kv + 16 * c) : kSkOut)
+                            : make_uint4(0, 0, 0, 0);
+  }
+}
+__device__ __forceinline__ void stash_bf(const RawBf& r, uint8_t* codes, int lane) {
+#pragma unroll
+  for (int ld = 0; ld < 8; ++ld) {
+    const int row = 4 * ld + (lane >> 4), c = lane & 15;
+    *reinterpret_cast<uint4*>(codes + swz_off<256>(row, c)) = r.c[ld];
+  }
+}
+// operand reads in the MFMA layout
+__device__ __forceinline__ void read_nv(OpNv& o, const uint8_t* codes, const uint8_t* scales, int lr, int lh,
+                                        int kv, int K) {
+  o.q[0] = *reinterpret_cast<const uint4*>(codes + swz_off<64>(lr, 2 * lh));
+  o.q[1] = *reinterpret_cast<const uint4*>(codes + swz_off<64>(lr, 2 * lh + 1));
+  const uint32_t s = *reinterpret_cast<const uint32_t*>(scales + lr * 8 + 4 * lh);
+  const int nvalid = (K - (kv + 64 * lh)) >> 4;  // blocks of this lane's window inside K
+  o.s = nvalid >= 4 ? s : nvalid <= 0 ? 0u : s & ((1u << (8 * nvalid)) - 1u);
+}
+__device__ __forceinline__ void read_bf16(OpBf& o, const uint8_t* codes, int lr, int lh) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
+}
 
 template <int MODE, int MB>
-__global__ __launch_bounds__(64 * kSkDirectWaves) void gemm_skinny_direct_kernel(DecArgs a) {
+__global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel(DecArgs a) {
   static_assert(MODE == kW4A4 || MODE == kW4A16, "nvfp4 weights only");
   using S = Scheme<MODE>;
-  constexpr int NW = kSkDirectWaves;
-  __shared__ __attribute__((aligned(16))) float red[NW * MB * 16 * 64];
+  constexpr int NW = kSkStagedWaves;
+  constexpr bool XBF = MODE == kW4A16;
+  using RawX = typename std::conditional<XBF, RawBf, RawNv>::type;
+  constexpr int NV_BYTES = 32 * 64 + 256;                   // codes + scales of one nvfp4 operand
+  constexpr int X_BYTES = XBF ? 32 * 256 : NV_BYTES;        // per activation block
+  constexpr int STAGE = NV_BYTES + MB * X_BYTES;            // one buffer per wave
+  constexpr int RED = NW * MB * 16 * 64 * 4;
+  constexpr int LDS = NW * STAGE > RED ? NW * STAGE : RED;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
 
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   const int nblk = (N + 31) / 32;
@@ -276,50 +349,90 @@ __global__ __launch_bounds__(64 * kSkDirectWaves) void gemm_skinny_direct_kernel
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
-  const int rows_w = N - n0 < 32 ? N - n0 : 32, rows_x = M - m0 < 32 * MB ? M - m0 : 32 * MB;
+  const int rows_w = N - n0 < 32 ? N - n0 : 32;
   const int kp = K >> 1, ks = K >> 4;
+  const bool dword_scales = (K & 63) == 0;
 
   const rsrc_t wq = make_rsrc(a.w + (int64_t)n0 * kp, (uint32_t)(rows_w * kp));
   const rsrc_t ws = make_rsrc(a.ws + (int64_t)n0 * ks, (uint32_t)(rows_w * ks));
-  rsrc_t xq, xs;
-  int xpitch = 0;
-  if constexpr (MODE == kW4A4) {
-    xq = make_rsrc(a.xq + (int64_t)m0 * kp, (uint32_t)(rows_x * kp));
-    xs = make_rsrc(a.xs + (int64_t)m0 * ks, (uint32_t)(rows_x * ks));
-  } else {
-    xpitch = (int)(a.ldx * 2);
-    xq = make_rsrc(a.x + (int64_t)m0 * a.ldx, (uint32_t)((rows_x - 1) * xpitch + 2 * K));
-    xs = xq;
+  const int xpitch = XBF ? (int)(a.ldx * 2) : kp;
+  rsrc_t xq[MB], xs[MB];
+  int xrows[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int mj = m0 + 32 * j;
+    const int rows = M - mj <= 0 ? 0 : M - mj < 32 ? M - mj : 32;
+    xrows[j] = rows;
+    if constexpr (XBF) {
+      xq[j] = make_rsrc(a.x + (int64_t)mj * a.ldx, rows ? (uint32_t)((rows - 1) * xpitch + 2 * K) : 0u);
+      xs[j] = xq[j];
+    } else {
+      xq[j] = make_rsrc(a.xq + (int64_t)mj * kp, (uint32_t)(rows * kp));
+      xs[j] = make_rsrc(a.xs + (int64_t)mj * ks, (uint32_t)(rows * ks));
+    }
   }
 
+  uint8_t* buf = smem + wave * STAGE;
   v16f acc[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) acc[j] = v16f{};
 
   const int nk = (K + kSkK - 1) / kSkK;
   const int mine = nk > wave ? (nk - wave + NW - 1) / NW : 0;  // uniform per wave
-  typename S::WOp w0, w1;
-  typename S::XOp x0[MB], x1[MB];
-  auto load = [&](typename S::WOp& w, typename S::XOp (&x)[MB], int i) {
-    const int kw = (wave + NW * i) * kSkK + 64 * lh;
-    load_nv(w, wq, ws, lr, kp, ks, kw, K);
+  const int rot = (int)(blockIdx.x % (unsigned)nk);
+  RawNv w0, w1, w2;
+  RawX x0[MB], x1[MB], x2[MB];
+  auto fetch = [&](RawNv& w, RawX (&x)[MB], int i) {
+    const int kv = stage_k(wave, NW, i, nk, rot, K);
+    fetch_nv(w, wq, ws, lane, kp, ks, kv, K, dword_scales, rows_w);
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      if constexpr (MODE == kW4A4) load_nv(x[j], xq, xs, 32 * j + lr, kp, ks, kw, K);
-      else load_bf(x[j], xq, 32 * j + lr, xpitch, kw, K);
+      if constexpr (XBF) fetch_bf(x[j], xq[j], lane, xpitch, kv, K, xrows[j]);
+      else fetch_nv(x[j], xq[j], xs[j], lane, kp, ks, kv, K, dword_scales, xrows[j]);
     }
   };
-  // Two stages in flight; a load for a stage past this wave's share addresses K values
-  // past the end and reads zeros, so the loop needs no guards around its loads.
-  load(w0, x0, 0);
-  load(w1, x1, 1);
-  for (int i = 0; i < mine; i += 2) {
-    S::template mma<MB>(acc, w0, x0);
-    load(w0, x0, i + 2);
-    if (i + 1 < mine) S::template mma<MB>(acc, w1, x1);
-    load(w1, x1, i + 3);
+  // stage i: registers -> LDS (after this wave's reads of stage i - 1, which precede in the
+  // LDS queue), operands back in the MFMA layout, MFMAs
+  auto consume = [&](const RawNv& w, const RawX (&x)[MB], int i) {
+    const int kv = stage_k(wave, NW, i, nk, rot, K);
+    stash_nv(w, buf, buf + 32 * 64, lane);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      uint8_t* xb = buf + NV_BYTES + j * X_BYTES;
+      if constexpr (XBF) stash_bf(x[j], xb, lane);
+      else stash_nv(x[j], xb, xb + 32 * 64, lane);
+    }
+    typename S::WOp wo;
+    typename S::XOp xo[MB];
+    read_nv(wo, buf, buf + 32 * 64, lr, lh, kv, K);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const uint8_t* xb = buf + NV_BYTES + j * X_BYTES;
+      if constexpr (XBF) read_bf16(xo[j], xb, lr, lh);
+      else read_nv(xo[j], xb, xb + 32 * 64, lr, lh, kv, K);
+    }
+    S::template mma<MB>(acc, wo, xo);
+  };
+  // Three stages in flight (a wave's whole share at K = 3072); nothing is fetched past the
+  // wave's share (the address unit is the scarce resource here)
+  if (mine > 0) fetch(w0, x0, 0);
+  if (mine > 1) fetch(w1, x1, 1);
+  if (mine > 2) fetch(w2, x2, 2);
+  for (int i = 0; i < mine; i += 3) {
+    consume(w0, x0, i);
+    if (i + 3 < mine) fetch(w0, x0, i + 3);
+    if (i + 1 < mine) {
+      consume(w1, x1, i + 1);
+      if (i + 4 < mine) fetch(w1, x1, i + 4);
+    }
+    if (i + 2 < mine) {
+      consume(w2, x2, i + 2);
+      if (i + 5 < mine) fetch(w2, x2, i + 5);
+    }
   }
+  __syncthreads();  // LDS is reused for the reduction
 
+  float* red = reinterpret_cast<float*>(smem);  // [NW][MB][16][64]
 #pragma unroll
   for (int j = 0; j < MB; ++j)
 #pragma unroll
@@ -356,14 +469,17 @@ __device__ __forceinline__ v4i sgpr(const v4i& r) {
 // DMA of one code region: load ld covers rows RPL * ld .. RPL * ld + RPL - 1; lane l writes
 // physical chunk l % C of its row, so it fetches the logical chunk the swizzle puts there.
 // `kv` is the first K value of the stage, `vpc` the K values per 16-byte chunk.
+// Loads that would only cover rows past `rows` (the tile's rows inside the matrix) are
+// skipped: those rows only feed outputs that are never stored.
 template <int R>
 __device__ __forceinline__ void dma_codes(const v4i& r, uint32_t lds, int lane, int pitch, int kbyte, int kv, int vpc,
-                                          int K) {
+                                          int K, int rows) {
   using G = CodeRegion<R>;
   const v4i rs = sgpr(r);
   const int lrow = lane / G::C, phys = lane % G::C;
 #pragma unroll
   for (int ld = 0; ld < G::LOADS; ++ld) {
+    if (ld * G::RPL >= rows) break;  // uniform
     const int row = ld * G::RPL + lrow;
     const int c = swz_chunk<R>(row, phys);
     const int voff = kv + c * vpc < K ? row * pitch + kbyte + 16 * c : kOutOfRange;
@@ -415,10 +531,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   const v4i rwq = buffer_rsrc(a.w + (int64_t)n0 * K, (uint32_t)(rows_w * K));
   const int xpitch = L::XBF ? (int)(a.ldx * 2) : K;
   v4i rxq[MB];
+  int xrows[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) {
     const int mj = m0 + 32 * j;
     const int rows = M - mj <= 0 ? 0 : M - mj < 32 ? M - mj : 32;
+    xrows[j] = rows;
     if constexpr (L::XBF)
       rxq[j] = buffer_rsrc(a.x + (int64_t)mj * a.ldx, rows ? (uint32_t)((rows - 1) * xpitch + 2 * K) : 0u);
     else
@@ -427,29 +545,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
 
   const uint32_t wave_lds = lds_offset(smem) + (uint32_t)(wave * WAVE);
   const uint8_t* wave_mem = smem + wave * WAVE;
+  const int nk = (K + kSkK - 1) / kSkK;
+  const int rot = (int)(blockIdx.x % (unsigned)nk);
   // fetch this wave's i-th stage into ring buffer i % 2 (stages past K read as zeros)
   auto issue = [&](int i) {
-    const int kv = (wave + NW * i) * kSkK;
+    const int kv = stage_k(wave, NW, i, nk, rot, K);
     const uint32_t base = wave_lds + (uint32_t)((i & 1) * STAGE);
-    dma_codes<128>(rwq, base, lane, K, kv, kv, 16, K);
+    // activation rows first, weight rows last: the weight loads of a stage are its last
+    // L::W_LOADS memory operations (the wait below relies on it)
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
       const uint32_t xb = base + L::W_BYTES + j * L::X_BYTES;
-      if constexpr (L::XBF) dma_codes<256>(rxq[j], xb, lane, xpitch, 2 * kv, kv, 8, K);
-      else dma_codes<128>(rxq[j], xb, lane, xpitch, kv, kv, 16, K);
+      if constexpr (L::XBF) dma_codes<256>(rxq[j], xb, lane, xpitch, 2 * kv, kv, 8, K, xrows[j]);
+      else dma_codes<128>(rxq[j], xb, lane, xpitch, kv, kv, 16, K, xrows[j]);
     }
+    dma_codes<128>(rwq, base, lane, K, kv, kv, 16, K, 32);
   };
 
   v16f acc[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) acc[j] = v16f{};
 
-  const int nk = (K + kSkK - 1) / kSkK;
   const int mine = nk > wave ? (nk - wave + NW - 1) / NW : 0;  // uniform per wave
-  issue(0);
-  issue(1);
+  // Nothing is fetched past the wave's share. A stage issues a variable number of activation
+  // loads (rows past M are skipped) followed by exactly L::W_LOADS weight loads, and loads
+  // complete in order: once at most L::W_LOADS are outstanding, stage i has landed.
+  if (mine > 0) issue(0);
+  if (mine > 1) issue(1);
   for (int i = 0; i < mine; ++i) {
-    wait_vm_fence<(kSkRing - 1) * LOADS>();  // this wave's stage i has landed
+    if (i + 1 < mine) wait_vm_fence<L::W_LOADS>();  // stage i has landed
+    else wait_vm_fence<0>();
     const uint8_t* st = wave_mem + (i & 1) * STAGE;
     typename S::WOp w;
     typename S::XOp x[MB];
@@ -461,7 +586,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
       else read_f8(x[j], xb, lr, lh);
     }
     wait_lds_fence();  // the buffer is free again
-    issue(i + 2);
+    if (i + 2 < mine) issue(i + 2);
     S::template mma<MB>(acc, w, x);
   }
   wait_vm_fence<0>();
@@ -485,20 +610,22 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 template <int MODE, int MB>
-hipError_t run_direct(const DecArgs& a, hipStream_t s) {
+hipError_t run_staged(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = ((a.N + 31) / 32) * ((a.M + 32 * MB - 1) / (32 * MB));
-  hipLaunchKernelGGL((gemm_skinny_direct_kernel<MODE, MB>), dim3((unsigned)blocks), dim3(64 * kSkDirectWaves), 0, s,
+  hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB>), dim3((unsigned)blocks), dim3(64 * kSkStagedWaves), 0, s,
                      a);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t pick(const DecArgs& a, hipStream_t s) {
-  if constexpr (MODE == kW4A4 || MODE == kW4A16) {
-    if (a.M <= 32) return run_direct<MODE, 1>(a, s);
-    return run_direct<MODE, 2>(a, s);
+  if constexpr (MODE == kW4A4) {
+    if (a.M <= 32) return run_staged<MODE, 1>(a, s);
+    return run_staged<MODE, 2>(a, s);
+  } else if constexpr (MODE == kW4A16) {
+    // bf16 activations fill registers and LDS fastest: one activation block per workgroup
+    return run_staged<MODE, 1>(a, s);
   } else if constexpr (MODE == kW8A16) {
-    // bf16 activations fill LDS fastest: one activation block per workgroup
     return run<MODE, 1, 4>(a, s);
   } else {
     if (a.M <= 32) return run<MODE, 1, 4>(a, s);

@@ -86,7 +86,7 @@ struct SkinnyRule {
 SkinnyRule skinny_rule(bsq::DecMode mode) {
   switch (mode) {
     case bsq::kW4A4: return {32, 128};
-    case bsq::kW4A16: return {64, 256};
+    case bsq::kW4A16: return {128, 256};
     case bsq::kW8A8: return {32, 256};
     default: return {128, 256};  // W8A16
   }

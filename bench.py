@@ -92,12 +92,94 @@ def cpu_baseline(rows=64, reps=2):
                       % (rows, M, reps, dt)}
 
 
+def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)):
+    """Few-token GEMMs (K = 3072), all four schemes, with cold weights.
+
+    Each configuration is launched 24 times back to back between two events, rotating over
+    enough weight copies (> 600 MB) that no launch finds its weights in the 256 MB Infinity
+    Cache; activations are pre-quantized for W4A4 / W8A8 (the quantizer is timed separately).
+    Bytes are the algorithmic ones: weights + activations + Y.
+    """
+    import torch
+
+    lib = L.lib
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def up_bf16(bits):
+        return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
+
+    def timed(calls, iters=24, warm=3):
+        for i in range(warm):
+            calls[i % len(calls)]()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e3  # us
+
+    def check(st):
+        if st != 0:
+            raise L.BsqError("small-M sweep", st)
+
+    rows = []
+    for N in Ns:
+        w = up_bf16(syn.weights(syn.SMALL_M, N, K))
+        gw = L.bsq_calibrate_global_scale(w)
+        wp, ws = L.bsq_quantize_act_nvfp4(w, gw)
+        wq, sw = L.bsq_quantize_act_fp8r(w)
+        del w
+        r4 = int(600e6 // (wp.numel() + ws.numel())) + 1
+        r8 = int(600e6 // wq.numel()) + 1
+        W4 = [(wp.clone(), ws.clone()) for _ in range(r4)]
+        W8 = [(wq.clone(), sw.clone()) for _ in range(r8)]
+        for Mi in Ms:
+            x = up_bf16(syn.activations(syn.SMALL_M, Mi, K))
+            gx = L.bsq_calibrate_global_scale(x)
+            xq8, sx8 = L.bsq_quantize_act_fp8r(x)
+            xq4, sx4 = L.bsq_quantize_act_nvfp4(x, gx)
+            y = torch.empty((Mi, N), dtype=torch.bfloat16, device=dev)
+            us = {
+                "w4a4": timed([lambda i=i: check(lib.bsq_gemm_nvfp4_q(P(xq4), P(sx4), P(gx), P(W4[i][0]), P(W4[i][1]),
+                                                                      P(gw), P(y), N, Mi, N, K, stream))
+                               for i in range(r4)]),
+                "w4a16": timed([lambda i=i: check(lib.bsq_gemm_nvfp4(P(x), K, P(W4[i][0]), P(W4[i][1]), P(gw), None,
+                                                                     P(y), N, Mi, N, K, L.BSQ_WEIGHT_ONLY, None, 0,
+                                                                     stream))
+                                for i in range(r4)]),
+                "w8a8": timed([lambda i=i: check(lib.bsq_gemm_fp8r_q(P(xq8), P(sx8), P(W8[i][0]), P(W8[i][1]), P(y),
+                                                                     N, Mi, N, K, stream))
+                               for i in range(r8)]),
+                "w8a16": timed([lambda i=i: check(lib.bsq_gemm_fp8r(P(x), K, P(W8[i][0]), P(W8[i][1]), P(y), N, Mi,
+                                                                    N, K, L.BSQ_WEIGHT_ONLY, None, 0, stream))
+                                for i in range(r8)]),
+            }
+            nbytes = {
+                "w4a4": N * K // 2 + N * K // 16 + Mi * K // 2 + Mi * K // 16 + 2 * Mi * N,
+                "w4a16": N * K // 2 + N * K // 16 + 2 * Mi * K + 2 * Mi * N,
+                "w8a8": N * K + 4 * N + Mi * K + 4 * Mi + 2 * Mi * N,
+                "w8a16": N * K + 4 * N + 2 * Mi * K + 2 * Mi * N,
+            }
+            rows.append({"M": Mi, "N": N, "us": {k: round(v, 2) for k, v in us.items()},
+                         "hbm_frac": {k: round(nbytes[k] / (us[k] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) for k in us},
+                         "tflops": {k: round(2.0 * Mi * N * K / (us[k] * 1e-6) / 1e12, 1) for k in us}})
+            log("small-M M=%d N=%d: %s" % (Mi, N, rows[-1]["us"]))
+        del W4, W8
+        torch.cuda.empty_cache()
+    return {"K": K, "cold": True, "rows": rows,
+            "note": "kernel time per call from events around 24 back-to-back launches (weights rotated over > 600 MB); "
+                    "hbm_frac = (weights + activations + Y bytes) / time / 8 TB/s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-small-m", action="store_true", help="skip the few-token sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (requested %d)" % args.gpus,
@@ -251,6 +333,9 @@ def main():
         "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
         "hbm_frac": {k: round(v / PEAK_HBM_GBS, 4) for k, v in hbm.items()},
     }
+    if not args.no_small_m:
+        log("few-token sweep")
+        result["small_m"] = small_m_sweep(L, syn, dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline()

@@ -2,7 +2,8 @@
 
 Two steps, run on one MI355X:
 
-  1. the workload, once under each counter (FETCH_SIZE, then WRITE_SIZE):
+  1. the workload, once under each counter (FETCH_SIZE, then WRITE_SIZE), from any directory
+     with the repository on the module path (cd /tmp && export TMPDIR=/tmp PYTHONPATH=<repo>):
          rocprofv3 --pmc FETCH_SIZE -d <d1> -o run --output-format csv -- python3 -m block_scaled_precision_row_amd.traffic run
          rocprofv3 --pmc WRITE_SIZE -d <d2> -o run --output-format csv -- python3 -m block_scaled_precision_row_amd.traffic run
      It launches a plain device copy of a known size (torch's copy kernel,

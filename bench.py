@@ -173,6 +173,88 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
                     "hbm_frac = (weights + activations + Y bytes) / time / 8 TB/s"}
 
 
+def joint_block_sweep(L, syn, dev, reps=5):
+    """The 4-megapixel joint-block workload: 16384 tokens through the four linears of a block
+    (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288), once as an nvfp4 W4A4 block
+    and once as an fp8r W8A8 block (the 28 blocks alternate the two schemes).
+
+    Weights follow the synthetic recipe (blocks 0 and 1); the two activation tensors
+    ([16384, 3072] and [16384, 12288], N(0, 1)) are drawn on the GPU with a fixed seed for speed.
+    Activations are quantized once per scheme outside the timing; each GEMM is timed over `reps`
+    back-to-back launches. `gemm_ms_28_blocks` = 14 x (nvfp4 block) + 14 x (fp8r block).
+    """
+    import torch
+
+    lib = L.lib
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    Mj = syn.JOINT_TOKENS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    xs = {k: torch.randn((Mj, k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+          for k in sorted({kk for _, _, kk in syn.JOINT_GEMMS})}
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    def check(st):
+        if st != 0:
+            raise L.BsqError("joint-block sweep", st)
+
+    out = {"tokens": Mj, "gemms": []}
+    block_us = {"nvfp4": 0.0, "fp8r": 0.0}
+    quant_us = {"nvfp4": 0.0, "fp8r": 0.0}
+    for scheme, block in (("nvfp4", 0), ("fp8r", 1)):
+        xq = {}
+        for k, x in xs.items():
+            if scheme == "nvfp4":
+                gx = L.bsq_calibrate_global_scale(x)
+                q, sq = L.bsq_quantize_act_nvfp4(x, gx)
+                xq[k] = (q, sq, gx)
+                quant_us[scheme] += timed(lambda: check(lib.bsq_quantize_act_nvfp4(P(x), Mj, k, k, P(gx), P(q), P(sq),
+                                                                                    stream)))
+            else:
+                q, sq = L.bsq_quantize_act_fp8r(x)
+                xq[k] = (q, sq, None)
+                quant_us[scheme] += timed(lambda: check(lib.bsq_quantize_act_fp8r(P(x), Mj, k, k, P(q), P(sq), stream)))
+        for gi, (name, N, Kj) in enumerate(syn.JOINT_GEMMS):
+            w = torch.from_numpy(syn.weights(syn.JOINT_4MP, N, Kj, block=block * 4 + gi).view("int16")) \
+                .to(dev).view(torch.bfloat16)
+            y = torch.empty((Mj, N), dtype=torch.bfloat16, device=dev)
+            q, sq, gx = xq[Kj]
+            if scheme == "nvfp4":
+                gw = L.bsq_calibrate_global_scale(w)
+                wq, ws = L.bsq_quantize_act_nvfp4(w, gw)
+                us = timed(lambda: check(lib.bsq_gemm_nvfp4_q(P(q), P(sq), P(gx), P(wq), P(ws), P(gw), P(y), N, Mj, N,
+                                                              Kj, stream)))
+                peak = PEAK_F16_TFLOPS
+            else:
+                wq, ws = L.bsq_quantize_act_fp8r(w)
+                us = timed(lambda: check(lib.bsq_gemm_fp8r_q(P(q), P(sq), P(wq), P(ws), P(y), N, Mj, N, Kj, stream)))
+                peak = PEAK_FP8_TFLOPS
+            tf = 2.0 * Mj * N * Kj / (us * 1e-6) / 1e12
+            out["gemms"].append({"scheme": scheme, "gemm": name, "N": N, "K": Kj, "us": round(us, 1),
+                                 "tflops": round(tf, 1), "frac_peak": round(tf / peak, 4)})
+            block_us[scheme] += us
+            log("joint block %s %s %dx%dx%d: %.1f us, %.0f TFLOP/s" % (scheme, name, Mj, N, Kj, us, tf))
+            del w, y
+    out["block_us"] = {k: round(v, 1) for k, v in block_us.items()}
+    out["activation_quant_us_per_block"] = {k: round(v, 1) for k, v in quant_us.items()}
+    out["gemm_ms_28_blocks"] = round(14 * (block_us["nvfp4"] + block_us["fp8r"]) / 1e3, 2)
+    out["note"] = ("peaks: f16 MFMA for nvfp4 (decoded operands), fp8 MFMA for fp8r; activations pre-quantized "
+                   "(their quantization time per block listed separately)")
+    del xs
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +262,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-small-m", action="store_true", help="skip the few-token sweep")
+    ap.add_argument("--no-joint", action="store_true", help="skip the 16384-token joint-block shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (requested %d)" % args.gpus,
@@ -336,6 +419,9 @@ def main():
     if not args.no_small_m:
         log("few-token sweep")
         result["small_m"] = small_m_sweep(L, syn, dev)
+    if not args.no_joint:
+        log("joint-block shapes")
+        result["joint_block_4mp"] = joint_block_sweep(L, syn, dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline()

@@ -200,3 +200,15 @@ def test_skinny_all_schemes(M, N, K):
     run_fp8r(x, w, weight_only=True, what="fp8r-w8a16 " + tag)
     run_nvfp4(x, w, what="nvfp4 " + tag)
     run_nvfp4(x, w, weight_only=True, what="nvfp4-w4a16 " + tag)
+
+
+# W4A4 shapes with more output tiles than compute units, ragged M and N tails, both tile
+# configurations, and both parities of the number of 256-deep K stages per tile.
+PERSISTENT_SHAPES = [(4100, 4100, 768), (4100, 4100, 1024), (1000, 5000, 512), (4100, 2300, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", PERSISTENT_SHAPES)
+def test_w4a4_several_tiles_per_workgroup(M, N, K):
+    x = syn.normal_bf16((M, K), 53, M)
+    w = syn.normal_bf16((N, K), 53, 3000 + N, sigma=0.02)
+    run_nvfp4(x, w, sample=96, what="nvfp4 rounds %dx%dx%d" % (M, N, K))

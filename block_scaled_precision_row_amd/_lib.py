@@ -40,6 +40,9 @@ SIGNATURES = {
     "bsq_dequant_to_bf16": (_int, [_int, _p, _p, _p, _i64, _i64, _p, _p]),
     "bsq_gemm_fp8r_q": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "bsq_gemm_nvfp4_q": (_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
+    "bsq_gemm_nvfp4_quantize_y_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "bsq_gemm_nvfp4_q_quantize_y": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
+                                           _p]),
 }
 
 
@@ -213,6 +216,40 @@ def bsq_gemm_nvfp4_q(xq, x_bscale, input_scale, w, w_bscale, w_scale2, y=None):
                                                     _ptr(w_bscale), _ptr(w_scale2), _ptr(y), ldy, M, N, K,
                                                     _stream()))
     return y
+
+
+def bsq_gemm_nvfp4_q_quantize_y(xq, x_bscale, input_scale, w, w_bscale, w_scale2, y_scale, with_y=False,
+                                yq=None, y_bscale=None, y=None, workspace=None):
+    """W4A4 GEMM as bsq_gemm_nvfp4_q whose output is also (or only) returned in nvfp4 with global scale
+    y_scale [1]: (yq uint8 [M, N/2], y_bscale uint8 [M, N/16], bf16 y [M, N] or None)."""
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = w.shape[0]
+    _dense(xq, torch.uint8, (M, K // 2), "xq")
+    _dense(x_bscale, torch.uint8, (M, K // 16), "x_bscale")
+    _scalar(input_scale, "input_scale")
+    _dense(w, torch.uint8, (N, K // 2), "w")
+    _dense(w_bscale, torch.uint8, (N, K // 16), "w_bscale")
+    _scalar(w_scale2, "w_scale2")
+    _scalar(y_scale, "y_scale")
+    dev = xq.device
+    yq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev) if yq is None else yq
+    y_bscale = torch.empty((M, N // 16), dtype=torch.uint8, device=dev) if y_bscale is None else y_bscale
+    _dense(yq, torch.uint8, (M, N // 2), "yq")
+    _dense(y_bscale, torch.uint8, (M, N // 16), "y_bscale")
+    ldy = 0
+    if with_y or y is not None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+        _, _, ldy = _rows(y, torch.bfloat16, "y")
+    nws = lib.bsq_gemm_nvfp4_quantize_y_workspace_bytes(M, N, K, 1 if y is not None else 0)
+    if workspace is None and nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check("bsq_gemm_nvfp4_q_quantize_y",
+           lib.bsq_gemm_nvfp4_q_quantize_y(_ptr(xq), _ptr(x_bscale), _ptr(input_scale), _ptr(w), _ptr(w_bscale),
+                                           _ptr(w_scale2), _ptr(y_scale), _ptr(yq), _ptr(y_bscale),
+                                           _ptr(y) if y is not None else None, ldy, M, N, K,
+                                           _ptr(workspace) if workspace is not None else None,
+                                           workspace.numel() if workspace is not None else 0, _stream()))
+    return yq, y_bscale, y
 
 
 def bsq_dequant_to_bf16(fmt, w, w_scale, w_scale2=None, out=None):

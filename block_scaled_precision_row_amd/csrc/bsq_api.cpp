@@ -271,6 +271,59 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
+size_t bsq_gemm_nvfp4_quantize_y_workspace_bytes(int64_t M, int64_t N, int64_t K, int with_y) {
+  if (with_y || M <= 0 || N <= 0 || K <= 0) return 0;
+  bsq::DecArgs a{};
+  a.M = M; a.N = N; a.K = K;
+  if (route_skinny(bsq::kW4A4, a) || bsq::gemm_w4a4_supported(a)) return 0;
+  return pad256((size_t)M * (size_t)N * 2);
+}
+
+bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
+                                       const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2,
+                                       const float* y_scale, uint8_t* yq, uint8_t* y_bscale, uint16_t* y,
+                                       int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  // without a bf16 output the shape is checked as for a dense [M][N] one, with yq standing in
+  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w,
+                                    y ? y : reinterpret_cast<uint16_t*>(yq), y ? ldy : N, M, N, K, 0);
+  if (st != BSQ_OK) return st;
+  if (N % 32 != 0 || (y && ldy % 8 != 0)) return BSQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!x_bscale || !input_scale || !w_bscale || !w_scale2 || !y_scale || !yq || !y_bscale) return BSQ_ERR_NULL;
+  if (!aligned(x_bscale, 4) || !aligned(input_scale, 4) || !aligned(w_bscale, 4) || !aligned(w_scale2, 4) ||
+      !aligned(y_scale, 4) || !aligned(yq, 16))
+    return BSQ_ERR_ALIGN;
+  if (M * (N / 16) >= kMaxThreads) return BSQ_ERR_SHAPE;
+  bsq::DecArgs a{};
+  a.xq = xq; a.xs = x_bscale; a.gx = input_scale; a.w = w; a.ws = w_bscale; a.gw = w_scale2;
+  a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
+  a.yq = yq; a.ys = y_bscale; a.gy = y_scale;
+  const bool fused = route_skinny(bsq::kW4A4, a) || bsq::gemm_w4a4_supported(a);
+  uint16_t* ybuf = y;
+  int64_t ldb = ldy;
+  if (!fused && !y) {
+    if (!workspace || workspace_bytes < bsq_gemm_nvfp4_quantize_y_workspace_bytes(M, N, K, 0) ||
+        !aligned(workspace, 16))
+      return BSQ_ERR_WORKSPACE;
+    ybuf = static_cast<uint16_t*>(workspace);
+    ldb = N;
+  }
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e;
+  if (route_skinny(bsq::kW4A4, a)) {
+    e = bsq::launch_gemm_skinny(bsq::kW4A4, a, stream);
+  } else if (fused) {
+    e = bsq::launch_gemm_w4a4(a, stream);
+  } else {
+    // unfused: bf16 Y (into y or the workspace), then the activation quantizer over it
+    a.y = ybuf; a.ldy = ldb; a.yq = nullptr; a.ys = nullptr; a.gy = nullptr;
+    e = bsq::launch_gemm_dec(bsq::kW4A4, a, stream);
+    if (e == hipSuccess) e = bsq::launch_quant_nvfp4(ybuf, M, N, ldb, y_scale, yq, y_bscale, stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
 bsq_status bsq_dequant_to_bf16(bsq_format f, const uint8_t* w, const void* w_scale, const float* w_scale2,
                                int64_t N, int64_t K, uint16_t* w_bf16, hipStream_t stream) {
   if (f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;

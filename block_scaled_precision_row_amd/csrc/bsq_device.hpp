@@ -90,6 +90,37 @@ __device__ __forceinline__ v2h dec_e2m1x2_f16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, sel);
 }
 
+// ---- nvfp4 block quantizer ---------------------------------------------------------
+// One 16-element block ("BFL (fp8r / nvfp4)", nvfp4 bullet; every step one IEEE-rounded fp32
+// operation): a = max |f|, sf = E4M3(fp32(fp32(a / 6) * G)), r = fp32(G / sf) (0 when sf
+// is 0), q = E2M1(fp32(f * r)); G = fp32(1 / g) is passed in. Returns the scale byte and
+// the 16 codes packed in `codes` (element 0 in the low nibble). Used by the activation
+// quantizer and by the GEMM epilogue that quantizes its own output, so both give identical
+// bits for the same inputs.
+__device__ __forceinline__ uint32_t quant_block16_nvfp4(float (&f)[16], float G, uint2& codes) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
+  const float u = (a / kE2M1Max) * G;
+  const uint32_t sf = enc_e4m3(u);
+  const float sfv = dec_e4m3<0>(sf);
+  const float r = sfv > 0.0f ? G / sfv : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = f[i] * r;
+  codes.x = enc_e2m1x8(f);
+  codes.y = enc_e2m1x8(f + 8);
+  return sf;
+}
+// the 16 bf16 values of two 16-byte chunks as fp32
+__device__ __forceinline__ void bf16x16_to_f32(uint4 v0, uint4 v1, float (&f)[16]) {
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
 // ---- streaming stores ----------------------------------------------------------
 // 16-byte store with the non-temporal hint, for outputs that this kernel does
 // not read back (dequantized weights, GEMM results)

@@ -43,9 +43,12 @@ struct DecArgs {
   const float* gw;     // weight global scale (nvfp4)
   const float* sw;     // per-row weight scales [N] (W8A16, W8A8)
   const float* sx;     // per-row activation scales [M] (W8A8)
-  uint16_t* y;
+  uint16_t* y;         // bf16 output [M][ldy]; may be null when yq is set (W4A4 only)
   int64_t ldy;
   int64_t M, N, K;
+  uint8_t* yq;         // optional nvfp4 copy of Y for the next linear: packed E2M1 [M][N/2] (W4A4)
+  uint8_t* ys;         // its E4M3 block scales [M][N/16]
+  const float* gy;     // its global scale (the next linear's input_scale)
 };
 hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
 // W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0

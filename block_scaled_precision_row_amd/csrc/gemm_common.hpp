@@ -162,6 +162,30 @@ __device__ __forceinline__ void store_tile_rows(const uint8_t* tile, uint16_t* _
   }
 }
 
+// Quantize a bf16 output tile [BM][BN] (rows TROW bytes apart in LDS) to nvfp4 for the next
+// linear: each 16-value block along n becomes 8 bytes of E2M1 codes in yq [M][N/2] and one
+// E4M3 scale in ys [M][N/16], with the activation quantizer's arithmetic (N % 32 == 0, so
+// blocks never straddle the matrix edge). Consecutive threads take consecutive blocks of a row.
+template <int BM, int BN, int TROW>
+__device__ __forceinline__ void quant_tile_rows(const uint8_t* tile, uint8_t* __restrict__ yq, uint8_t* __restrict__ ys,
+                                                float G, int M, int N, int m0, int n0, int tid) {
+  constexpr int BPR = BN / 16;  // blocks per tile row
+  for (int idx = tid; idx < BM * BPR; idx += kThreads) {
+    const int ml = idx / BPR, b = idx - ml * BPR;
+    const int m = m0 + ml, n = n0 + 16 * b;
+    if (m >= M) break;  // rows only grow with idx
+    if (n >= N) continue;
+    const uint4 v0 = *reinterpret_cast<const uint4*>(tile + ml * TROW + 32 * b);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(tile + ml * TROW + 32 * b + 16);
+    float f[16];
+    bf16x16_to_f32(v0, v1, f);
+    uint2 codes;
+    const uint32_t sf = quant_block16_nvfp4(f, G, codes);
+    *reinterpret_cast<uint2*>(yq + (int64_t)m * (N >> 1) + (n >> 1)) = codes;
+    ys[(int64_t)m * (N >> 4) + (n >> 4)] = (uint8_t)sf;
+  }
+}
+
 // tile index of this workgroup (XCD-contiguous, grouped along M)
 __device__ __forceinline__ void tile_of_block(int M, int N, int BM, int BN, int& m0, int& n0) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;

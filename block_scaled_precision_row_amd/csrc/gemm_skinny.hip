@@ -193,7 +193,7 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
   if constexpr (MODE == kW4A4) alpha = a.gx[0] * a.gw[0];
   if constexpr (MODE == kW4A16) alpha = a.gw[0];
   // thread -> (row ml of the tile, output pair p): consecutive threads write consecutive pairs
-  for (int idx = tid; idx < 32 * MB * 16; idx += 64 * NW) {
+  for (int idx = tid; a.y && idx < 32 * MB * 16; idx += 64 * NW) {
     const int ml = idx >> 4, p = idx & 15;
     const int m = m0 + ml;
     if (m >= M) break;
@@ -225,6 +225,33 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
       *reinterpret_cast<uint32_t*>(yr + n) = pk;
     } else if (n < N) {
       yr[n] = (uint16_t)(pk & 0xFFFFu);
+    }
+  }
+  // W4A4 only: the nvfp4 encoding of Y for the next linear, from the same bf16 values
+  if constexpr (MODE == kW4A4) {
+    if (a.yq) {
+      const float G = 1.0f / a.gy[0];
+      for (int idx = tid; idx < 32 * MB * 2; idx += 64 * NW) {  // (row, 16-block) of the tile
+        const int ml = idx >> 1, blk = idx & 1;
+        const int m = m0 + ml, n = n0 + 16 * blk;
+        if (m >= M) break;
+        if (n >= N) continue;
+        const int j = ml >> 5, lm = ml & 31;
+        float f[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int nl = 16 * blk + e;
+          const int r = 4 * (nl >> 3) + (nl & 3), ln = lm + 32 * ((nl >> 2) & 1);
+          float sum = 0.0f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) sum += red[((w * MB + j) * 16 + r) * 64 + ln];
+          f[e] = bf16_lo(pack_bf16x2(sum * alpha, 0.0f));  // the value the bf16 output holds
+        }
+        uint2 codes;
+        const uint32_t sf = quant_block16_nvfp4(f, G, codes);
+        *reinterpret_cast<uint2*>(a.yq + (int64_t)m * (N >> 1) + (n >> 1)) = codes;
+        a.ys[(int64_t)m * (N >> 4) + (n >> 4)] = (uint8_t)sf;
+      }
     }
   }
 }

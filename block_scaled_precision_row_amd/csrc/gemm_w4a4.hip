@@ -276,7 +276,11 @@ void gemm_w4a4_kernel(DecArgs a) {
     }
   }
   __syncthreads();
-  store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid);
+  if (a.y) store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid);
+  // optionally the nvfp4 encoding of Y for the next linear ("BFL (fp8r / nvfp4)": every
+  // quantized linear quantizes its input at run time); its 16-blocks run along this N, inside
+  // the tile
+  if (a.yq) quant_tile_rows<BM, BN, C::TROW>(smem, a.yq, a.ys, 1.0f / a.gy[0], M, N, m0, n0, tid);
 }
 
 template <int BM, int BN>

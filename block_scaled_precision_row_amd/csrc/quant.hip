@@ -87,23 +87,11 @@ __global__ __launch_bounds__(256) void quant_nvfp4_blocks(const uint16_t* __rest
   const uint16_t* p = x + row * ldx + (int64_t)b * 16;
   const uint4 v0 = *reinterpret_cast<const uint4*>(p);
   const uint4 v1 = *reinterpret_cast<const uint4*>(p + 8);
-  float f[16] = {bf16_lo(v0.x), bf16_hi(v0.x), bf16_lo(v0.y), bf16_hi(v0.y),
-                 bf16_lo(v0.z), bf16_hi(v0.z), bf16_lo(v0.w), bf16_hi(v0.w),
-                 bf16_lo(v1.x), bf16_hi(v1.x), bf16_lo(v1.y), bf16_hi(v1.y),
-                 bf16_lo(v1.z), bf16_hi(v1.z), bf16_lo(v1.w), bf16_hi(v1.w)};
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
+  float f[16];
+  bf16x16_to_f32(v0, v1, f);
   const float G = 1.0f / gptr[0];
-  const float u = (a / kE2M1Max) * G;
-  const uint32_t sf = enc_e4m3(u);
-  const float sfv = dec_e4m3<0>(sf);
-  const float r = sfv > 0.0f ? G / sfv : 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) f[i] = f[i] * r;
   uint2 o;
-  o.x = enc_e2m1x8(f);
-  o.y = enc_e2m1x8(f + 8);
+  const uint32_t sf = quant_block16_nvfp4(f, G, o);
   *reinterpret_cast<uint2*>(xq + row * (int64_t)(K >> 1) + (int64_t)b * 8) = o;
   xs[row * (int64_t)nb + b] = (uint8_t)sf;
 }

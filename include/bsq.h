@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define BSQ_ABI_VERSION 1
+#define BSQ_ABI_VERSION 2
 
 typedef enum {
   BSQ_OK = 0,
@@ -171,6 +171,30 @@ bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_
 bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
                             const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2, uint16_t* y,
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * W4A4 linear whose output is also handed to the next quantized linear in
+ * nvfp4 ("BFL (fp8r / nvfp4)": every quantized linear quantizes its input at
+ * run time; here the producing GEMM does it in its epilogue, where the
+ * 16-element blocks -- along this N, the next linear's K -- lie inside one
+ * output tile). Y is the bsq_gemm_nvfp4_q result; yq / y_bscale are exactly
+ * what bsq_quantize_act_nvfp4(Y, y_scale) returns for that bf16 Y:
+ *   xq, x_bscale, input_scale, w, w_bscale, w_scale2: as bsq_gemm_nvfp4_q
+ *   y_scale   [1] fp32: global scale of Y's encoding (the next input_scale)
+ *   yq        [M][N/2] packed E2M1 (16-byte aligned), y_bscale [M][N/16] E4M3
+ *   y         [M][ldy] bf16, or NULL to skip writing the bf16 output
+ * Requires N % 32 == 0 (BSQ_ERR_SHAPE otherwise). Shapes that the fused
+ * kernels do not cover (K % 256 != 0 beyond the few-token range) run the
+ * GEMM and then the quantizer; with y == NULL they need a workspace of
+ * bsq_gemm_nvfp4_quantize_y_workspace_bytes(M, N, K, 0) bytes (16-byte
+ * aligned, 0 for every other shape); the query with with_y != 0 returns 0.
+ */
+size_t bsq_gemm_nvfp4_quantize_y_workspace_bytes(int64_t M, int64_t N, int64_t K, int with_y);
+bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
+                                       const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2,
+                                       const float* y_scale, uint8_t* yq, uint8_t* y_bscale, uint16_t* y,
+                                       int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fallback dequantization to bf16 ("BFL (fp8r / nvfp4)", last paragraph of

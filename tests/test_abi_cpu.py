@@ -33,12 +33,12 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 13
+    assert len(syms) == 15
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
         assert s in _lib.SIGNATURES, s
-    assert L.bsq_abi_version() == 1
+    assert L.bsq_abi_version() == 2
     assert L.bsq_status_string(SHAPE).decode().startswith("invalid shape")
 
 
@@ -90,6 +90,23 @@ def test_gemm_validation():
     assert n(A, 64, B, C, D, D, A, 64, 64, 64, 64, 0, None, 0, None) == WS
     assert n(A, 64, B, ODD, D, D, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == ALIGN
     assert n(A, 64, B, C, D, None, A, 64, 64, 64, 64, 4, None, 0, None) == ARG
+
+
+def test_quantize_y_validation():
+    q = L.bsq_gemm_nvfp4_q_quantize_y
+    # xq, x_bscale, input_scale, w, w_bscale, w_scale2, y_scale, yq, y_bscale, y, ldy, M, N, K, ws, ws_bytes, stream
+    assert q(A, B, C, A, B, C, D, A, B, None, 0, 64, 48, 256, None, 0, None) == SHAPE     # N % 32
+    assert q(A, B, C, A, B, C, D, A, B, D, 68, 64, 64, 256, None, 0, None) == SHAPE       # ldy % 8
+    assert q(A, B, C, A, B, C, None, A, B, None, 0, 64, 64, 256, None, 0, None) == NULL   # y_scale
+    assert q(A, B, C, A, B, C, D, A, None, None, 0, 64, 64, 256, None, 0, None) == NULL   # y_bscale
+    assert q(A, B, C, A, B, C, D, ODD, B, None, 0, 64, 64, 256, None, 0, None) == ALIGN  # yq
+    assert q(A, B, C, A, B, C, D, A, B, None, 0, 0, 64, 256, None, 0, None) == OK         # empty
+    # K % 256 != 0 beyond the few-token range has no fused kernel: without y it needs a workspace
+    assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(4096, 1024, 96, 0) == 4096 * 1024 * 2
+    assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(4096, 1024, 96, 1) == 0
+    assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(4096, 1024, 512, 0) == 0
+    assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(16, 1024, 96, 0) == 0
+    assert q(A, B, C, A, B, C, D, A, B, None, 0, 4096, 1024, 96, None, 0, None) == WS
 
 
 def test_dequant_validation():

@@ -92,6 +92,44 @@ def cpu_baseline(rows=64, reps=2):
                       % (rows, M, reps, dt)}
 
 
+def quantized_output_comparison(L, dev, y3, gemm_args, operands):
+    """The W4A4 linear 4096x12288x3072 feeding another nvfp4 linear: GEMM, then the activation
+    quantizer over the bf16 Y, against the GEMM that quantizes Y in its epilogue (bit-identical
+    codes), with and without writing the bf16 Y. Ten back-to-back repetitions each, in us."""
+    import torch
+
+    lib = L.lib
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    xq, xs, gx, wq, ws, gw = operands
+    gy = L.bsq_calibrate_global_scale(y3)
+    yq = torch.empty((M, N_FP4 // 2), dtype=torch.uint8, device=dev)
+    ys = torch.empty((M, N_FP4 // 16), dtype=torch.uint8, device=dev)
+    fused_args = (P(xq), P(xs), P(gx), P(wq), P(ws), P(gw), P(gy), P(yq), P(ys))
+    variants = {
+        "gemm_then_quantizer": [(lib.bsq_gemm_nvfp4_q, gemm_args),
+                                (lib.bsq_quantize_act_nvfp4, (P(y3), M, N_FP4, N_FP4, P(gy), P(yq), P(ys), stream))],
+        "fused_no_bf16_y": [(lib.bsq_gemm_nvfp4_q_quantize_y, fused_args + (None, 0, M, N_FP4, K, None, 0, stream))],
+        "fused_with_bf16_y": [(lib.bsq_gemm_nvfp4_q_quantize_y,
+                               fused_args + (P(y3), N_FP4, M, N_FP4, K, None, 0, stream))],
+    }
+    out = {}
+    for name, calls in variants.items():
+        for fn, a in calls:
+            fn(*a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            for fn, a in calls:
+                st = fn(*a)
+                if st != 0:
+                    raise L.BsqError(fn.__name__, st)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / 10 * 1e3, 2)
+    return out
+
+
 def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)):
     """Few-token GEMMs (K = 3072), all four schemes, with cold weights.
 
@@ -263,7 +301,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-small-m", action="store_true", help="skip the few-token sweep")
     ap.add_argument("--no-joint", action="store_true", help="skip the 16384-token joint-block shapes")
+    ap.add_argument("--no-quant-out", action="store_true", help="skip the quantized-output comparison")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step only (no CPU baseline, no extra measurements), e.g. under a profiler")
     args = ap.parse_args()
+    if args.only_step:
+        args.no_cpu_baseline = args.no_small_m = args.no_joint = args.no_quant_out = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (requested %d)" % args.gpus,
               file=sys.stderr)
@@ -416,6 +459,10 @@ def main():
         "hbm_gbs": {k: round(v, 1) for k, v in hbm.items()},
         "hbm_frac": {k: round(v / PEAK_HBM_GBS, 4) for k, v in hbm.items()},
     }
+    if not args.no_quant_out:
+        log("quantized-output comparison")
+        result["w4a4_quantized_output_us"] = quantized_output_comparison(
+            L, dev, y3, seq[DOM][1], (x3q, x3s, gx3, w3q, w3s, g3))
     if not args.no_small_m:
         log("few-token sweep")
         result["small_m"] = small_m_sweep(L, syn, dev)

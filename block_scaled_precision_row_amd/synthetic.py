@@ -70,3 +70,16 @@ JOINT_TOKENS = 16384
 def joint_scheme(block):
     """Even joint blocks carry nvfp4 weights, odd ones fp8r."""
     return "nvfp4" if block % 2 == 0 else "fp8r"
+
+
+# low-rank adapters (LoRA) on a linear of any workload: A [rank, K] ~ N(0, 1 / K) (unit-variance
+# X A^T for unit-variance X), B [N, rank] ~ N(0, 0.02^2); their tensor ids follow the layer's
+LORA_A_ID, LORA_B_ID = 3, 4
+LORA_B_SIGMA = 0.02
+
+
+def lora_adapter(workload, rank, N, K, block=0):
+    """(A bits [rank, K], B bits [N, rank]) of a synthetic adapter on an N x K linear."""
+    a = normal_bf16((rank, K), workload, LORA_A_ID, block, float(1.0 / np.sqrt(K)))
+    b = normal_bf16((N, rank), workload, LORA_B_ID, block, LORA_B_SIGMA)
+    return a, b

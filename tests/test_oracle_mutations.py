@@ -101,3 +101,35 @@ def test_rowwise_fp8r_max_over_columns_caught(monkeypatch):
         return codec.encode_e4m3(codec.rn32(x * r[:, None])), d.astype(np.float32)
     monkeypatch.setattr(quant, "quantize_fp8r", bad)
     _fails(tq.test_fp8r_row_max_lands_on_448_and_error_bound)
+
+
+def test_lora_dropped_scale_caught(monkeypatch):
+    from oracle import lora
+    from tests import test_oracle_lora as tl
+    monkeypatch.setattr(lora, "scale_f32", lambda s: np.float64(1.0))
+    _fails(tl.test_delta_equals_exact_rank_one_sum, 3, 5, 32, 2)
+
+
+def test_lora_up_projection_read_as_its_transpose_caught(monkeypatch):
+    from oracle import codec as oc
+    from oracle import lora
+    from tests import test_oracle_lora as tl
+
+    def bad(x_bits, a_bits, b_bits, scale):
+        t = lora.lora_down(x_bits, a_bits, scale)
+        bm = oc.bf16_to_f64(b_bits)
+        return t @ bm.reshape(bm.shape[1], bm.shape[0])  # B's storage taken as [r][N]
+    monkeypatch.setattr(lora, "lora_delta", bad)
+    _fails(tl.test_merged_weight_identity)
+
+
+def test_lora_down_projection_transposed_caught(monkeypatch):
+    from oracle import codec as oc
+    from oracle import lora
+    from tests import test_oracle_lora as tl
+
+    def bad(x_bits, a_bits, scale):
+        am = oc.bf16_to_f64(a_bits)
+        return lora.scale_f32(scale) * (oc.bf16_to_f64(x_bits) @ am.reshape(am.shape[1], am.shape[0]))
+    monkeypatch.setattr(lora, "lora_down", bad)
+    _fails(tl.test_merged_weight_identity)

@@ -24,6 +24,7 @@ STATUS = {0: "BSQ_OK", 1: "BSQ_ERR_NULL", 2: "BSQ_ERR_SHAPE", 3: "BSQ_ERR_ALIGN"
           5: "BSQ_ERR_DEVICE", 6: "BSQ_ERR_HIP", 7: "BSQ_ERR_ARG"}
 
 _p, _i64, _u32, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_int
+_f32 = ctypes.c_float
 
 # symbol -> (restype, argtypes); mirrors include/bsq.h
 SIGNATURES = {
@@ -43,6 +44,12 @@ SIGNATURES = {
     "bsq_gemm_nvfp4_quantize_y_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "bsq_gemm_nvfp4_q_quantize_y": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
                                            _p]),
+    "bsq_lora_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _u32]),
+    "bsq_gemm_fp8r_lora": (_int, [_p, _i64, _p, _p, _p, _p, _i64, _f32, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz,
+                                  _p]),
+    "bsq_gemm_nvfp4_lora": (_int, [_p, _i64, _p, _p, _p, _p, _p, _p, _i64, _f32, _p, _i64, _i64, _i64, _i64, _u32,
+                                   _p, _sz, _p]),
+    "bsq_lora_down": (_int, [_p, _i64, _p, _i64, _i64, _i64, _f32, _p, _p]),
 }
 
 
@@ -182,6 +189,73 @@ def bsq_gemm_nvfp4(x, w, w_bscale, w_scale2, input_scale=None, flags=0, y=None, 
     _check("bsq_gemm_nvfp4", lib.bsq_gemm_nvfp4(_ptr(x), ldx, _ptr(w), _ptr(w_bscale), _ptr(w_scale2),
                                                 _ptr(input_scale), _ptr(y), ldy, M, N, K, flags, _ptr(ws), nbytes,
                                                 _stream()))
+    return y
+
+
+def _adapter(lora_a, lora_b, N, K):
+    rank = lora_a.shape[0]
+    _dense(lora_a, torch.bfloat16, (rank, K), "lora_a")
+    _dense(lora_b, torch.bfloat16, (N, rank), "lora_b")
+    return rank
+
+
+def _lora_workspace(fmt, M, N, K, rank, flags, workspace, device):
+    nbytes = lib.bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags)
+    if workspace is None and nbytes:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    return workspace, (0 if workspace is None else workspace.numel())
+
+
+def bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags=0):
+    return lib.bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags)
+
+
+def bsq_lora_down(x, lora_a, lora_scale, t=None):
+    """bf16 x [M, K], bf16 lora_a [rank, K], float scale -> bf16 t = scale * x lora_a^T [M, rank]."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    rank = lora_a.shape[0]
+    _dense(lora_a, torch.bfloat16, (rank, K), "lora_a")
+    t = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device) if t is None else t
+    _dense(t, torch.bfloat16, (M, rank), "t")
+    _check("bsq_lora_down", lib.bsq_lora_down(_ptr(x), ldx, _ptr(lora_a), M, K, rank, float(lora_scale), _ptr(t),
+                                              _stream()))
+    return t
+
+
+def bsq_gemm_fp8r_lora(x, w, w_scale, lora_a, lora_b, lora_scale, flags=0, y=None, workspace=None):
+    """bsq_gemm_fp8r plus a LoRA: y = linear(x) + scale * (x lora_a^T) lora_b^T, with
+    lora_a [rank, K] and lora_b [N, rank] bf16."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N = w.shape[0]
+    _dense(w, torch.uint8, (N, K), "w")
+    _dense(w_scale, torch.float32, (N,), "w_scale")
+    rank = _adapter(lora_a, lora_b, N, K)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    ws, nbytes = _lora_workspace(BSQ_FMT_FP8R, M, N, K, rank, flags, workspace, x.device)
+    _check("bsq_gemm_fp8r_lora", lib.bsq_gemm_fp8r_lora(
+        _ptr(x), ldx, _ptr(w), _ptr(w_scale), _ptr(lora_a), _ptr(lora_b), rank, float(lora_scale), _ptr(y), ldy,
+        M, N, K, flags, _ptr(ws), nbytes, _stream()))
+    return y
+
+
+def bsq_gemm_nvfp4_lora(x, w, w_bscale, w_scale2, input_scale, lora_a, lora_b, lora_scale, flags=0, y=None,
+                        workspace=None):
+    """bsq_gemm_nvfp4 plus a LoRA: y = linear(x) + scale * (x lora_a^T) lora_b^T, with
+    lora_a [rank, K] and lora_b [N, rank] bf16 (input_scale None with BSQ_WEIGHT_ONLY)."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N = w.shape[0]
+    _dense(w, torch.uint8, (N, K // 2), "w")
+    _dense(w_bscale, torch.uint8, (N, K // 16), "w_bscale")
+    _scalar(w_scale2, "w_scale2")
+    _scalar(input_scale, "input_scale")
+    rank = _adapter(lora_a, lora_b, N, K)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    ws, nbytes = _lora_workspace(BSQ_FMT_NVFP4, M, N, K, rank, flags, workspace, x.device)
+    _check("bsq_gemm_nvfp4_lora", lib.bsq_gemm_nvfp4_lora(
+        _ptr(x), ldx, _ptr(w), _ptr(w_bscale), _ptr(w_scale2), _ptr(input_scale), _ptr(lora_a), _ptr(lora_b), rank,
+        float(lora_scale), _ptr(y), ldy, M, N, K, flags, _ptr(ws), nbytes, _stream()))
     return y
 
 

@@ -7,6 +7,7 @@
 #include "bsq.h"
 
 #include <atomic>
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -101,11 +102,30 @@ hipError_t launch_dec_or_skinny(bsq::DecMode mode, const bsq::DecArgs& a, hipStr
   return route_skinny(mode, a) ? bsq::launch_gemm_skinny(mode, a, s) : bsq::launch_gemm_dec(mode, a, s);
 }
 hipError_t launch_w8a8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw, uint16_t* y,
-                       int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                       int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s, const uint16_t* lt = nullptr,
+                       const uint16_t* lb = nullptr, int rank = 0) {
   bsq::DecArgs a{};
   a.xq = xq; a.sx = sx; a.w = w; a.sw = sw; a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
+  a.lt = lt; a.lb = lb; a.rank = rank;
   if (route_skinny(bsq::kW8A8, a)) return bsq::launch_gemm_skinny(bsq::kW8A8, a, s);
-  return bsq::launch_gemm_fp8(xq, sx, w, sw, y, ldy, M, N, K, s);
+  return bsq::launch_gemm_fp8(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+}
+
+// ---- low-rank adapter ----------------------------------------------------------------
+constexpr int64_t kMaxRank = 128;
+size_t ws_lora_t(int64_t M, int64_t rank) { return pad256((size_t)(M * rank * 2)); }
+
+// adapter rules on top of the linear's: rank, scale, pointers, and the 32-bit buffer offsets
+// of the down-projection (32 rows of x) and up-projection (T and B rows) kernels
+bsq_status check_lora(int64_t ldx, const uint16_t* a, const uint16_t* b, int64_t rank, float scale, int64_t M,
+                      int64_t N) {
+  if (rank < 1 || rank > kMaxRank) return BSQ_ERR_SHAPE;
+  if (ldx >= ((int64_t)1 << 24)) return BSQ_ERR_SHAPE;
+  if (M * rank >= ((int64_t)1 << 29) || N * rank >= ((int64_t)1 << 29)) return BSQ_ERR_SHAPE;
+  if (!std::isfinite(scale)) return BSQ_ERR_ARG;
+  if (!a || !b) return BSQ_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16)) return BSQ_ERR_ALIGN;
+  return BSQ_OK;
 }
 
 }  // namespace
@@ -320,6 +340,95 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscal
     a.y = ybuf; a.ldy = ldb; a.yq = nullptr; a.ys = nullptr; a.gy = nullptr;
     e = bsq::launch_gemm_dec(bsq::kW4A4, a, stream);
     if (e == hipSuccess) e = bsq::launch_quant_nvfp4(ybuf, M, N, ldb, y_scale, yq, y_bscale, stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+size_t bsq_lora_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, int64_t rank, uint32_t flags) {
+  if ((f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) || M <= 0 || K <= 0 || rank <= 0) return 0;
+  return bsq_gemm_workspace_bytes(f, M, N, K, flags) + ws_lora_t(M, rank);
+}
+
+bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64_t M, int64_t K,
+                         int64_t rank, float lora_scale, uint16_t* t, hipStream_t stream) {
+  bsq_status st = check_rows(M, K, ldx);
+  if (st != BSQ_OK) return st;
+  if (rank < 1 || rank > kMaxRank || ldx >= ((int64_t)1 << 24) || M * rank >= ((int64_t)1 << 29))
+    return BSQ_ERR_SHAPE;
+  if (!std::isfinite(lora_scale)) return BSQ_ERR_ARG;
+  if (M == 0) return BSQ_OK;
+  if (!x || !lora_a || !t) return BSQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(lora_a, 16) || !aligned(t, 16)) return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_gemm_fp8r_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* w_scale,
+                              const uint16_t* lora_a, const uint16_t* lora_b, int64_t rank, float lora_scale,
+                              uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bsq_status st = check_gemm_common(x, ldx, w, y, ldy, M, N, K, flags);
+  if (st != BSQ_OK) return st;
+  if ((st = check_lora(ldx, lora_a, lora_b, rank, lora_scale, M, N)) != BSQ_OK) return st;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!w_scale) return BSQ_ERR_NULL;
+  if (!aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bsq_lora_workspace_bytes(BSQ_FMT_FP8R, M, N, K, rank, flags))
+    return BSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  const bool weight_only = flags & BSQ_WEIGHT_ONLY;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* t = reinterpret_cast<uint16_t*>(ws + bsq_gemm_workspace_bytes(BSQ_FMT_FP8R, M, N, K, flags));
+  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, stream);
+  if (e == hipSuccess) {
+    if (weight_only) {
+      bsq::DecArgs a{};
+      a.x = x; a.ldx = ldx; a.w = w; a.sw = w_scale; a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
+      a.lt = t; a.lb = lora_b; a.rank = (int)rank;
+      e = launch_dec_or_skinny(bsq::kW8A16, a, stream);
+    } else {
+      float* sx = reinterpret_cast<float*>(ws + pad256((size_t)(M * K)));
+      e = bsq::launch_quant_fp8r(x, M, K, ldx, ws, sx, stream);
+      if (e == hipSuccess) e = launch_w8a8(ws, sx, w, w_scale, y, ldy, M, N, K, stream, t, lora_b, (int)rank);
+    }
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_gemm_nvfp4_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* w_bscale,
+                               const float* w_scale2, const float* input_scale, const uint16_t* lora_a,
+                               const uint16_t* lora_b, int64_t rank, float lora_scale, uint16_t* y, int64_t ldy,
+                               int64_t M, int64_t N, int64_t K, uint32_t flags, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  bsq_status st = check_gemm_common(x, ldx, w, y, ldy, M, N, K, flags);
+  if (st != BSQ_OK) return st;
+  if ((st = check_lora(ldx, lora_a, lora_b, rank, lora_scale, M, N)) != BSQ_OK) return st;
+  if (M == 0 || N == 0) return BSQ_OK;
+  const bool weight_only = flags & BSQ_WEIGHT_ONLY;
+  if (!w_bscale || !w_scale2 || (!weight_only && !input_scale)) return BSQ_ERR_NULL;
+  if (!aligned(w_bscale, 4) || !aligned(w_scale2, 4) || (input_scale && !aligned(input_scale, 4)))
+    return BSQ_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bsq_lora_workspace_bytes(BSQ_FMT_NVFP4, M, N, K, rank, flags))
+    return BSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* t = reinterpret_cast<uint16_t*>(ws + bsq_gemm_workspace_bytes(BSQ_FMT_NVFP4, M, N, K, flags));
+  bsq::DecArgs a{};
+  a.x = x; a.ldx = ldx; a.w = w; a.ws = w_bscale; a.gw = w_scale2; a.y = y; a.ldy = ldy;
+  a.M = M; a.N = N; a.K = K;
+  a.lt = t; a.lb = lora_b; a.rank = (int)rank;
+  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, stream);
+  if (e == hipSuccess) {
+    if (weight_only) {
+      e = launch_dec_or_skinny(bsq::kW4A16, a, stream);
+    } else {
+      a.xq = ws; a.xs = ws + pad256((size_t)(M * K / 2)); a.gx = input_scale;
+      e = bsq::launch_quant_nvfp4(x, M, K, ldx, input_scale, ws, const_cast<uint8_t*>(a.xs), stream);
+      if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
+    }
   }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }

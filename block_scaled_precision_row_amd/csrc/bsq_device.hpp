@@ -175,6 +175,22 @@ __device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t bytes) {
   return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, kBufferConfig};
 }
 
+// The same resource as the compiler's buffer-resource type, for the raw
+// buffer-load builtins (the compiler keeps it in scalar registers)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kBufOut = 0x40000000u;  // an offset past the records of every resource built here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferConfig);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 // LDS byte offset of a pointer into a __shared__ array
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)(p));

@@ -22,8 +22,13 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* sw, int64_t N, int
                                uint16_t* out, hipStream_t s);
 
 // W8A8: y = bf16((sum e4m3(xq) e4m3(w)) * sx[m] * sw[n])
+// (with lt != nullptr, plus the adapter term T B^T; see DecArgs)
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
-                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s);
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,
+                           const uint16_t* lb, int rank, hipStream_t s);
+// LoRA down projection: t [M][rank] = bf16(scale * X A^T), X bf16 [M][ldx], A bf16 [rank][K]
+hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+                            float scale, uint16_t* t, hipStream_t s);
 
 // Decode-to-16-bit GEMMs on the bf16 / f16 matrix cores.
 enum DecMode : int {
@@ -49,6 +54,11 @@ struct DecArgs {
   uint8_t* yq;         // optional nvfp4 copy of Y for the next linear: packed E2M1 [M][N/2] (W4A4)
   uint8_t* ys;         // its E4M3 block scales [M][N/16]
   const float* gy;     // its global scale (the next linear's input_scale)
+  // optional low-rank adapter: y += T B^T with T = s X A^T [M][rank] (bf16, scaled) and
+  // B [N][rank] (bf16); lt == nullptr means none
+  const uint16_t* lt;
+  const uint16_t* lb;
+  int rank;
 };
 hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
 // W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0

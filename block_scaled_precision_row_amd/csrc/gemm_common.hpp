@@ -186,6 +186,57 @@ __device__ __forceinline__ void quant_tile_rows(const uint8_t* tile, uint8_t* __
   }
 }
 
+// ---- low-rank adapter (LoRA) up-projection on the accumulators ---------------------------
+// An adapter adds T B^T to the layer's output, with T = s X A^T [M][rank] (bf16, the adapter's
+// scale already applied by the down-projection kernel) and B [N][rank] (bf16). The tiled GEMMs
+// run it after their K loop on their own accumulators, once those hold output units:
+// acc[i][j] += (B rows as the MFMA A operand, n) x (T rows as the B operand, m) over the rank,
+// 16 values per step on the bf16 matrix cores, in the accumulator layout of the main loop.
+// Rows past M or N and values past the rank read as zero.
+
+// values k8 .. k8 + 7 (k8 a multiple of 8) of row `row` of the bf16 [rows][rank] matrix behind r
+__device__ __forceinline__ v8bf lora_chunk(rsrc_t r, int row, int k8, int rank) {
+  union {
+    uint4 u;
+    v8bf h;
+  } c;
+  if ((rank & 7) == 0) {
+    c.u = bload16(r, k8 < rank ? (uint32_t)(row * rank + k8) * 2u : kBufOut);
+  } else {  // rows are not 16-byte aligned: two-byte loads
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k8 + 2 * e;
+      const uint32_t off = (uint32_t)(row * rank + k) * 2u;
+      const uint32_t lo = bload2(r, k < rank ? off : kBufOut), hi = bload2(r, k + 1 < rank ? off + 2u : kBufOut);
+      w[e] = (lo & 0xFFFFu) | (hi << 16);
+    }
+    c.u = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return c.h;
+}
+
+// acc[i][j] (n-tile i at n = nw0 + 32 i, m-tile j at m = mw0 + 32 j) += T[m][:] . B[n][:]
+template <int TN, int TM>
+__device__ __forceinline__ void lora_update(v16f (&acc)[TN][TM], const uint16_t* lt, const uint16_t* lb, int rank,
+                                            int M, int N, int nw0, int mw0, int lane) {
+  const rsrc_t rt = make_rsrc(lt, (uint32_t)M * (uint32_t)rank * 2u);
+  const rsrc_t rb = make_rsrc(lb, (uint32_t)N * (uint32_t)rank * 2u);
+  const int lr = lane & 31, lh = lane >> 5;
+  for (int k = 0; k < rank; k += 16) {
+    v8bf ua[TN], ub[TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) ua[i] = lora_chunk(rb, nw0 + 32 * i + lr, k + 8 * lh, rank);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) ub[j] = lora_chunk(rt, mw0 + 32 * j + lr, k + 8 * lh, rank);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[i], ub[j], acc[i][j], 0, 0, 0);
+  }
+}
+
 // tile index of this workgroup (XCD-contiguous, grouped along M)
 __device__ __forceinline__ void tile_of_block(int M, int N, int BM, int BN, int& m0, int& n0) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;

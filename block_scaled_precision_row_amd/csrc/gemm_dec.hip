@@ -26,8 +26,8 @@
 // Each thread stages whole rows: it loads the packed row segment (32 bytes
 // of E2M1 plus 4 block scales, 64 bytes of E4M3 or 128 bytes of bf16),
 // decodes it in registers and writes 8 swizzled 16-byte chunks.
-#include "bsq_device.hpp"
 #include "bsq_launch.hpp"
+#include "gemm_common.hpp"
 
 namespace bsq {
 
@@ -163,7 +163,7 @@ struct ModeTraits<kW8A16> {
   static constexpr bool F16 = false;
 };
 
-template <int MODE, int BM, int BN>
+template <int MODE, int BM, int BN, bool LORA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_dec_kernel(DecArgs a) {
   using T = ModeTraits<MODE>;
@@ -283,6 +283,27 @@ void gemm_dec_kernel(DecArgs a) {
   float alpha = 1.0f;
   if (MODE == kW4A4) alpha = a.gx[0] * a.gw[0];
   if (MODE == kW4A16) alpha = a.gw[0];
+  if constexpr (LORA) {
+    // with an adapter: y = bf16(acc * scale + T B^T), the adapter's MFMAs accumulating onto the
+    // scaled accumulators
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * lh;
+        float s[4] = {alpha, alpha, alpha, alpha};
+        if (MODE == kW8A16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[e] = (n + e < N) ? a.sw[n + e] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] *= s[e];
+      }
+    gemm::lora_update<TN, TM>(acc, a.lt, a.lb, a.rank, M, N, n0 + wn * WN, m0 + wm * WM, lane);
+    alpha = 1.0f;
+  }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int m = m0 + wm * WM + j * 32 + lr;
@@ -295,7 +316,7 @@ void gemm_dec_kernel(DecArgs a) {
         const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * lh;
         const v16f& A = acc[i][j];
         float s[4] = {alpha, alpha, alpha, alpha};
-        if (MODE == kW8A16) {
+        if (MODE == kW8A16 && !LORA) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[e] = (n + e < N) ? a.sw[n + e] : 0.0f;
         }
@@ -312,15 +333,20 @@ void gemm_dec_kernel(DecArgs a) {
   }
 }
 
-template <int MODE, int BM, int BN>
-hipError_t run(const DecArgs& a, hipStream_t s) {
+template <int MODE, int BM, int BN, bool LORA>
+hipError_t run_kernel(const DecArgs& a, hipStream_t s) {
   const size_t lds = 2 * (size_t)(BM + BN) * 128;
   static std::atomic<unsigned long long> lds_set{0};
-  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&gemm_dec_kernel<MODE, BM, BN>), (int)lds, lds_set);
+  hipError_t e =
+      ensure_lds_limit(reinterpret_cast<const void*>(&gemm_dec_kernel<MODE, BM, BN, LORA>), (int)lds, lds_set);
   if (e != hipSuccess) return e;
   const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_dec_kernel<MODE, BM, BN>), dim3(tiles), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemm_dec_kernel<MODE, BM, BN, LORA>), dim3(tiles), dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+template <int MODE, int BM, int BN>
+hipError_t run(const DecArgs& a, hipStream_t s) {
+  return a.lt ? run_kernel<MODE, BM, BN, true>(a, s) : run_kernel<MODE, BM, BN, false>(a, s);
 }
 
 template <int MODE>

@@ -81,11 +81,12 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, bool LORA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                      const uint8_t* __restrict__ w, const float* __restrict__ sw,
-                     uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K) {
+                     uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, const uint16_t* lt,
+                     const uint16_t* lb, int rank) {
   using C = Cfg<BM, BN, NS>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -157,19 +158,38 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   }
 
   // ---- epilogue: y = bf16(acc * sx[m] * sw[n]) via an LDS copy of the tile [BM][BN]
+  if constexpr (LORA) {
+    // with an adapter: y = bf16(acc * sx[m] * sw[n] + T B^T), the adapter's MFMAs accumulating
+    // onto the scaled accumulators
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const float xs = s_sx[wm * C::WM + j * 32 + lr];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 s4 = *reinterpret_cast<const float4*>(&s_sw[wn * C::WN + i * 32 + 8 * g + 4 * lh]);
+          acc[i][j][4 * g + 0] = acc[i][j][4 * g + 0] * xs * s4.x;
+          acc[i][j][4 * g + 1] = acc[i][j][4 * g + 1] * xs * s4.y;
+          acc[i][j][4 * g + 2] = acc[i][j][4 * g + 2] * xs * s4.z;
+          acc[i][j][4 * g + 3] = acc[i][j][4 * g + 3] * xs * s4.w;
+        }
+    }
+    lora_update<TN, TM>(acc, lt, lb, rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
+  }
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int ml = wm * C::WM + j * 32 + lr;
-    const float xs = s_sx[ml];
+    const float xs = LORA ? 1.0f : s_sx[ml];
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
         const v16f& A = acc[i][j];
-        const float4 s4 = *reinterpret_cast<const float4*>(&s_sw[nl]);
+        const float4 s4 = LORA ? make_float4(1.0f, 1.0f, 1.0f, 1.0f) : *reinterpret_cast<const float4*>(&s_sw[nl]);
         *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
             make_uint2(pack_bf16x2(A[4 * g + 0] * xs * s4.x, A[4 * g + 1] * xs * s4.y),
                        pack_bf16x2(A[4 * g + 2] * xs * s4.z, A[4 * g + 3] * xs * s4.w));
@@ -182,21 +202,27 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
 
 template <int BM, int BN, int NS>
 hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw, uint16_t* y,
-               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+               int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt, const uint16_t* lb, int rank,
+               hipStream_t s) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y, ldy,
-                     (int)M, (int)N, (int)K);
+  if (lt)
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, true>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
+                       ldy, (int)M, (int)N, (int)K, lt, lb, rank);
+  else
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
+                       ldy, (int)M, (int)N, (int)K, lt, lb, rank);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
-                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,
+                           const uint16_t* lb, int rank, hipStream_t s) {
   // pick the tile whose grid best fills the 256 compute units
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
-  if (t192 >= 192) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, s);
-  return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, s);
+  if (t192 >= 192) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
 }
 
 }  // namespace bsq

@@ -186,7 +186,18 @@ struct Scheme<kW8A16> {
 
 // sum the NW partial tiles (red = [NW][MB][16 registers][64 lanes]) in wave order, scale,
 // convert and store the tile
-template <int MODE, int MB, int NW>
+// low-rank adapter term of output (m, n): T[m][:] . B[n][:] over the rank, fp32 in rank order
+// (few tokens: a handful of outputs per thread, read straight from the caches)
+__device__ __forceinline__ float lora_dot(const DecArgs& a, int m, int n) {
+  const uint16_t* t = a.lt + (int64_t)m * a.rank;
+  const uint16_t* b = a.lb + (int64_t)n * a.rank;
+  float d = 0.0f;
+  for (int k = 0; k < a.rank; ++k)
+    d = fmaf(__uint_as_float((uint32_t)t[k] << 16), __uint_as_float((uint32_t)b[k] << 16), d);
+  return d;
+}
+
+template <int MODE, int MB, int NW, bool LORA>
 __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* red, int m0, int n0, int tid) {
   const int M = (int)a.M, N = (int)a.N;
   float alpha = 1.0f;
@@ -219,7 +230,12 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
       v[0] = v[0] * xs;
       v[1] = v[1] * xs;
     }
-    const uint32_t pk = pack_bf16x2(v[0] * s0, v[1] * s1);
+    float y0 = v[0] * s0, y1 = v[1] * s1;
+    if constexpr (LORA) {  // y = bf16(acc * scale + T B^T)
+      if (n < N) y0 += lora_dot(a, m, n);
+      if (n + 1 < N) y1 += lora_dot(a, m, n + 1);
+    }
+    const uint32_t pk = pack_bf16x2(y0, y1);
     uint16_t* yr = a.y + (int64_t)m * a.ldy;
     if (n + 1 < N) {
       *reinterpret_cast<uint32_t*>(yr + n) = pk;
@@ -245,7 +261,9 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
           float sum = 0.0f;
 #pragma unroll
           for (int w = 0; w < NW; ++w) sum += red[((w * MB + j) * 16 + r) * 64 + ln];
-          f[e] = bf16_lo(pack_bf16x2(sum * alpha, 0.0f));  // the value the bf16 output holds
+          float yv = sum * alpha;
+          if constexpr (LORA) yv += lora_dot(a, m, n + e);
+          f[e] = bf16_lo(pack_bf16x2(yv, 0.0f));  // the value the bf16 output holds
         }
         uint2 codes;
         const uint32_t sf = quant_block16_nvfp4(f, G, codes);
@@ -257,19 +275,7 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
 }
 
 // ---- direct operand loads (nvfp4 schemes) --------------------------------------------
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kSkOut = 0x40000000u;  // buffer offset past every tile's records
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferConfig);
-}
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
-  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
-}
+constexpr uint32_t kSkOut = kBufOut;  // buffer offset past every tile's records
 // K offset of a wave's i-th stage. Every workgroup reads the same activation rows; starting
 // the walk over K at a different stage per workgroup spreads those reads over the cache
 // channels instead of having all workgroups hit the same lines at once. Stages past the
@@ -355,7 +361,7 @@ __device__ __forceinline__ void read_bf16(OpBf& o, const uint8_t* codes, int lr,
   for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
 }
 
-template <int MODE, int MB>
+template <int MODE, int MB, bool LORA>
 __global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel(DecArgs a) {
   static_assert(MODE == kW4A4 || MODE == kW4A16, "nvfp4 weights only");
   using S = Scheme<MODE>;
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
   __syncthreads();
-  skinny_epilogue<MODE, MB, NW>(a, red, m0, n0, tid);
+  skinny_epilogue<MODE, MB, NW, LORA>(a, red, m0, n0, tid);
 }
 
 // ---- LDS-DMA variant (E4M3 weights): stage layout of one wave -----------------------
@@ -533,7 +539,7 @@ __device__ __forceinline__ void read_bf(OpBf& o, const uint8_t* codes, int lr, i
   for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
 }
 
-template <int MODE, int MB, int NW>
+template <int MODE, int MB, int NW, bool LORA>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   using S = Scheme<MODE>;
   using L = Layout<MODE>;
@@ -627,20 +633,27 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
     for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
   __syncthreads();
 
-  skinny_epilogue<MODE, MB, NW>(a, red, m0, n0, tid);
+  skinny_epilogue<MODE, MB, NW, LORA>(a, red, m0, n0, tid);
 }
 
 template <int MODE, int MB, int NW>
 hipError_t run(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = ((a.N + 31) / 32) * ((a.M + 32 * MB - 1) / (32 * MB));
-  hipLaunchKernelGGL((gemm_skinny_kernel<MODE, MB, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+  if (a.lt)
+    hipLaunchKernelGGL((gemm_skinny_kernel<MODE, MB, NW, true>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<MODE, MB, NW, false>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 template <int MODE, int MB>
 hipError_t run_staged(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = ((a.N + 31) / 32) * ((a.M + 32 * MB - 1) / (32 * MB));
-  hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB>), dim3((unsigned)blocks), dim3(64 * kSkStagedWaves), 0, s,
-                     a);
+  if (a.lt)
+    hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB, true>), dim3((unsigned)blocks),
+                       dim3(64 * kSkStagedWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB, false>), dim3((unsigned)blocks),
+                       dim3(64 * kSkStagedWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q) {
   return T == 0 ? q.x : T == 1 ? q.y : T == 2 ? q.z : q.w;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool LORA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_w4a4_kernel(DecArgs a) {
   using C = W4Cfg<BM, BN>;
@@ -257,7 +257,17 @@ void gemm_w4a4_kernel(DecArgs a) {
   if (s < nk) stage(s, s0a, s0b, s1a, s1b);
 
   // ---- epilogue: y = bf16(acc * gx * gw) via an LDS copy of the tile [BM][BN]
-  const float alpha = a.gx[0] * a.gw[0];
+  float alpha = a.gx[0] * a.gw[0];
+  if constexpr (LORA) {
+    // with an adapter: y = bf16(acc * gx * gw + T B^T), the adapter's MFMAs accumulating onto
+    // the scaled accumulators
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] *= alpha;
+    lora_update<TN, TM>(acc, a.lt, a.lb, a.rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
+    alpha = 1.0f;
+  }
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
 #pragma unroll
@@ -286,7 +296,10 @@ void gemm_w4a4_kernel(DecArgs a) {
 template <int BM, int BN>
 hipError_t run(const DecArgs& a, hipStream_t s) {
   const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN>), dim3(tiles), dim3(kThreads), 0, s, a);
+  if (a.lt)
+    hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, true>), dim3(tiles), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, false>), dim3(tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

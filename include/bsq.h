@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define BSQ_ABI_VERSION 2
+#define BSQ_ABI_VERSION 3
 
 typedef enum {
   BSQ_OK = 0,
@@ -195,6 +195,46 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscal
                                        const float* y_scale, uint8_t* yq, uint8_t* y_bscale, uint16_t* y,
                                        int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Low-rank adapter (LoRA) side path on the quantized linear. "FLUX 3 Image
+ * Klein vs Qwen-Image-2.1" (model overview) and the FLUX 3 Image Klein
+ * open-source release page (section three, speed figures): the quantized
+ * model can run with a LoRA attached, at about 5 % more generation time. The
+ * pages give no arithmetic; these entry points compute the standard adapter
+ *   y = linear(x) + s * (x A^T) B^T
+ * where linear(x) is exactly what bsq_gemm_fp8r / bsq_gemm_nvfp4 compute for
+ * the same arguments and flags, the adapter reads the unquantized bf16 x,
+ *   lora_a [rank][K] bf16 (down projection), lora_b [N][rank] bf16 (up
+ *   projection), 1 <= rank <= 128, lora_scale s a finite fp32 host value
+ *   (alpha / rank times the adapter's strength).
+ * Arithmetic: T = bf16(s * sum_k x[m][k] a[j][k]) (fp32 accumulation), then
+ *   y[m][n] = bf16( base_acc[m][n] * (the linear's scales) + sum_j T[m][j] b[n][j] )
+ * with the adapter sum accumulated in fp32 onto the scaled base accumulator,
+ * so the output is rounded once. T is the only other rounding.
+ * Workspace: bsq_lora_workspace_bytes(f, M, N, K, rank, flags) bytes,
+ * 256-byte aligned: the linear's workspace followed by T [M][rank].
+ * Extra shape rules: ldx < 2^24; M * rank and N * rank below 2^29.
+ * BSQ_ERR_ARG for a non-finite lora_scale; lora_a / lora_b 16-byte aligned.
+ */
+size_t bsq_lora_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, int64_t rank, uint32_t flags);
+bsq_status bsq_gemm_fp8r_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* w_scale,
+                              const uint16_t* lora_a, const uint16_t* lora_b, int64_t rank, float lora_scale,
+                              uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+bsq_status bsq_gemm_nvfp4_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* w_bscale,
+                               const float* w_scale2, const float* input_scale, const uint16_t* lora_a,
+                               const uint16_t* lora_b, int64_t rank, float lora_scale, uint16_t* y, int64_t ldy,
+                               int64_t M, int64_t N, int64_t K, uint32_t flags, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+/*
+ * The adapter's down projection alone, as the entry points above compute it:
+ *   t[m][j] = bf16( s * sum_k x[m][k] a[j][k] ),  t [M][rank] bf16 (16-byte aligned)
+ * x [M][ldx] bf16 (rules as for the quantizers, plus ldx < 2^24), lora_a and
+ * rank as above.
+ */
+bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64_t M, int64_t K,
+                         int64_t rank, float lora_scale, uint16_t* t, hipStream_t stream);
 
 /*
  * Fallback dequantization to bf16 ("BFL (fp8r / nvfp4)", last paragraph of

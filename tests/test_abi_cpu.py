@@ -33,12 +33,12 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 15
+    assert len(syms) == 19
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
         assert s in _lib.SIGNATURES, s
-    assert L.bsq_abi_version() == 2
+    assert L.bsq_abi_version() == 3
     assert L.bsq_status_string(SHAPE).decode().startswith("invalid shape")
 
 
@@ -107,6 +107,43 @@ def test_quantize_y_validation():
     assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(4096, 1024, 512, 0) == 0
     assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(16, 1024, 96, 0) == 0
     assert q(A, B, C, A, B, C, D, A, B, None, 0, 4096, 1024, 96, None, 0, None) == WS
+
+
+def test_lora_validation():
+    pad = lambda n: (n + 255) // 256 * 256
+    fp8, nv, wo = _lib.BSQ_FMT_FP8R, _lib.BSQ_FMT_NVFP4, _lib.BSQ_WEIGHT_ONLY
+    wsb = L.bsq_lora_workspace_bytes
+    assert wsb(fp8, 4096, 3072, 3072, 32, 0) == L.bsq_gemm_workspace_bytes(fp8, 4096, 3072, 3072, 0) + pad(4096 * 64)
+    assert wsb(nv, 4096, 12288, 3072, 16, wo) == pad(4096 * 32)
+    assert wsb(nv, 0, 12288, 3072, 16, 0) == 0 and wsb(3, 64, 64, 64, 16, 0) == 0
+    g = L.bsq_gemm_fp8r_lora
+    ws = wsb(fp8, 64, 64, 64, 16, 0)
+    # x, ldx, w, w_scale, a, b, rank, scale, y, ldy, M, N, K, flags, ws, ws_bytes, stream
+    assert g(A, 64, B, C, A, B, 16, 1.0, D, 64, 64, 64, 64, 0, A, ws - 1, None) == WS
+    assert g(A, 64, B, C, A, B, 0, 1.0, D, 64, 64, 64, 64, 0, A, ws, None) == SHAPE       # rank 0
+    assert g(A, 64, B, C, A, B, 129, 1.0, D, 64, 64, 64, 64, 0, A, 1 << 24, None) == SHAPE  # rank > 128
+    assert g(A, 64, B, C, A, B, 16, float("nan"), D, 64, 64, 64, 64, 0, A, ws, None) == ARG
+    assert g(A, 64, B, C, A, B, 16, float("inf"), D, 64, 64, 64, 64, 0, A, ws, None) == ARG
+    assert g(A, 64, B, C, None, B, 16, 1.0, D, 64, 64, 64, 64, 0, A, ws, None) == NULL
+    assert g(A, 64, B, C, A, ODD, 16, 1.0, D, 64, 64, 64, 64, 0, A, ws, None) == ALIGN
+    assert g(A, 1 << 24, B, C, A, B, 16, 1.0, D, 64, 4, 64, 64, 0, A, 1 << 30, None) == SHAPE  # ldx
+    assert g(A, 64, B, C, A, B, 128, 1.0, D, 1 << 22, 1 << 22, 64, 64, 0, A, 1 << 40, None) == SHAPE  # M * rank
+    assert g(None, 64, None, None, A, B, 16, 1.0, None, 64, 0, 64, 64, 0, None, 0, None) == OK  # empty
+    n = L.bsq_gemm_nvfp4_lora
+    ws = wsb(nv, 64, 64, 64, 16, 0)
+    # x, ldx, w, w_bscale, w_scale2, input_scale, a, b, rank, scale, y, ldy, M, N, K, flags, ws, ws_bytes, stream
+    assert n(A, 64, B, C, D, None, A, B, 16, 1.0, D, 64, 64, 64, 64, 0, A, ws, None) == NULL     # input_scale
+    assert n(A, 64, B, C, D, D, A, B, 16, 1.0, D, 64, 64, 64, 64, 0, A, ws - 1, None) == WS
+    assert n(A, 64, B, C, D, None, A, B, 16, 1.0, D, 64, 64, 64, 64, wo, None, 0, None) == WS    # T needs room
+    assert n(A, 64, B, C, D, D, A, B, 16, 1.0, D, 64, 64, 64, 64, 8, A, ws, None) == ARG
+    d = L.bsq_lora_down
+    # x, ldx, a, M, K, rank, scale, t, stream
+    assert d(A, 64, B, 4, 64, 0, 1.0, C, None) == SHAPE
+    assert d(A, 64, B, 4, 48, 16, 1.0, C, None) == SHAPE                 # K % 32
+    assert d(A, 64, B, 4, 64, 16, float("nan"), C, None) == ARG
+    assert d(A, 64, None, 4, 64, 16, 1.0, C, None) == NULL
+    assert d(A, 64, B, 4, 64, 16, 1.0, ODD, None) == ALIGN
+    assert d(None, 64, None, 0, 64, 16, 1.0, None, None) == OK
 
 
 def test_dequant_validation():

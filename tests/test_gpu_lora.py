@@ -1,0 +1,178 @@
+"""GPU parity of the LoRA side path: y = linear(x) + s (x A^T) B^T on every GEMM route.
+
+The oracle's output is the fp64 base product (as in test_gpu_gemm.py) plus the
+adapter's exact fp64 contribution. The GPU rounds the output once, as the
+GEMMs do, and also holds the rank-r intermediate T in bf16; the comparison is
+the GEMM tolerance plus that rounding's elementwise bound (the adapter term is
+10-30 % of the output here, so a dropped scale, term or transpose fails it).
+With a zero scale the LoRA entry points must reproduce the plain entry points
+bit for bit on every route. Shapes are picked to reach every kernel: few-token
+(skinny) kernels, the 128 x 128 and 256 x 256 / 256 x 192 tiled kernels, the
+decode-GEMM fallback (K % 256 != 0), ragged M / N tails, and ranks that are
+not multiples of 8 or 16.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_row_amd import synthetic as syn
+from oracle import codec, gemm, lora, quant
+from tests.gpu_util import assert_gemm_close, dev, dev_bf16, dev_scalar, host
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from block_scaled_precision_row_amd import _lib as L
+
+SCALE = 0.75  # not 1, so that an ignored scale shows
+
+
+def _rows_subset(M, n, seed):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, n - 2, replace=False)]))
+
+
+def _inputs(M, N, K, rank, wid):
+    x = syn.normal_bf16((M, K), 60, M + 7 * K)
+    w = syn.normal_bf16((N, K), 60, 5000 + N + K, sigma=0.02)
+    a, b = syn.lora_adapter(60, rank, N, K, block=wid)
+    return x, w, a, b
+
+
+def run_lora(scheme, weight_only, x, w, a, b, scale, sample=None, what=""):
+    M, K = x.shape
+    flags = L.BSQ_WEIGHT_ONLY if weight_only else 0
+    rows = _rows_subset(M, sample, M + 3) if sample else np.arange(M)
+    da, db = dev_bf16(a), dev_bf16(b)
+    if scheme == "fp8r":
+        wq, sw = quant.quantize_fp8r(w)
+        y = L.bsq_gemm_fp8r_lora(dev_bf16(x), dev(wq), dev(sw), da, db, scale, flags=flags)
+        torch.cuda.synchronize()
+        if weight_only:
+            base = gemm.gemm_fp8r_weight_only(x[rows], wq, sw)
+        else:
+            xq, sx = quant.quantize_fp8r(x[rows])
+            base = gemm.gemm_fp8r(xq, sx, wq, sw)
+    else:
+        gw = quant.calibrate_global_scale(w)
+        wq, sfw = quant.quantize_nvfp4(w, gw)
+        gx = quant.calibrate_global_scale(x)
+        y = L.bsq_gemm_nvfp4_lora(dev_bf16(x), dev(wq), dev(sfw), dev_scalar(gw),
+                                  None if weight_only else dev_scalar(gx), da, db, scale, flags=flags)
+        torch.cuda.synchronize()
+        if weight_only:
+            base = gemm.gemm_nvfp4_weight_only(x[rows], wq, sfw, gw)
+        else:
+            xq, sfx = quant.quantize_nvfp4(x[rows], gx)
+            base = gemm.gemm_nvfp4(xq, sfx, gx, wq, sfw, gw)
+    ref = lora.lora_linear(base, x[rows], a, b, scale)
+    delta = ref - base
+    share = np.linalg.norm(delta) / max(np.linalg.norm(ref), 1e-300)
+    assert_gemm_close(host(y)[rows], ref, "%s adapter share %.2f" % (what, share),
+                      extra=t_rounding_bound(x[rows], a, b, scale))
+    return y
+
+
+def t_rounding_bound(x, a, b, scale):
+    """Elementwise bound of what holding T = s X A^T in bf16 changes in T B^T: each T value
+    moves by at most 2^-9 of itself (round to nearest), plus fp32 accumulation slack, so the
+    product moves by at most 2^-9 sum_j |T[m][j]| |B[n][j]|; twice that is allowed."""
+    t = np.abs(lora.lora_down(x, a, scale))
+    return 2.0 ** -8 * (t @ np.abs(codec.bf16_to_f64(b)).T)
+
+
+SCHEMES = [("fp8r", False), ("fp8r", True), ("nvfp4", False), ("nvfp4", True)]
+
+# (M, N, K, rank)
+ROUTE_SHAPES = [
+    (1, 64, 256, 5),        # few-token kernels, odd rank (two-byte adapter loads)
+    (20, 1024, 512, 32),    # few-token kernels
+    (100, 300, 96, 8),      # few-token kernels of all schemes, K below one stage
+    (300, 512, 512, 16),    # 128 x 128 tiled W4A4 and fp8, decode GEMM for the weight-only schemes
+    (300, 520, 96, 24),     # decode GEMM for W4A4 (K % 256 != 0), ragged N, rank % 16 != 0
+    (257, 300, 544, 128),   # largest rank, ragged everything
+    (130, 200, 160, 48),    # decode GEMM W4A4, few-token fp8
+]
+
+
+@pytest.mark.parametrize("M,N,K,rank", ROUTE_SHAPES)
+@pytest.mark.parametrize("scheme,weight_only", SCHEMES)
+def test_lora_matches_oracle(scheme, weight_only, M, N, K, rank):
+    x, w, a, b = _inputs(M, N, K, rank, rank)
+    run_lora(scheme, weight_only, x, w, a, b, SCALE,
+             what="%s%s %dx%dx%d r%d" % (scheme, "-wo" if weight_only else "", M, N, K, rank))
+
+
+# 256 x 256 W4A4 and decode tiles, 256 x 192 fp8 tiles: compared on sampled rows
+BIG_SHAPES = [(4096, 3072, 3072, 32), (4096, 4096, 512, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,rank", BIG_SHAPES)
+@pytest.mark.parametrize("scheme,weight_only", SCHEMES)
+def test_lora_large_tiles_sampled(scheme, weight_only, M, N, K, rank):
+    x, w, a, b = _inputs(M, N, K, rank, 1)
+    run_lora(scheme, weight_only, x, w, a, b, 1.0, sample=64,
+             what="%s%s %dx%dx%d r%d" % (scheme, "-wo" if weight_only else "", M, N, K, rank))
+
+
+@pytest.mark.parametrize("M,N,K,rank", ROUTE_SHAPES + [(4096, 3072, 3072, 32)])
+@pytest.mark.parametrize("scheme,weight_only", SCHEMES)
+def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K, rank):
+    x, w, a, b = _inputs(M, N, K, rank, 2)
+    flags = L.BSQ_WEIGHT_ONLY if weight_only else 0
+    dx, da, db = dev_bf16(x), dev_bf16(a), dev_bf16(b)
+    if scheme == "fp8r":
+        wq, sw = quant.quantize_fp8r(w)
+        plain = L.bsq_gemm_fp8r(dx, dev(wq), dev(sw), flags=flags)
+        with_lora = L.bsq_gemm_fp8r_lora(dx, dev(wq), dev(sw), da, db, 0.0, flags=flags)
+    else:
+        gw = quant.calibrate_global_scale(w)
+        wq, sfw = quant.quantize_nvfp4(w, gw)
+        gx = None if weight_only else dev_scalar(quant.calibrate_global_scale(x))
+        plain = L.bsq_gemm_nvfp4(dx, dev(wq), dev(sfw), dev_scalar(gw), gx, flags=flags)
+        with_lora = L.bsq_gemm_nvfp4_lora(dx, dev(wq), dev(sfw), dev_scalar(gw), gx, da, db, 0.0, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(with_lora), host(plain))
+
+
+DOWN_SHAPES = [(1, 32, 1), (17, 96, 4), (64, 256, 48), (40, 512, 64), (33, 128, 128), (300, 3072, 32),
+               (4096, 3072, 32), (77, 12288, 16)]
+
+
+@pytest.mark.parametrize("M,K,rank", DOWN_SHAPES)
+def test_down_projection(M, K, rank):
+    """T = bf16(s X A^T) within bf16 rounding (2^-9) plus fp32 accumulation of the exact value."""
+    x = syn.normal_bf16((M, K), 61, M + K)
+    a, _ = syn.lora_adapter(61, rank, 8, K, block=rank)
+    t = host(L.bsq_lora_down(dev_bf16(x), dev_bf16(a), SCALE))
+    torch.cuda.synchronize()
+    ref = lora.lora_down(x, a, SCALE)
+    got = codec.bf16_to_f64(t)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms)
+
+
+def test_down_projection_strided_input_and_determinism():
+    M, K, ldx, rank = 70, 256, 320, 24
+    xf = syn.normal_bf16((M, ldx), 62, 1)
+    a, _ = syn.lora_adapter(62, rank, 8, K)
+    xs = dev_bf16(xf)[:, :K]
+    t1 = host(L.bsq_lora_down(xs, dev_bf16(a), 2.0))
+    t2 = host(L.bsq_lora_down(xs, dev_bf16(a), 2.0))
+    torch.cuda.synchronize()
+    assert np.array_equal(t1, t2)
+    ref = lora.lora_down(np.ascontiguousarray(xf[:, :K]), a, 2.0)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(np.abs(codec.bf16_to_f64(t1) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms)
+
+
+def test_empty_batch_is_a_noop():
+    w = torch.zeros((64, 64), dtype=torch.uint8, device="cuda")
+    s = torch.ones((64,), dtype=torch.float32, device="cuda")
+    a = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((64, 8), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    y = L.bsq_gemm_fp8r_lora(x, w, s, a, b, 1.0)
+    assert y.shape == (0, 64)

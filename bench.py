@@ -130,6 +130,70 @@ def quantized_output_comparison(L, dev, y3, gemm_args, operands):
     return out
 
 
+def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
+    """LoRA side path: each linear from bf16 X (activation quantization + GEMM) without and with a
+    synthetic adapter of several ranks (down projection + GEMM with the up projection in its
+    epilogue), warm, `reps` back-to-back calls each, in us; plus the down projection alone and
+    its HBM rate (X read once, A read, T written). Also a 16-token nvfp4 linear."""
+    import torch
+
+    lib = L.lib
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def up_bf16(bits):
+        return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
+
+    def timed(fn, a):
+        st = fn(*a)
+        if st != 0:
+            raise L.BsqError(fn.__name__, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {}
+    layers = [("nvfp4", "nvfp4_4096x12288x3072", x3, M, N_FP4), ("fp8r", "fp8r_4096x3072x3072", x2, M, N_FP8),
+              ("nvfp4", "nvfp4_16x12288x3072", x3[:16], 16, N_FP4)]
+    for scheme, name, x, Mx, N in layers:
+        fmt = L.BSQ_FMT_NVFP4 if scheme == "nvfp4" else L.BSQ_FMT_FP8R
+        y = torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((lib.bsq_lora_workspace_bytes(fmt, Mx, N, K, 128, 0),), dtype=torch.uint8, device=dev)
+        if scheme == "nvfp4":
+            plain = (lib.bsq_gemm_nvfp4, (P(x), K, P(w3q), P(w3s), P(g3), P(gx3), P(y), N, Mx, N, K, 0, P(ws),
+                                          ws.numel(), stream))
+        else:
+            plain = (lib.bsq_gemm_fp8r, (P(x), K, P(w2q), P(w2s), P(y), N, Mx, N, K, 0, P(ws), ws.numel(), stream))
+        entry = {"plain_us": round(timed(*plain), 2), "ranks": {}}
+        for rank in (16, 32, 64, 128):
+            a, b = syn.lora_adapter(syn.NVFP4_UP if scheme == "nvfp4" else syn.FP8R_4096, rank, N, K)
+            da, db = up_bf16(a), up_bf16(b)
+            if scheme == "nvfp4":
+                call = (lib.bsq_gemm_nvfp4_lora, (P(x), K, P(w3q), P(w3s), P(g3), P(gx3), P(da), P(db), rank, 1.0,
+                                                  P(y), N, Mx, N, K, 0, P(ws), ws.numel(), stream))
+            else:
+                call = (lib.bsq_gemm_fp8r_lora, (P(x), K, P(w2q), P(w2s), P(da), P(db), rank, 1.0, P(y), N, Mx, N,
+                                                 K, 0, P(ws), ws.numel(), stream))
+            us = timed(*call)
+            t = torch.empty((Mx, rank), dtype=torch.bfloat16, device=dev)
+            dws = torch.empty((max(1, lib.bsq_lora_down_workspace_bytes(Mx, K, rank)),), dtype=torch.uint8,
+                              device=dev)
+            down_us = timed(lib.bsq_lora_down, (P(x), K, P(da), Mx, K, rank, 1.0, P(t), P(dws), dws.numel(), stream))
+            down_bytes = Mx * K * 2 + rank * K * 2 + Mx * rank * 2
+            entry["ranks"][str(rank)] = {
+                "us": round(us, 2), "overhead_pct": round(100.0 * (us / entry["plain_us"] - 1.0), 2),
+                "down_us": round(down_us, 2), "down_gbs": round(down_bytes / (down_us * 1e-6) / 1e9, 1)}
+        out[name] = entry
+    out["note"] = ("whole linear from bf16 X in both columns (activation quantizer + GEMM; with the adapter also "
+                   "its down projection), synthetic adapter with scale 1; the pages report about 5 % more "
+                   "generation time with a LoRA attached (whole model, other hardware)")
+    return out
+
+
 def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)):
     """Few-token GEMMs (K = 3072), all four schemes, with cold weights.
 
@@ -302,11 +366,12 @@ def main():
     ap.add_argument("--no-small-m", action="store_true", help="skip the few-token sweep")
     ap.add_argument("--no-joint", action="store_true", help="skip the 16384-token joint-block shapes")
     ap.add_argument("--no-quant-out", action="store_true", help="skip the quantized-output comparison")
+    ap.add_argument("--no-lora", action="store_true", help="skip the LoRA side-path measurement")
     ap.add_argument("--only-step", action="store_true",
                     help="time the step only (no CPU baseline, no extra measurements), e.g. under a profiler")
     args = ap.parse_args()
     if args.only_step:
-        args.no_cpu_baseline = args.no_small_m = args.no_joint = args.no_quant_out = True
+        args.no_cpu_baseline = args.no_small_m = args.no_joint = args.no_quant_out = args.no_lora = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (requested %d)" % args.gpus,
               file=sys.stderr)
@@ -463,6 +528,9 @@ def main():
         log("quantized-output comparison")
         result["w4a4_quantized_output_us"] = quantized_output_comparison(
             L, dev, y3, seq[DOM][1], (x3q, x3s, gx3, w3q, w3s, g3))
+    if not args.no_lora:
+        log("LoRA side path")
+        result["lora"] = lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3)
     if not args.no_small_m:
         log("few-token sweep")
         result["small_m"] = small_m_sweep(L, syn, dev)

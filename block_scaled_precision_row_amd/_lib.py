@@ -49,7 +49,8 @@ SIGNATURES = {
                                   _p]),
     "bsq_gemm_nvfp4_lora": (_int, [_p, _i64, _p, _p, _p, _p, _p, _p, _i64, _f32, _p, _i64, _i64, _i64, _i64, _u32,
                                    _p, _sz, _p]),
-    "bsq_lora_down": (_int, [_p, _i64, _p, _i64, _i64, _i64, _f32, _p, _p]),
+    "bsq_lora_down_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bsq_lora_down": (_int, [_p, _i64, _p, _i64, _i64, _i64, _f32, _p, _p, _sz, _p]),
 }
 
 
@@ -210,14 +211,18 @@ def bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags=0):
     return lib.bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags)
 
 
-def bsq_lora_down(x, lora_a, lora_scale, t=None):
+def bsq_lora_down(x, lora_a, lora_scale, t=None, workspace=None):
     """bf16 x [M, K], bf16 lora_a [rank, K], float scale -> bf16 t = scale * x lora_a^T [M, rank]."""
     M, K, ldx = _rows(x, torch.bfloat16, "x")
     rank = lora_a.shape[0]
     _dense(lora_a, torch.bfloat16, (rank, K), "lora_a")
     t = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device) if t is None else t
     _dense(t, torch.bfloat16, (M, rank), "t")
+    nbytes = lib.bsq_lora_down_workspace_bytes(M, K, rank)
+    if workspace is None and nbytes:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
     _check("bsq_lora_down", lib.bsq_lora_down(_ptr(x), ldx, _ptr(lora_a), M, K, rank, float(lora_scale), _ptr(t),
+                                              _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                               _stream()))
     return t
 

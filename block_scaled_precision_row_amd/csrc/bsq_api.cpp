@@ -113,7 +113,14 @@ hipError_t launch_w8a8(const uint8_t* xq, const float* sx, const uint8_t* w, con
 
 // ---- low-rank adapter ----------------------------------------------------------------
 constexpr int64_t kMaxRank = 128;
-size_t ws_lora_t(int64_t M, int64_t rank) { return pad256((size_t)(M * rank * 2)); }
+// the down projection's output T [M][rank] bf16, then its fp32 partial products when K is sliced
+size_t ws_lora_down(int64_t M, int64_t K, int64_t rank) {
+  const int slices = bsq::lora_down_slices(M, K, (int)rank);
+  return pad256((size_t)(M * rank * 2)) + (slices > 1 ? pad256((size_t)slices * (size_t)(M * rank * 4)) : 0);
+}
+float* lora_part(void* ws, int64_t M, int64_t rank) {
+  return reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pad256((size_t)(M * rank * 2)));
+}
 
 // adapter rules on top of the linear's: rank, scale, pointers, and the 32-bit buffer offsets
 // of the down-projection (32 rows of x) and up-projection (T and B rows) kernels
@@ -346,11 +353,18 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscal
 
 size_t bsq_lora_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, int64_t rank, uint32_t flags) {
   if ((f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) || M <= 0 || K <= 0 || rank <= 0) return 0;
-  return bsq_gemm_workspace_bytes(f, M, N, K, flags) + ws_lora_t(M, rank);
+  return bsq_gemm_workspace_bytes(f, M, N, K, flags) + ws_lora_down(M, K, rank);
+}
+
+size_t bsq_lora_down_workspace_bytes(int64_t M, int64_t K, int64_t rank) {
+  if (M <= 0 || K <= 0 || rank <= 0) return 0;
+  const int slices = bsq::lora_down_slices(M, K, (int)rank);
+  return slices > 1 ? pad256((size_t)slices * (size_t)(M * rank * 4)) : 0;
 }
 
 bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64_t M, int64_t K,
-                         int64_t rank, float lora_scale, uint16_t* t, hipStream_t stream) {
+                         int64_t rank, float lora_scale, uint16_t* t, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
   bsq_status st = check_rows(M, K, ldx);
   if (st != BSQ_OK) return st;
   if (rank < 1 || rank > kMaxRank || ldx >= ((int64_t)1 << 24) || M * rank >= ((int64_t)1 << 29))
@@ -359,8 +373,12 @@ bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a,
   if (M == 0) return BSQ_OK;
   if (!x || !lora_a || !t) return BSQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(lora_a, 16) || !aligned(t, 16)) return BSQ_ERR_ALIGN;
+  const size_t need = bsq_lora_down_workspace_bytes(M, K, rank);
+  if (need && (!workspace || workspace_bytes < need)) return BSQ_ERR_WORKSPACE;
+  if (need && !aligned(workspace, 16)) return BSQ_ERR_ALIGN;
   if ((st = check_device()) != BSQ_OK) return st;
-  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, stream);
+  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr,
+                                       static_cast<float*>(workspace), t, stream);
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
@@ -381,7 +399,8 @@ bsq_status bsq_gemm_fp8r_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, 
   const bool weight_only = flags & BSQ_WEIGHT_ONLY;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* t = reinterpret_cast<uint16_t*>(ws + bsq_gemm_workspace_bytes(BSQ_FMT_FP8R, M, N, K, flags));
-  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, stream);
+  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr,
+                                       lora_part(t, M, rank), t, stream);
   if (e == hipSuccess) {
     if (weight_only) {
       bsq::DecArgs a{};
@@ -420,15 +439,20 @@ bsq_status bsq_gemm_nvfp4_lora(const uint16_t* x, int64_t ldx, const uint8_t* w,
   a.x = x; a.ldx = ldx; a.w = w; a.ws = w_bscale; a.gw = w_scale2; a.y = y; a.ldy = ldy;
   a.M = M; a.N = N; a.K = K;
   a.lt = t; a.lb = lora_b; a.rank = (int)rank;
-  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, stream);
-  if (e == hipSuccess) {
-    if (weight_only) {
-      e = launch_dec_or_skinny(bsq::kW4A16, a, stream);
-    } else {
-      a.xq = ws; a.xs = ws + pad256((size_t)(M * K / 2)); a.gx = input_scale;
-      e = bsq::launch_quant_nvfp4(x, M, K, ldx, input_scale, ws, const_cast<uint8_t*>(a.xs), stream);
-      if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
-    }
+  // the tiled W4A4 kernel adds the adapter before its K loop and takes T / (gx gw)
+  const bool pre = !weight_only && !route_skinny(bsq::kW4A4, a) && bsq::lora_pre_scaled_w4a4(a);
+  hipError_t e;
+  if (weight_only) {
+    e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr, lora_part(t, M, rank), t,
+                              stream);
+    if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A16, a, stream);
+  } else {
+    // one pass over X: the down projection also writes X's nvfp4 encoding for the GEMM
+    uint8_t* xs = ws + pad256((size_t)(M * K / 2));
+    a.xq = ws; a.xs = xs; a.gx = input_scale;
+    e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, pre ? input_scale : nullptr,
+                              pre ? w_scale2 : nullptr, lora_part(t, M, rank), t, stream, input_scale, ws, xs);
+    if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
   }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }

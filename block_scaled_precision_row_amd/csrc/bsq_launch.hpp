@@ -26,9 +26,16 @@ hipError_t launch_dequant_fp8r(const uint8_t* w, const float* sw, int64_t N, int
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                            uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,
                            const uint16_t* lb, int rank, hipStream_t s);
-// LoRA down projection: t [M][rank] = bf16(scale * X A^T), X bf16 [M][ldx], A bf16 [rank][K]
+// LoRA down projection: t [M][rank] = bf16(f * X A^T), X bf16 [M][ldx], A bf16 [rank][K], with
+// f = scale, or scale / (*ga * *gb) when ga != nullptr (T for a GEMM that scales its
+// accumulators by *ga * *gb). K is cut into lora_down_slices(M, K, rank) slices; with more than
+// one, `part` holds their fp32 partial products [slices][M][rank]. With xq != nullptr the same
+// kernel also writes X's nvfp4 encoding with global scale *gq (as launch_quant_nvfp4 does).
+int lora_down_slices(int64_t M, int64_t K, int rank);
+int64_t lora_down_slice_k(int64_t K, int slices);
 hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
-                            float scale, uint16_t* t, hipStream_t s);
+                            float scale, const float* ga, const float* gb, float* part, uint16_t* t, hipStream_t s,
+                            const float* gq = nullptr, uint8_t* xq = nullptr, uint8_t* xs = nullptr);
 
 // Decode-to-16-bit GEMMs on the bf16 / f16 matrix cores.
 enum DecMode : int {
@@ -55,11 +62,14 @@ struct DecArgs {
   uint8_t* ys;         // its E4M3 block scales [M][N/16]
   const float* gy;     // its global scale (the next linear's input_scale)
   // optional low-rank adapter: y += T B^T with T = s X A^T [M][rank] (bf16, scaled) and
-  // B [N][rank] (bf16); lt == nullptr means none
+  // B [N][rank] (bf16); lt == nullptr means none. The tiled W4A4 kernel instead takes
+  // T / (gx gw) and adds T B^T to its accumulators before the K loop.
   const uint16_t* lt;
   const uint16_t* lb;
   int rank;
 };
+// whether the adapter's T must be divided by gx * gw for this W4A4 launch (tiled kernel)
+bool lora_pre_scaled_w4a4(const DecArgs& a);
 hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
 // W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0
 bool gemm_w4a4_supported(const DecArgs& a);

@@ -216,6 +216,35 @@ __device__ __forceinline__ v8bf lora_chunk(rsrc_t r, int row, int k8, int rank) 
   return c.h;
 }
 
+// S rank steps of 16 of this lane's adapter operands (B rows for the MFMA A operand, T rows for B)
+template <int TN, int TM, int S>
+struct LoraRegs {
+  v8bf b[S][TN];
+  v8bf t[S][TM];
+};
+template <int TN, int TM, int S>
+__device__ __forceinline__ void lora_load(LoraRegs<TN, TM, S>& r, rsrc_t rt, rsrc_t rb, int k0, int rank, int nw0,
+                                          int mw0, int lane) {
+  const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) r.b[s][i] = lora_chunk(rb, nw0 + 32 * i + lr, k0 + 16 * s + 8 * lh, rank);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) r.t[s][j] = lora_chunk(rt, mw0 + 32 * j + lr, k0 + 16 * s + 8 * lh, rank);
+  }
+}
+template <int TN, int TM, int S>
+__device__ __forceinline__ void lora_mfma(v16f (&acc)[TN][TM], const LoraRegs<TN, TM, S>& r) {
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.b[s][i], r.t[s][j], acc[i][j], 0, 0, 0);
+}
+
 // acc[i][j] (n-tile i at n = nw0 + 32 i, m-tile j at m = mw0 + 32 j) += T[m][:] . B[n][:]
 template <int TN, int TM>
 __device__ __forceinline__ void lora_update(v16f (&acc)[TN][TM], const uint16_t* lt, const uint16_t* lb, int rank,

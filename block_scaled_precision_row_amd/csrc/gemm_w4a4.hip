@@ -224,8 +224,26 @@ void gemm_w4a4_kernel(DecArgs a) {
     pipeline(NV{}, I0{});
   };
 
-  issue_stage(0);
-  wait_vmcnt<0>();
+  if constexpr (LORA) {
+    // low-rank adapter: the accumulators start at T' B^T with T' = T / (gx gw) (the down
+    // projection divides), so the epilogue's scaling by gx gw leaves y = bf16(base + T B^T).
+    // Its first 32 rank values are loaded alongside the first stage; larger ranks follow.
+    const rsrc_t rt = make_rsrc(a.lt, (uint32_t)M * (uint32_t)a.rank * 2u);
+    const rsrc_t rb = make_rsrc(a.lb, (uint32_t)N * (uint32_t)a.rank * 2u);
+    const int nw0 = n0 + wn * C::WN, mw0 = m0 + wm * C::WM;
+    LoraRegs<TN, TM, 2> lo;
+    lora_load(lo, rt, rb, 0, a.rank, nw0, mw0, lane);
+    issue_stage(0);
+    wait_vmcnt<0>();
+    lora_mfma(acc, lo);
+    for (int k0 = 32; k0 < a.rank; k0 += 32) {
+      lora_load(lo, rt, rb, k0, a.rank, nw0, mw0, lane);
+      lora_mfma(acc, lo);
+    }
+  } else {
+    issue_stage(0);
+    wait_vmcnt<0>();
+  }
   __syncthreads();
   issue_stage(1);
   read_raw<TN, TM>(smem, C::A_OFF, C::B_OFF, rowa, rowb, lh, 0, r0a, r0b);
@@ -257,17 +275,7 @@ void gemm_w4a4_kernel(DecArgs a) {
   if (s < nk) stage(s, s0a, s0b, s1a, s1b);
 
   // ---- epilogue: y = bf16(acc * gx * gw) via an LDS copy of the tile [BM][BN]
-  float alpha = a.gx[0] * a.gw[0];
-  if constexpr (LORA) {
-    // with an adapter: y = bf16(acc * gx * gw + T B^T), the adapter's MFMAs accumulating onto
-    // the scaled accumulators
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j) acc[i][j] *= alpha;
-    lora_update<TN, TM>(acc, a.lt, a.lb, a.rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
-    alpha = 1.0f;
-  }
+  const float alpha = a.gx[0] * a.gw[0];
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
 #pragma unroll
@@ -306,6 +314,7 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
 }  // namespace
 
 bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kStageK == 0; }
+bool lora_pre_scaled_w4a4(const DecArgs& a) { return gemm_w4a4_supported(a); }
 
 hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s) {
   const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);

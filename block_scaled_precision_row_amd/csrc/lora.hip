@@ -5,19 +5,30 @@
 // model can run with a LoRA attached. The adapter adds s * B (A x) to the
 // linear's output; its rank-r intermediate T = s * X A^T [M][r] is computed
 // here from the unquantized bf16 activations and held in bf16 (the adapter
-// scale applied before that rounding), and the GEMM epilogues add T B^T.
+// scale applied before that rounding), and the GEMMs add T B^T. For a GEMM
+// whose output scale is one number alpha (the nvfp4 W4A4 kernel: gx * gw),
+// T may be produced as T / alpha, so that the GEMM can accumulate T B^T into
+// its accumulators before the main loop and let its own epilogue scale it.
 //
-// A workgroup owns 32 rows of X; its 8 waves split K in 64-deep chunks (wave
-// w takes chunks w, w + 8, ...). v_mfma_f32_32x32x16_bf16 takes 32 adapter
-// rows as the A operand (RT tiles of 32 cover the rank) and the 32 X rows as
-// the B operand, so a lane accumulates token m = lane % 32 and adapter rows
-// j = 32 r + 8 g + 4 (lane / 32) + e in register 4 g + e of tile r. In a chunk
-// starting at kc, lane half h holds K values [kc + 32 h, kc + 32 h + 32) of
-// both operands in 4 MFMA steps of 8, so each lane reads 64 contiguous bytes
-// of each of its rows. The adapter matrix (r x K bf16) is read by every
-// workgroup and stays in L2; X streams from HBM once. The 8 partial tiles
-// are summed through LDS in wave order, so the result does not depend on
-// timing.
+// This is a tall, thin GEMM (r <= 128 columns): X streams from HBM once and
+// the adapter matrix A (r x K) must reach every compute unit that works on
+// some rows. A workgroup takes 128 rows of X and one slice of K; its 8 waves
+// own 16 rows each and share the adapter slice, which the workgroup stages in
+// LDS 256 K values at a time, so A is read once per 128 rows instead of once
+// per wave. Every load of a 256-deep step (the adapter chunks and the wave's
+// 16 rows x 256 values of X, 128 bytes per lane) is issued at once, so a step
+// costs one memory latency. Slicing K gives enough workgroups to fill the chip
+// at a few thousand tokens with one or a few steps each; the slices' fp32
+// partial tiles go to a workspace and a second kernel adds them in slice order
+// (deterministic), scales and rounds. With one slice the first kernel writes
+// T itself.
+//
+// MFMA v_mfma_f32_16x16x32_bf16: the A operand is 16 adapter rows (RT tiles of
+// 16 cover the rank), the B operand the wave's 16 X rows, so a lane accumulates
+// token m = lane % 16 and adapter rows j = 16 r + 4 (lane / 16) + e in register
+// e of tile r. Within a 64-deep chunk at kc, lane group g = lane / 16 holds K
+// values [kc + 16 g, kc + 16 g + 16) of both operands (two MFMA steps of 8):
+// four lanes read one full 128-byte line of each X row.
 #include "bsq_device.hpp"
 #include "bsq_launch.hpp"
 
@@ -26,13 +37,10 @@ namespace bsq {
 namespace {
 
 constexpr int kDownWaves = 8;
-constexpr int kDownRows = 32;
-
-template <int RT>
-struct DownOps {
-  uint4 x[4];      // this lane's 32 values of its X row
-  uint4 a[RT][4];  // and of adapter rows 32 r + lane % 32
-};
+constexpr int kDownRows = 16 * kDownWaves;  // rows of X per workgroup
+constexpr int kStep = 256;                  // K values per step (adapter stage in LDS, X in registers)
+constexpr int kAPitch = kStep * 2 + 16;     // bytes per adapter row in LDS (padded against bank conflicts)
+constexpr int kMaxSlices = 16;
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 u) {
   union {
@@ -43,89 +51,246 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 u) {
   return c.h;
 }
 
-template <int RT>
+__device__ __forceinline__ float out_factor(float scale, const float* ga, const float* gb) {
+  return ga ? scale / (ga[0] * gb[0]) : scale;
+}
+
+// adapter step at kb: chunk c (thread tid + 512 i) is adapter row c / 32, values kb + 8 (c % 32) .. + 7
+template <int APT, int ACH>
+__device__ __forceinline__ void load_adapter(uint4 (&areg)[APT], rsrc_t ra, int tid, int kb, int k1, int K) {
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int c = tid + 64 * kDownWaves * i;
+    const int row = c >> 5, k = kb + 8 * (c & 31);
+    const bool ok = c < ACH && k < k1;
+    areg[i] = bload16(ra, ok ? (uint32_t)(row * K + k) * 2u : kBufOut);
+  }
+}
+// this lane's X values of the step at kb: 16 values at kb + 64 c + 16 g for c = 0 .. 3
+__device__ __forceinline__ void load_rows(uint4 (&r)[8], rsrc_t rx, uint32_t xrow, int lg, int kb, int k1) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int k = kb + 64 * c + 16 * lg;  // K % 32 == 0: all 16 values inside the slice or none
+    const bool ok = k < k1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) r[2 * c + q] = bload16(rx, ok ? xrow + (uint32_t)k * 2u + 16u * q : kBufOut);
+  }
+}
+
+// Grid (K slices, row blocks): the slices of a row block are neighbours in launch order, so
+// the workgroups running together read whole rows of X rather than one segment of every row.
+// Slice z covers K values [z * kr, min(K, (z + 1) * kr)), kr a multiple of kStep. With one slice: t = bf16(f * acc); otherwise the fp32 partial tile goes to
+// part [slices][M][rank].
+// With QUANT the kernel also writes X's nvfp4 encoding with global scale *gq (what the
+// activation quantizer writes): a lane's 16 values of a 64-deep chunk are one 16-element block,
+// so every block is encoded once, from the registers the projection uses.
+template <int RT, bool QUANT>
 __global__ __launch_bounds__(64 * kDownWaves) void lora_down_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                      const uint16_t* __restrict__ a, int M, int K,
-                                                                     int rank, float scale,
-                                                                     uint16_t* __restrict__ t) {
-  __shared__ float red[kDownWaves * RT * 16 * 64];
-  const int m0 = blockIdx.x * kDownRows;
-  const int rows = M - m0 < kDownRows ? M - m0 : kDownRows;
+                                                                     int rank, int kr, float scale, const float* ga,
+                                                                     const float* gb, float* __restrict__ part,
+                                                                     uint16_t* __restrict__ t, const float* gq,
+                                                                     uint8_t* __restrict__ xq,
+                                                                     uint8_t* __restrict__ xs) {
+  constexpr int AROWS = 16 * RT;
+  constexpr int ACH = AROWS * (kStep / 8);                              // 16-byte chunks per adapter step
+  constexpr int APT = (ACH + 64 * kDownWaves - 1) / (64 * kDownWaves);  // chunks per thread
+  constexpr int TP = 16 * RT + 4;  // floats per row of the output tile in LDS (padded)
+  constexpr int SA = AROWS * kAPitch > kDownRows * TP * 4 ? AROWS * kAPitch : kDownRows * TP * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t sa[SA];
+
+  const int m0 = blockIdx.y * kDownRows;
+  const int k0 = blockIdx.x * kr;
+  const int k1 = K - k0 < kr ? K : k0 + kr;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31, lh = lane >> 5;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int rows = M - m0 < kDownRows ? M - m0 : kDownRows;
 
-  // rows past M and adapter rows past the rank read as zeros (offsets past the records)
-  const rsrc_t rx = make_rsrc(x + (int64_t)m0 * ldx, (uint32_t)rows * (uint32_t)ldx * 2u);
+  // this wave's rows of X (rows past M read as zeros) and the adapter (rows past the rank too)
+  // (readfirstlane: the compiler computes the clamp on the vector unit, and a buffer resource
+  // it cannot prove uniform turns every load into a loop over lanes)
+  const int wrow0 = 16 * wave;
+  const int wrows = __builtin_amdgcn_readfirstlane(rows - wrow0 < 0 ? 0 : (rows - wrow0 < 16 ? rows - wrow0 : 16));
+  const rsrc_t rx = make_rsrc(x + (int64_t)(m0 + (wrows ? wrow0 : 0)) * ldx, (uint32_t)wrows * (uint32_t)ldx * 2u);
   const rsrc_t ra = make_rsrc(a, (uint32_t)rank * (uint32_t)K * 2u);
   const uint32_t xrow = (uint32_t)lr * (uint32_t)ldx * 2u;
-  uint32_t arow[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) arow[r] = (uint32_t)(32 * r + lr) * (uint32_t)K * 2u;
 
-  const int nch = (K + 63) / 64;
-  auto load = [&](DownOps<RT>& o, int c) __attribute__((always_inline)) {
-    const int kc = c * 64 + 32 * lh;  // K % 32 == 0: a lane's 32 values are all inside K or all past it
-    const bool ok = c < nch && kc < K;
+  v4f acc[RT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o.x[q] = bload16(rx, ok ? xrow + (uint32_t)kc * 2u + 16u * q : kBufOut);
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o.a[r][q] = bload16(ra, ok ? arow[r] + (uint32_t)kc * 2u + 16u * q : kBufOut);
-  };
+  for (int r = 0; r < RT; ++r) acc[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  v16f acc[RT];
+  for (int kb = k0; kb < k1; kb += kStep) {
+    uint4 areg[APT], xr[8];
+    load_adapter<APT, ACH>(areg, ra, tid, kb, k1, K);  // adapter first: its wait leaves X in flight
+    load_rows(xr, rx, xrow, lg, kb, k1);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the step ahead of its first use
 #pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = v16f{};
-  DownOps<RT> cur, nxt;
-  load(cur, wave);
-  for (int c = wave; c < nch; c += kDownWaves) {
-    load(nxt, c + kDownWaves);  // past the wave's last chunk: reads zeros, unused
+    for (int i = 0; i < APT; ++i) {
+      const int c = tid + 64 * kDownWaves * i;
+      if (c < ACH) *reinterpret_cast<uint4*>(&sa[(c >> 5) * kAPitch + 16 * (c & 31)]) = areg[i];
+    }
+    __syncthreads();
+    if constexpr (QUANT) {
+      const float G = 1.0f / gq[0];
+      const int64_t row = m0 + wrow0 + lr;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+      for (int c = 0; c < 4; ++c) {
+        const int k = kb + 64 * c + 16 * lg;
+        if (lr < wrows && k < k1) {
+          float fv[16];
+          bf16x16_to_f32(xr[2 * c], xr[2 * c + 1], fv);
+          uint2 codes;
+          const uint32_t sf = quant_block16_nvfp4(fv, G, codes);
+          *reinterpret_cast<uint2*>(xq + row * (K >> 1) + (k >> 1)) = codes;
+          xs[row * (K >> 4) + (k >> 4)] = (uint8_t)sf;
+        }
+      }
+    }
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf(cur.a[r][q]), as_v8bf(cur.x[q]), acc[r], 0, 0, 0);
-    cur = nxt;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const uint4 av =
+              *reinterpret_cast<const uint4*>(sa + (16 * r + lr) * kAPitch + 2 * (64 * c + 16 * lg) + 16 * q);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(av), as_v8bf(xr[2 * c + q]), acc[r], 0, 0, 0);
+        }
+    __syncthreads();  // the adapter stage is rewritten by the next step
   }
 
+  // The block's result is one contiguous run of rows * rank values (T or this slice's partials):
+  // stage the tile [128][16 RT] fp32 in LDS (lane: row 16 wave + m, adapter rows 16 r + 4 g + e)
+  // and write the run with consecutive threads on consecutive values.
+  float* tile = reinterpret_cast<float*>(sa);
 #pragma unroll
   for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[((wave * RT + r) * 16 + e) * 64 + lane] = acc[r][e];
+    *reinterpret_cast<float4*>(&tile[(wrow0 + lr) * TP + 16 * r + 4 * lg]) =
+        make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
   __syncthreads();
-
-  // output (ml, j): adapter row j = 32 r + jj sits in register 4 (jj / 8) + jj % 4 of lane
-  // ml + 32 ((jj / 4) % 2); consecutive threads write consecutive j of a row
-  for (int idx = tid; idx < kDownRows * rank; idx += 64 * kDownWaves) {
-    const int ml = idx / rank, j = idx - ml * rank;
-    if (ml >= rows) break;  // rows only grow with idx
-    const int r = j >> 5, jj = j & 31;
-    const int reg = 4 * (jj >> 3) + (jj & 3), ln = ml + 32 * ((jj >> 2) & 1);
-    float sum = 0.0f;
+  const int n = rows * rank;
+  if (gridDim.x == 1) {
+    const float f = out_factor(scale, ga, gb);
+    uint16_t* dst = t + (int64_t)m0 * rank;  // 16-byte aligned: m0 * rank * 2 is a multiple of 256
+    for (int i = 8 * tid; i < n; i += 8 * 64 * kDownWaves) {
+      uint32_t w[4];
 #pragma unroll
-    for (int w = 0; w < kDownWaves; ++w) sum += red[((w * RT + r) * 16 + reg) * 64 + ln];
-    t[(int64_t)(m0 + ml) * rank + j] = (uint16_t)(pack_bf16x2(scale * sum, 0.0f) & 0xFFFFu);
+      for (int e = 0; e < 4; ++e) {
+        const int i0 = i + 2 * e, i1 = i0 + 1;
+        const float v0 = i0 < n ? tile[(i0 / rank) * TP + i0 % rank] : 0.0f;
+        const float v1 = i1 < n ? tile[(i1 / rank) * TP + i1 % rank] : 0.0f;
+        w[e] = pack_bf16x2(f * v0, f * v1);
+      }
+      if (i + 8 <= n) {
+        *reinterpret_cast<uint4*>(dst + i) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (i + e < n) dst[i + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  } else {
+    float* dst = part + ((int64_t)blockIdx.x * M + m0) * rank;
+    const bool vec = ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
+    for (int i = 4 * tid; i < n; i += 4 * 64 * kDownWaves) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = i + e < n ? tile[((i + e) / rank) * TP + (i + e) % rank] : 0.0f;
+      if (vec && i + 4 <= n) {
+        *reinterpret_cast<float4*>(dst + i) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i + e < n) dst[i + e] = v[e];
+      }
+    }
+  }
+}
+
+// t[i] = bf16(f * sum over slices z in order of part[z][i]), i over M * rank; four consecutive
+// values per thread, all slices' loads issued before the sums
+template <int Z>
+__global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __restrict__ part, int64_t n, int slices,
+                                                               float scale, const float* ga, const float* gb,
+                                                               uint16_t* __restrict__ t) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  const float f = out_factor(scale, ga, gb);
+  if (i0 + 4 <= n && (n & 3) == 0) {
+    float4 v[Z];
+#pragma unroll
+    for (int z = 0; z < Z; ++z)
+      v[z] = z < slices ? *reinterpret_cast<const float4*>(part + z * n + i0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 s = v[0];
+#pragma unroll
+    for (int z = 1; z < Z; ++z)
+      if (z < slices) {
+        s.x += v[z].x;
+        s.y += v[z].y;
+        s.z += v[z].z;
+        s.w += v[z].w;
+      }
+    *reinterpret_cast<uint2*>(t + i0) = make_uint2(pack_bf16x2(f * s.x, f * s.y), pack_bf16x2(f * s.z, f * s.w));
+  } else {
+    for (int64_t i = i0; i < n && i < i0 + 4; ++i) {
+      float s = 0.0f;
+      for (int z = 0; z < slices; ++z) s += part[z * n + i];
+      t[i] = (uint16_t)(pack_bf16x2(f * s, 0.0f) & 0xFFFFu);
+    }
   }
 }
 
 template <int RT>
 hipError_t run_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank, float scale,
-                    uint16_t* t, hipStream_t s) {
-  const unsigned blocks = (unsigned)((M + kDownRows - 1) / kDownRows);
-  hipLaunchKernelGGL((lora_down_kernel<RT>), dim3(blocks), dim3(64 * kDownWaves), 0, s, x, ldx, a, (int)M, (int)K,
-                     rank, scale, t);
+                    const float* ga, const float* gb, float* part, uint16_t* t, const float* gq, uint8_t* xq,
+                    uint8_t* xs, hipStream_t s) {
+  const int slices = lora_down_slices(M, K, rank);
+  const int64_t kr = lora_down_slice_k(K, slices);
+  const dim3 grid((unsigned)slices, (unsigned)((M + kDownRows - 1) / kDownRows));
+  if (xq)
+    hipLaunchKernelGGL((lora_down_kernel<RT, true>), grid, dim3(64 * kDownWaves), 0, s, x, ldx, a, (int)M, (int)K,
+                       rank, (int)kr, scale, ga, gb, part, t, gq, xq, xs);
+  else
+    hipLaunchKernelGGL((lora_down_kernel<RT, false>), grid, dim3(64 * kDownWaves), 0, s, x, ldx, a, (int)M, (int)K,
+                       rank, (int)kr, scale, ga, gb, part, t, gq, xq, xs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || slices == 1) return e;
+  const int64_t n = M * rank;
+  const dim3 fgrid((unsigned)((n + 1023) / 1024));
+  hipLaunchKernelGGL(lora_down_finish_kernel<kMaxSlices>, fgrid, dim3(256), 0, s, part, n, slices, scale, ga, gb, t);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// K slices: enough workgroups (row blocks x slices) to cover the 256 compute units twice, at
+// most kMaxSlices, and few enough that the partial products (slices x M x rank fp32, written
+// and read once) stay within a quarter of X's bytes; slices are whole steps, all but the last
+// of equal length.
+int64_t lora_down_slice_k(int64_t K, int slices) {
+  const int64_t steps = (K + kStep - 1) / kStep;
+  return ((steps + slices - 1) / slices) * kStep;
+}
+int lora_down_slices(int64_t M, int64_t K, int rank) {
+  const int64_t blocks = (M + kDownRows - 1) / kDownRows;
+  int64_t z = (512 + blocks - 1) / blocks;
+  const int64_t steps = (K + kStep - 1) / kStep;
+  if (z > steps) z = steps;
+  if (z > kMaxSlices) z = kMaxSlices;
+  if (z > K / (8 * (int64_t)rank)) z = K / (8 * (int64_t)rank);
+  if (z < 1) z = 1;
+  const int64_t kr = lora_down_slice_k(K, (int)z);
+  return (int)((K + kr - 1) / kr);  // no empty slice
+}
+
 hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
-                            float scale, uint16_t* t, hipStream_t s) {
-  if (rank <= 32) return run_down<1>(x, ldx, a, M, K, rank, scale, t, s);
-  if (rank <= 64) return run_down<2>(x, ldx, a, M, K, rank, scale, t, s);
-  return run_down<4>(x, ldx, a, M, K, rank, scale, t, s);
+                            float scale, const float* ga, const float* gb, float* part, uint16_t* t, hipStream_t s,
+                            const float* gq, uint8_t* xq, uint8_t* xs) {
+  if (rank <= 16) return run_down<1>(x, ldx, a, M, K, rank, scale, ga, gb, part, t, gq, xq, xs, s);
+  if (rank <= 32) return run_down<2>(x, ldx, a, M, K, rank, scale, ga, gb, part, t, gq, xq, xs, s);
+  if (rank <= 64) return run_down<4>(x, ldx, a, M, K, rank, scale, ga, gb, part, t, gq, xq, xs, s);
+  return run_down<8>(x, ldx, a, M, K, rank, scale, ga, gb, part, t, gq, xq, xs, s);
 }
 
 }  // namespace bsq

@@ -211,9 +211,14 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscal
  * Arithmetic: T = bf16(s * sum_k x[m][k] a[j][k]) (fp32 accumulation), then
  *   y[m][n] = bf16( base_acc[m][n] * (the linear's scales) + sum_j T[m][j] b[n][j] )
  * with the adapter sum accumulated in fp32 onto the scaled base accumulator,
- * so the output is rounded once. T is the only other rounding.
+ * so the output is rounded once. T is the only other rounding. On the tiled
+ * W4A4 path (K % 256 == 0 beyond the few-token range) the output scale
+ * alpha = input_scale * w_scale2 is folded into T instead: T = bf16(s / alpha
+ * * sum ...) is accumulated with the base and the sum scaled by alpha, which
+ * requires alpha to be a positive normal fp32 number (calibrated scales are).
  * Workspace: bsq_lora_workspace_bytes(f, M, N, K, rank, flags) bytes,
- * 256-byte aligned: the linear's workspace followed by T [M][rank].
+ * 256-byte aligned: the linear's workspace, T [M][rank], and for shapes where
+ * the down projection splits K over workgroups its fp32 partial products.
  * Extra shape rules: ldx < 2^24; M * rank and N * rank below 2^29.
  * BSQ_ERR_ARG for a non-finite lora_scale; lora_a / lora_b 16-byte aligned.
  */
@@ -231,10 +236,13 @@ bsq_status bsq_gemm_nvfp4_lora(const uint16_t* x, int64_t ldx, const uint8_t* w,
  * The adapter's down projection alone, as the entry points above compute it:
  *   t[m][j] = bf16( s * sum_k x[m][k] a[j][k] ),  t [M][rank] bf16 (16-byte aligned)
  * x [M][ldx] bf16 (rules as for the quantizers, plus ldx < 2^24), lora_a and
- * rank as above.
+ * rank as above. Workspace: bsq_lora_down_workspace_bytes(M, K, rank) bytes,
+ * 16-byte aligned (0, and workspace may be NULL, when K is not split).
  */
+size_t bsq_lora_down_workspace_bytes(int64_t M, int64_t K, int64_t rank);
 bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a, int64_t M, int64_t K,
-                         int64_t rank, float lora_scale, uint16_t* t, hipStream_t stream);
+                         int64_t rank, float lora_scale, uint16_t* t, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * Fallback dequantization to bf16 ("BFL (fp8r / nvfp4)", last paragraph of

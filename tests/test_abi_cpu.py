@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 19
+    assert len(syms) == 20
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
@@ -113,8 +113,16 @@ def test_lora_validation():
     pad = lambda n: (n + 255) // 256 * 256
     fp8, nv, wo = _lib.BSQ_FMT_FP8R, _lib.BSQ_FMT_NVFP4, _lib.BSQ_WEIGHT_ONLY
     wsb = L.bsq_lora_workspace_bytes
-    assert wsb(fp8, 4096, 3072, 3072, 32, 0) == L.bsq_gemm_workspace_bytes(fp8, 4096, 3072, 3072, 0) + pad(4096 * 64)
-    assert wsb(nv, 4096, 12288, 3072, 16, wo) == pad(4096 * 32)
+    # the linear's workspace, T, and the fp32 partials of the K slices: at 4096 tokens K = 3072
+    # is cut into 12 slices of 256 for rank 32 (384 workgroups), 3 of 1024 for rank 128 (partials
+    # within a quarter of X's bytes)
+    assert L.bsq_lora_down_workspace_bytes(4096, 3072, 32) == pad(12 * 4096 * 32 * 4)
+    assert L.bsq_lora_down_workspace_bytes(4096, 3072, 128) == pad(3 * 4096 * 128 * 4)
+    assert wsb(fp8, 4096, 3072, 3072, 32, 0) == (L.bsq_gemm_workspace_bytes(fp8, 4096, 3072, 3072, 0) + pad(4096 * 64)
+                                                 + pad(12 * 4096 * 32 * 4))
+    assert wsb(nv, 4096, 12288, 3072, 16, wo) == pad(4096 * 32) + pad(12 * 4096 * 16 * 4)
+    # many row blocks: one slice, no partials
+    assert L.bsq_lora_down_workspace_bytes(65536, 3072, 32) == 0
     assert wsb(nv, 0, 12288, 3072, 16, 0) == 0 and wsb(3, 64, 64, 64, 16, 0) == 0
     g = L.bsq_gemm_fp8r_lora
     ws = wsb(fp8, 64, 64, 64, 16, 0)
@@ -137,13 +145,14 @@ def test_lora_validation():
     assert n(A, 64, B, C, D, None, A, B, 16, 1.0, D, 64, 64, 64, 64, wo, None, 0, None) == WS    # T needs room
     assert n(A, 64, B, C, D, D, A, B, 16, 1.0, D, 64, 64, 64, 64, 8, A, ws, None) == ARG
     d = L.bsq_lora_down
-    # x, ldx, a, M, K, rank, scale, t, stream
-    assert d(A, 64, B, 4, 64, 0, 1.0, C, None) == SHAPE
-    assert d(A, 64, B, 4, 48, 16, 1.0, C, None) == SHAPE                 # K % 32
-    assert d(A, 64, B, 4, 64, 16, float("nan"), C, None) == ARG
-    assert d(A, 64, None, 4, 64, 16, 1.0, C, None) == NULL
-    assert d(A, 64, B, 4, 64, 16, 1.0, ODD, None) == ALIGN
-    assert d(None, 64, None, 0, 64, 16, 1.0, None, None) == OK
+    # x, ldx, a, M, K, rank, scale, t, ws, ws_bytes, stream
+    assert d(A, 64, B, 4, 64, 0, 1.0, C, None, 0, None) == SHAPE
+    assert d(A, 64, B, 4, 48, 16, 1.0, C, None, 0, None) == SHAPE                 # K % 32
+    assert d(A, 64, B, 4, 64, 16, float("nan"), C, None, 0, None) == ARG
+    assert d(A, 64, None, 4, 64, 16, 1.0, C, None, 0, None) == NULL
+    assert d(A, 64, B, 4, 64, 16, 1.0, ODD, None, 0, None) == ALIGN
+    assert d(A, 3072, B, 4, 3072, 16, 1.0, C, None, 0, None) == WS                # K is split: partials
+    assert d(None, 64, None, 0, 64, 16, 1.0, None, None, 0, None) == OK
 
 
 def test_dequant_validation():

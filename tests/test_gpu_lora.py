@@ -176,3 +176,26 @@ def test_empty_batch_is_a_noop():
     x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
     y = L.bsq_gemm_fp8r_lora(x, w, s, a, b, 1.0)
     assert y.shape == (0, 64)
+
+
+@pytest.mark.parametrize("M,N,K,rank", [(300, 512, 512, 16), (4096, 3072, 3072, 32), (20, 1024, 512, 32),
+                                        (130, 200, 160, 48), (257, 300, 544, 128)])
+def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, rank):
+    """The W4A4 path encodes X to nvfp4 inside its down projection: the workspace's first two
+    parts (packed codes, then block scales, each padded to 256 bytes) must equal the activation
+    quantizer's output bit for bit."""
+    x, w, a, b = _inputs(M, N, K, rank, 3)
+    gw = quant.calibrate_global_scale(w)
+    wq, sfw = quant.quantize_nvfp4(w, gw)
+    gx = dev_scalar(quant.calibrate_global_scale(x))
+    dx = dev_bf16(x)
+    nbytes = L.bsq_lora_workspace_bytes(L.BSQ_FMT_NVFP4, M, N, K, rank)
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    L.bsq_gemm_nvfp4_lora(dx, dev(wq), dev(sfw), dev_scalar(gw), gx, dev_bf16(a), dev_bf16(b), SCALE, workspace=ws)
+    xq, xs = L.bsq_quantize_act_nvfp4(dx, gx)
+    torch.cuda.synchronize()
+    pad = lambda n: (n + 255) // 256 * 256
+    got = host(ws)
+    assert np.array_equal(got[:M * K // 2], host(xq).reshape(-1))
+    off = pad(M * K // 2)
+    assert np.array_equal(got[off:off + M * K // 16], host(xs).reshape(-1))

@@ -234,6 +234,9 @@ void gemm_w4a4_kernel(DecArgs a) {
     LoraRegs<TN, TM, 2> lo;
     lora_load(lo, rt, rb, 0, a.rank, nw0, mw0, lane);
     issue_stage(0);
+    // both sets of loads are in flight before anything waits (the scheduler would otherwise
+    // hoist the adapter MFMAs, and their wait, above the stage's DMA)
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     lora_mfma(acc, lo);
     for (int k0 = 32; k0 < a.rank; k0 += 32) {

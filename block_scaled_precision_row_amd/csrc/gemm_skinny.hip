@@ -186,19 +186,28 @@ struct Scheme<kW8A16> {
 
 // sum the NW partial tiles (red = [NW][MB][16 registers][64 lanes]) in wave order, scale,
 // convert and store the tile
-// low-rank adapter term of output (m, n): T[m][:] . B[n][:] over the rank, fp32 in rank order
-// (few tokens: a handful of outputs per thread, read straight from the caches)
-__device__ __forceinline__ float lora_dot(const DecArgs& a, int m, int n) {
-  const uint16_t* t = a.lt + (int64_t)m * a.rank;
-  const uint16_t* b = a.lb + (int64_t)n * a.rank;
-  float d = 0.0f;
-  for (int k = 0; k < a.rank; ++k)
-    d = fmaf(__uint_as_float((uint32_t)t[k] << 16), __uint_as_float((uint32_t)b[k] << 16), d);
-  return d;
+// Low-rank adapter tile of the workgroup: T B^T for its 32 weight rows and activation block j
+// = wave (waves 0 .. MB - 1), on the bf16 matrix cores, 64 rank values per batch of loads, into
+// lred [MB][16][64] in the accumulator layout (lane: token, register: weight row).
+template <int MB>
+__device__ __forceinline__ void skinny_lora_tile(const DecArgs& a, float* lred, int m0, int n0, int wave, int lane) {
+  if (wave >= MB) return;
+  const rsrc_t rt = make_rsrc(a.lt, (uint32_t)a.M * (uint32_t)a.rank * 2u);
+  const rsrc_t rb = make_rsrc(a.lb, (uint32_t)a.N * (uint32_t)a.rank * 2u);
+  v16f l[1][1] = {{v16f{}}};
+  for (int k0 = 0; k0 < a.rank; k0 += 64) {
+    LoraRegs<1, 1, 4> r;
+    lora_load(r, rt, rb, k0, a.rank, n0, m0 + 32 * wave, lane);
+    lora_mfma(l, r);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lred[(wave * 16 + e) * 64 + lane] = l[0][0][e];
 }
 
+// lred: the adapter tiles (LORA), added to the scaled sums: y = bf16(acc * scale + T B^T)
 template <int MODE, int MB, int NW, bool LORA>
-__device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* red, int m0, int n0, int tid) {
+__device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* red, const float* lred, int m0, int n0,
+                                                int tid) {
   const int M = (int)a.M, N = (int)a.N;
   float alpha = 1.0f;
   if constexpr (MODE == kW4A4) alpha = a.gx[0] * a.gw[0];
@@ -209,7 +218,7 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
     const int m = m0 + ml;
     if (m >= M) break;
     const int j = ml >> 5, lm = ml & 31;
-    float v[2];
+    float v[2], lv[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int nl = 2 * p + e;  // n = 8 G + 4 H + q is held by lane lm + 32 H in register 4 G + q
@@ -218,6 +227,7 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += red[((w * MB + j) * 16 + r) * 64 + ln];
       v[e] = s;
+      lv[e] = LORA ? lred[(j * 16 + r) * 64 + ln] : 0.0f;
     }
     const int n = n0 + 2 * p;
     float s0 = alpha, s1 = alpha;
@@ -232,8 +242,8 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
     }
     float y0 = v[0] * s0, y1 = v[1] * s1;
     if constexpr (LORA) {  // y = bf16(acc * scale + T B^T)
-      if (n < N) y0 += lora_dot(a, m, n);
-      if (n + 1 < N) y1 += lora_dot(a, m, n + 1);
+      y0 += lv[0];
+      y1 += lv[1];
     }
     const uint32_t pk = pack_bf16x2(y0, y1);
     uint16_t* yr = a.y + (int64_t)m * a.ldy;
@@ -262,7 +272,7 @@ __device__ __forceinline__ void skinny_epilogue(const DecArgs& a, const float* r
 #pragma unroll
           for (int w = 0; w < NW; ++w) sum += red[((w * MB + j) * 16 + r) * 64 + ln];
           float yv = sum * alpha;
-          if constexpr (LORA) yv += lora_dot(a, m, n + e);
+          if constexpr (LORA) yv += lred[(j * 16 + r) * 64 + ln];
           f[e] = bf16_lo(pack_bf16x2(yv, 0.0f));  // the value the bf16 output holds
         }
         uint2 codes;
@@ -371,7 +381,7 @@ __global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel
   constexpr int NV_BYTES = 32 * 64 + 256;                   // codes + scales of one nvfp4 operand
   constexpr int X_BYTES = XBF ? 32 * 256 : NV_BYTES;        // per activation block
   constexpr int STAGE = NV_BYTES + MB * X_BYTES;            // one buffer per wave
-  constexpr int RED = NW * MB * 16 * 64 * 4;
+  constexpr int RED = NW * MB * 16 * 64 * 4 + (LORA ? MB * 16 * 64 * 4 : 0);  // partial tiles, adapter tiles
   constexpr int LDS = NW * STAGE > RED ? NW * STAGE : RED;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
@@ -465,13 +475,15 @@ __global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel
   }
   __syncthreads();  // LDS is reused for the reduction
 
-  float* red = reinterpret_cast<float*>(smem);  // [NW][MB][16][64]
+  float* red = reinterpret_cast<float*>(smem);  // [NW][MB][16][64], then the adapter tiles [MB][16][64]
+  float* lred = red + NW * MB * 16 * 64;
 #pragma unroll
   for (int j = 0; j < MB; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
+  if constexpr (LORA) skinny_lora_tile<MB>(a, lred, m0, n0, wave, lane);
   __syncthreads();
-  skinny_epilogue<MODE, MB, NW, LORA>(a, red, m0, n0, tid);
+  skinny_epilogue<MODE, MB, NW, LORA>(a, red, lred, m0, n0, tid);
 }
 
 // ---- LDS-DMA variant (E4M3 weights): stage layout of one wave -----------------------
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   constexpr int STAGE = L::W_BYTES + MB * L::X_BYTES;
   constexpr int WAVE = kSkRing * STAGE;
   constexpr int LOADS = L::W_LOADS + MB * L::X_LOADS;  // DMA instructions per stage
-  constexpr int RED = NW * MB * 16 * 64 * 4;
+  constexpr int RED = NW * MB * 16 * 64 * 4 + (LORA ? MB * 16 * 64 * 4 : 0);  // partial tiles, adapter tiles
   constexpr int LDS = NW * WAVE > RED ? NW * WAVE : RED;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert((kSkRing - 1) * LOADS < 64, "vmcnt range");
@@ -626,14 +638,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   __syncthreads();  // every ring is idle: the LDS is reused for the reduction
 
   // sum the NW partial tiles in wave order
-  float* red = reinterpret_cast<float*>(smem);  // [NW][MB][16][64]
+  float* red = reinterpret_cast<float*>(smem);  // [NW][MB][16][64], then the adapter tiles [MB][16][64]
+  float* lred = red + NW * MB * 16 * 64;
 #pragma unroll
   for (int j = 0; j < MB; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
+  if constexpr (LORA) skinny_lora_tile<MB>(a, lred, m0, n0, wave, lane);
   __syncthreads();
 
-  skinny_epilogue<MODE, MB, NW, LORA>(a, red, m0, n0, tid);
+  skinny_epilogue<MODE, MB, NW, LORA>(a, red, lred, m0, n0, tid);
 }
 
 template <int MODE, int MB, int NW>

@@ -133,10 +133,9 @@ def quantized_output_comparison(L, dev, y3, gemm_args, operands):
 def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
     """LoRA side path: each linear from bf16 X (activation quantization + GEMM) without and with a
     synthetic adapter of several ranks (down projection + GEMM with the up projection fused),
-    warm, in us (fastest of three runs of `reps` back-to-back calls; the plain linear is re-timed
-    between ranks and its fastest time is the reference); plus the down projection alone and its
-    rate over the bytes it must move (X read once, A read, T written). Also a 16-token nvfp4
-    linear."""
+    warm, in us: medians of 20 alternating pairs of calls; plus the down projection alone (mean
+    of `reps` back-to-back calls) and its rate over the bytes it must move (X read once, A read,
+    T written). Also a 16-token nvfp4 linear."""
     import torch
 
     lib = L.lib
@@ -146,22 +145,37 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
     def up_bf16(bits):
         return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
 
-    def timed(fn, a, batches=3):
-        """us per call: the fastest of `batches` runs of `reps` back-to-back calls (clock and
-        power drift between runs is larger than the adapter's cost at small ranks)"""
+    def paired(plain, call, pairs=20):
+        """median us per call of the plain linear and of the linear with the adapter, timed in
+        alternating pairs (each call between two events on the stream), so that clock and
+        power drift affect both alike"""
+        for fn, a in (plain, call):
+            st = fn(*a)
+            if st != 0:
+                raise L.BsqError(fn.__name__, st)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(pairs)]
+        for e in ev:
+            e[0].record()
+            plain[0](*plain[1])
+            e[1].record()
+            call[0](*call[1])
+            e[2].record()
+        torch.cuda.synchronize()
+        tp = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+        tl = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
+        return tp[pairs // 2], tl[pairs // 2]
+
+    def timed(fn, a):
         st = fn(*a)
         if st != 0:
             raise L.BsqError(fn.__name__, st)
-        best = float("inf")
-        for _ in range(batches):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                fn(*a)
-            e1.record()
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1) / reps * 1e3)
-        return best
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
 
     out = {}
     layers = [("nvfp4", "nvfp4_4096x12288x3072", x3, M, N_FP4), ("fp8r", "fp8r_4096x3072x3072", x2, M, N_FP8),
@@ -175,7 +189,7 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
                                           ws.numel(), stream))
         else:
             plain = (lib.bsq_gemm_fp8r, (P(x), K, P(w2q), P(w2s), P(y), N, Mx, N, K, 0, P(ws), ws.numel(), stream))
-        entry = {"plain_us": round(timed(*plain), 2), "ranks": {}}
+        entry = {"ranks": {}}
         for rank in (16, 32, 64, 128):
             a, b = syn.lora_adapter(syn.NVFP4_UP if scheme == "nvfp4" else syn.FP8R_4096, rank, N, K)
             da, db = up_bf16(a), up_bf16(b)
@@ -185,18 +199,16 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
             else:
                 call = (lib.bsq_gemm_fp8r_lora, (P(x), K, P(w2q), P(w2s), P(da), P(db), rank, 1.0, P(y), N, Mx, N,
                                                  K, 0, P(ws), ws.numel(), stream))
-            us = timed(*call)
-            entry["plain_us"] = round(min(entry["plain_us"], timed(*plain)), 2)  # interleaved re-check
+            plain_us, us = paired(plain, call)
             t = torch.empty((Mx, rank), dtype=torch.bfloat16, device=dev)
             dws = torch.empty((max(1, lib.bsq_lora_down_workspace_bytes(Mx, K, rank)),), dtype=torch.uint8,
                               device=dev)
             down_us = timed(lib.bsq_lora_down, (P(x), K, P(da), Mx, K, rank, 1.0, P(t), P(dws), dws.numel(), stream))
             down_bytes = Mx * K * 2 + rank * K * 2 + Mx * rank * 2
             entry["ranks"][str(rank)] = {
-                "us": round(us, 2), "down_us": round(down_us, 2),
+                "plain_us": round(plain_us, 2), "us": round(us, 2),
+                "overhead_pct": round(100.0 * (us / plain_us - 1.0), 2), "down_us": round(down_us, 2),
                 "down_gbs": round(down_bytes / (down_us * 1e-6) / 1e9, 1)}
-        for r in entry["ranks"].values():
-            r["overhead_pct"] = round(100.0 * (r["us"] / entry["plain_us"] - 1.0), 2)
         out[name] = entry
     out["note"] = ("whole linear from bf16 X in both columns (activation quantizer + GEMM; with the adapter also "
                    "its down projection), synthetic adapter with scale 1; the pages report about 5 % more "

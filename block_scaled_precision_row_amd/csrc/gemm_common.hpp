@@ -234,35 +234,33 @@ __device__ __forceinline__ void lora_load(LoraRegs<TN, TM, S>& r, rsrc_t rt, rsr
     for (int j = 0; j < TM; ++j) r.t[s][j] = lora_chunk(rt, mw0 + 32 * j + lr, k0 + 16 * s + 8 * lh, rank);
   }
 }
+// the adapter MFMAs of rank steps k0 / 16 .. k0 / 16 + S - 1 (steps past the rank are skipped)
 template <int TN, int TM, int S>
-__device__ __forceinline__ void lora_mfma(v16f (&acc)[TN][TM], const LoraRegs<TN, TM, S>& r) {
+__device__ __forceinline__ void lora_mfma(v16f (&acc)[TN][TM], const LoraRegs<TN, TM, S>& r, int k0, int rank) {
 #pragma unroll
-  for (int s = 0; s < S; ++s)
+  for (int s = 0; s < S; ++s) {
+    if (k0 + 16 * s >= rank) break;  // uniform
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int j = 0; j < TM; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.b[s][i], r.t[s][j], acc[i][j], 0, 0, 0);
+  }
 }
 
-// acc[i][j] (n-tile i at n = nw0 + 32 i, m-tile j at m = mw0 + 32 j) += T[m][:] . B[n][:]
+// acc[i][j] (n-tile i at n = nw0 + 32 i, m-tile j at m = mw0 + 32 j) += T[m][:] . B[n][:],
+// 64 rank values per batch of loads (32 for the largest wave tiles, whose accumulators leave
+// fewer registers)
 template <int TN, int TM>
 __device__ __forceinline__ void lora_update(v16f (&acc)[TN][TM], const uint16_t* lt, const uint16_t* lb, int rank,
                                             int M, int N, int nw0, int mw0, int lane) {
+  constexpr int S = TN + TM >= 8 ? 2 : 4;
   const rsrc_t rt = make_rsrc(lt, (uint32_t)M * (uint32_t)rank * 2u);
   const rsrc_t rb = make_rsrc(lb, (uint32_t)N * (uint32_t)rank * 2u);
-  const int lr = lane & 31, lh = lane >> 5;
-  for (int k = 0; k < rank; k += 16) {
-    v8bf ua[TN], ub[TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i) ua[i] = lora_chunk(rb, nw0 + 32 * i + lr, k + 8 * lh, rank);
-#pragma unroll
-    for (int j = 0; j < TM; ++j) ub[j] = lora_chunk(rt, mw0 + 32 * j + lr, k + 8 * lh, rank);
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[i], ub[j], acc[i][j], 0, 0, 0);
+  for (int k0 = 0; k0 < rank; k0 += 16 * S) {
+    LoraRegs<TN, TM, S> r;
+    lora_load(r, rt, rb, k0, rank, nw0, mw0, lane);
+    lora_mfma(acc, r, k0, rank);
   }
 }
 

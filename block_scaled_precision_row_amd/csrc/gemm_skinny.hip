@@ -198,7 +198,7 @@ __device__ __forceinline__ void skinny_lora_tile(const DecArgs& a, float* lred, 
   for (int k0 = 0; k0 < a.rank; k0 += 64) {
     LoraRegs<1, 1, 4> r;
     lora_load(r, rt, rb, k0, a.rank, n0, m0 + 32 * wave, lane);
-    lora_mfma(l, r);
+    lora_mfma(l, r, k0, a.rank);
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) lred[(wave * 16 + e) * 64 + lane] = l[0][0][e];

@@ -227,21 +227,21 @@ void gemm_w4a4_kernel(DecArgs a) {
   if constexpr (LORA) {
     // low-rank adapter: the accumulators start at T' B^T with T' = T / (gx gw) (the down
     // projection divides), so the epilogue's scaling by gx gw leaves y = bf16(base + T B^T).
-    // Its first 32 rank values are loaded alongside the first stage; larger ranks follow.
+    // Its first 64 rank values are loaded alongside the first stage; larger ranks follow.
     const rsrc_t rt = make_rsrc(a.lt, (uint32_t)M * (uint32_t)a.rank * 2u);
     const rsrc_t rb = make_rsrc(a.lb, (uint32_t)N * (uint32_t)a.rank * 2u);
     const int nw0 = n0 + wn * C::WN, mw0 = m0 + wm * C::WM;
-    LoraRegs<TN, TM, 2> lo;
+    LoraRegs<TN, TM, 4> lo;
     lora_load(lo, rt, rb, 0, a.rank, nw0, mw0, lane);
     issue_stage(0);
     // both sets of loads are in flight before anything waits (the scheduler would otherwise
     // hoist the adapter MFMAs, and their wait, above the stage's DMA)
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
-    lora_mfma(acc, lo);
-    for (int k0 = 32; k0 < a.rank; k0 += 32) {
+    lora_mfma(acc, lo, 0, a.rank);
+    for (int k0 = 64; k0 < a.rank; k0 += 64) {
       lora_load(lo, rt, rb, k0, a.rank, nw0, mw0, lane);
-      lora_mfma(acc, lo);
+      lora_mfma(acc, lo, k0, a.rank);
     }
   } else {
     issue_stage(0);

@@ -87,7 +87,7 @@ def summarize(fetch_csv, write_csv):
     total = out["FETCH_SIZE"]["gemm_bytes"] + out["WRITE_SIZE"]["gemm_bytes"]
     algorithmic = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + M * N * 2
     sha = source_hash()
-    res = {"kernel": "gemm_w4a4_kernel<256, 256>", "shape": "4096x12288x3072", "bytes_per_launch": round(total),
+    res = {"kernel": "gemm_w4a4_kernel<256, 256, false> (no adapter)", "shape": "4096x12288x3072", "bytes_per_launch": round(total),
            "algorithmic_bytes_per_launch": algorithmic, "counters": out, "source_sha256": sha,
            "copy_bytes": COPY_BYTES}
     os.makedirs(os.path.dirname(OUT), exist_ok=True)

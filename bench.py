@@ -41,6 +41,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def warm_gpu(fn, ms=60.0):
+    """Call fn back to back until at least `ms` of GPU time has passed: the clocks need tens of
+    milliseconds of sustained load to settle, and the GPU idles while inputs are generated."""
+    import torch
+
+    done, n = 0.0, 4
+    while done < ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        done += e0.elapsed_time(e1)
+        n *= 2
+
+
 def measured_traffic():
     """HBM bytes per launch of the dominant kernel from the committed counter summary, if current."""
     try:
@@ -117,6 +134,7 @@ def quantized_output_comparison(L, dev, y3, gemm_args, operands):
     for name, calls in variants.items():
         for fn, a in calls:
             fn(*a)
+        warm_gpu(lambda: [fn(*a) for fn, a in calls])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(10):
@@ -153,6 +171,7 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
             st = fn(*a)
             if st != 0:
                 raise L.BsqError(fn.__name__, st)
+        warm_gpu(lambda: (plain[0](*plain[1]), call[0](*call[1])))
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(pairs)]
         for e in ev:
             e[0].record()
@@ -169,6 +188,7 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
         st = fn(*a)
         if st != 0:
             raise L.BsqError(fn.__name__, st)
+        warm_gpu(lambda: fn(*a), ms=20.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -234,6 +254,8 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
         return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
 
     def timed(calls, iters=24, warm=3):
+        it = iter(range(1 << 30))
+        warm_gpu(lambda: calls[next(it) % len(calls)](), ms=30.0)
         for i in range(warm):
             calls[i % len(calls)]()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -319,7 +341,7 @@ def joint_block_sweep(L, syn, dev, reps=5):
           for k in sorted({kk for _, _, kk in syn.JOINT_GEMMS})}
 
     def timed(fn):
-        fn()
+        warm_gpu(fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -382,8 +404,11 @@ def joint_block_sweep(L, syn, dev, reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU needs 30-50 ms of sustained load to reach its steady clocks (a W4A4 GEMM measured
+    # 430 us on the first call, 280 us after 7 ms, 236 us from 50 ms on): the default warmup is
+    # about 0.2 s of steps, so that the timed steps see the steady state
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=600)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-small-m", action="store_true", help="skip the few-token sweep")
     ap.add_argument("--no-joint", action="store_true", help="skip the 16384-token joint-block shapes")

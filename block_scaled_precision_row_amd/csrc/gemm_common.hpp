@@ -140,6 +140,9 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TN][TM], uint16_t* 
 
 // Copy a bf16 output tile [BM][BN] (rows TROW bytes apart in LDS) to Y in
 // 16-byte row chunks: consecutive threads write consecutive chunks of a row.
+// Plain (cached) stores: the L2 absorbs a tile's burst of writes and drains it
+// while the next tiles compute; non-temporal stores, which go straight on to
+// memory, measured 11 % slower on the 4096x12288x3072 W4A4 GEMM.
 template <int BM, int BN, int TROW>
 __device__ __forceinline__ void store_tile_rows(const uint8_t* tile, uint16_t* __restrict__ y, int64_t ldy, int M,
                                                 int N, int m0, int n0, int tid) {
@@ -152,7 +155,7 @@ __device__ __forceinline__ void store_tile_rows(const uint8_t* tile, uint16_t* _
     const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * TROW + c * 16);
     uint16_t* dst = y + (int64_t)m * ldy + n;
     if (n + 8 <= N && vec_ok) {
-      store_stream(reinterpret_cast<uint4*>(dst), v);
+      *reinterpret_cast<uint4*>(dst) = v;
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -249,12 +252,12 @@ __device__ __forceinline__ void lora_mfma(v16f (&acc)[TN][TM], const LoraRegs<TN
 }
 
 // acc[i][j] (n-tile i at n = nw0 + 32 i, m-tile j at m = mw0 + 32 j) += T[m][:] . B[n][:],
-// 64 rank values per batch of loads (32 for the largest wave tiles, whose accumulators leave
+// 64 rank values per batch of loads (32 for the larger wave tiles, whose accumulators leave
 // fewer registers)
 template <int TN, int TM>
 __device__ __forceinline__ void lora_update(v16f (&acc)[TN][TM], const uint16_t* lt, const uint16_t* lb, int rank,
                                             int M, int N, int nw0, int mw0, int lane) {
-  constexpr int S = TN + TM >= 8 ? 2 : 4;
+  constexpr int S = TN + TM >= 7 ? 2 : 4;
   const rsrc_t rt = make_rsrc(lt, (uint32_t)M * (uint32_t)rank * 2u);
   const rsrc_t rb = make_rsrc(lb, (uint32_t)N * (uint32_t)rank * 2u);
   for (int k0 = 0; k0 < rank; k0 += 16 * S) {

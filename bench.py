@@ -236,6 +236,47 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
     return out
 
 
+def vendor_gemm_context(dev, reps=20):
+    """Context, not part of the path: the ROCm vendor library's GEMMs (hipBLASLt, through
+    torch.matmul in bf16 and torch._scaled_mm with row-wise fp32 scales in E4M3) on the two step
+    shapes with random operands, warmed like everything else; us per call (mean of `reps`)."""
+    import torch
+
+    out = {}
+
+    def t(fn):
+        warm_gpu(fn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    for Mv, Nv, Kv in ((M, N_FP4, K), (M, N_FP8, K)):
+        x = torch.randn((Mv, Kv), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        w = (torch.randn((Nv, Kv), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        wt = w.t().contiguous()
+        name = "%dx%dx%d" % (Mv, Nv, Kv)
+        us = t(lambda: torch.matmul(x, wt))
+        out["bf16_matmul_" + name] = {"us": round(us, 1), "tflops": round(2.0 * Mv * Nv * Kv / us / 1e6, 1)}
+        try:
+            xf, wf = x.to(torch.float8_e4m3fn), w.to(torch.float8_e4m3fn)
+            sa = torch.ones((Mv, 1), device=dev)
+            sb = torch.ones((1, Nv), device=dev)
+            us = t(lambda: torch._scaled_mm(xf, wf.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16))
+            out["fp8_rowwise_scaled_mm_" + name] = {"us": round(us, 1),
+                                                    "tflops": round(2.0 * Mv * Nv * Kv / us / 1e6, 1)}
+        except (RuntimeError, TypeError) as e:
+            out["fp8_rowwise_scaled_mm_" + name] = "unavailable: %s" % str(e)[:80]
+        del x, w, wt
+    out["note"] = "vendor library on plain bf16 / E4M3 operands, for context only (not the nvfp4 path)"
+    return out
+
+
 def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)):
     """Few-token GEMMs (K = 3072), all four schemes, with cold weights.
 
@@ -414,11 +455,13 @@ def main():
     ap.add_argument("--no-joint", action="store_true", help="skip the 16384-token joint-block shapes")
     ap.add_argument("--no-quant-out", action="store_true", help="skip the quantized-output comparison")
     ap.add_argument("--no-lora", action="store_true", help="skip the LoRA side-path measurement")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the vendor-library GEMM context")
     ap.add_argument("--only-step", action="store_true",
                     help="time the step only (no CPU baseline, no extra measurements), e.g. under a profiler")
     args = ap.parse_args()
     if args.only_step:
         args.no_cpu_baseline = args.no_small_m = args.no_joint = args.no_quant_out = args.no_lora = True
+        args.no_vendor = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (requested %d)" % args.gpus,
               file=sys.stderr)
@@ -575,6 +618,9 @@ def main():
         log("quantized-output comparison")
         result["w4a4_quantized_output_us"] = quantized_output_comparison(
             L, dev, y3, seq[DOM][1], (x3q, x3s, gx3, w3q, w3s, g3))
+    if not args.no_vendor:
+        log("vendor-library GEMM context")
+        result["vendor_gemm_context"] = vendor_gemm_context(dev)
     if not args.no_lora:
         log("LoRA side path")
         result["lora"] = lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3)

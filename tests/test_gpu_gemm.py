@@ -212,3 +212,15 @@ def test_w4a4_several_tiles_per_workgroup(M, N, K):
     x = syn.normal_bf16((M, K), 53, M)
     w = syn.normal_bf16((N, K), 53, 3000 + N, sigma=0.02)
     run_nvfp4(x, w, sample=96, what="nvfp4 rounds %dx%dx%d" % (M, N, K))
+
+
+# fp8r grids of 512 or more 256 x 256 tiles run the square tile: ragged M and N tails, K of
+# several 128-deep stages and one with a half stage (K % 128 == 64)
+SQUARE_FP8_SHAPES = [(6100, 5400, 512), (8192, 4096, 320), (16384, 9216, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", SQUARE_FP8_SHAPES)
+def test_fp8r_square_tiles(M, N, K):
+    x = syn.normal_bf16((M, K), 56, M, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 56, 6000 + N, sigma=0.02)
+    run_fp8r(x, w, sample=96, what="fp8r square tiles %dx%dx%d" % (M, N, K))

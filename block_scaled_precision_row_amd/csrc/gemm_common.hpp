@@ -140,14 +140,38 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[TN][TM], uint16_t* 
 
 // Copy a bf16 output tile [BM][BN] (rows TROW bytes apart in LDS) to Y in
 // 16-byte row chunks: consecutive threads write consecutive chunks of a row.
-// Plain (cached) stores: the L2 absorbs a tile's burst of writes and drains it
-// while the next tiles compute; non-temporal stores, which go straight on to
-// memory, measured 11 % slower on the 4096x12288x3072 W4A4 GEMM.
+// Whole tiles use non-temporal stores when `stream` is set (stream_output():
+// outputs that would push the operands out of the last-level cache), plain
+// cached stores otherwise.
 template <int BM, int BN, int TROW>
 __device__ __forceinline__ void store_tile_rows(const uint8_t* tile, uint16_t* __restrict__ y, int64_t ldy, int M,
-                                                int N, int m0, int n0, int tid) {
+                                                int N, int m0, int n0, int tid, bool stream) {
   constexpr int CPR = BN / 8;  // 16-byte chunks per row
   const bool vec_ok = (ldy & 7) == 0;
+  constexpr int IT = BM * CPR / kThreads;
+  if (BM * CPR % kThreads == 0 && IT % 8 == 0 && vec_ok && m0 + BM <= M && n0 + BN <= N) {
+    // Whole tile inside the matrix: read eight chunks from LDS before storing them, so the
+    // LDS latency is paid once per eight stores instead of once per store.
+#pragma unroll
+    for (int i0 = 0; i0 < IT; i0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = tid + (i0 + u) * kThreads, ml = idx / CPR, c = idx - ml * CPR;
+        v[u] = *reinterpret_cast<const uint4*>(tile + ml * TROW + c * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = tid + (i0 + u) * kThreads, ml = idx / CPR, c = idx - ml * CPR;
+        uint4* dst = reinterpret_cast<uint4*>(y + (int64_t)(m0 + ml) * ldy + n0 + 8 * c);
+        if (stream)
+          store_stream(dst, v[u]);
+        else
+          *dst = v[u];
+      }
+    }
+    return;
+  }
   for (int idx = tid; idx < BM * CPR; idx += kThreads) {
     const int ml = idx / CPR, c = idx - ml * CPR;
     const int m = m0 + ml, n = n0 + 8 * c;

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                      const uint8_t* __restrict__ w, const float* __restrict__ sw,
                      uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, const uint16_t* lt,
-                     const uint16_t* lb, int rank) {
+                     const uint16_t* lb, int rank, int stream_y) {
   using C = Cfg<BM, BN, NS>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -197,7 +197,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     }
   }
   __syncthreads();
-  store_tile_rows<BM, BN, C::TROW>(smem, y, ldy, M, N, m0, n0, tid);
+  store_tile_rows<BM, BN, C::TROW>(smem, y, ldy, M, N, m0, n0, tid, stream_y != 0);
 }
 
 template <int BM, int BN, int NS>
@@ -208,10 +208,10 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
   constexpr bool kAdapter = !(BM == 256 && BN == 256);  // the 256 x 256 tile never carries one (launch_gemm_fp8)
   if (kAdapter && lt)
     hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
-                       ldy, (int)M, (int)N, (int)K, lt, lb, rank);
+                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, (int)stream_output((M + N) * K, M, N));
   else
     hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
-                       ldy, (int)M, (int)N, (int)K, lt, lb, rank);
+                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, (int)stream_output((M + N) * K, M, N));
   return hipGetLastError();
 }
 

@@ -297,7 +297,7 @@ void gemm_w4a4_kernel(DecArgs a) {
     }
   }
   __syncthreads();
-  if (a.y) store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid);
+  if (a.y) store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid, a.stream_y != 0);
   // optionally the nvfp4 encoding of Y for the next linear ("BFL (fp8r / nvfp4)": every
   // quantized linear quantizes its input at run time); its 16-blocks run along this N, inside
   // the tile
@@ -319,7 +319,9 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
 bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kStageK == 0; }
 bool lora_pre_scaled_w4a4(const DecArgs& a) { return gemm_w4a4_supported(a); }
 
-hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s) {
+hipError_t launch_gemm_w4a4(const DecArgs& args, hipStream_t s) {
+  DecArgs a = args;
+  a.stream_y = stream_output((a.M + a.N) * (a.K / 2 + a.K / 16), a.M, a.N);
   const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if (t256 >= 192) return run<256, 256>(a, s);
   return run<128, 128>(a, s);

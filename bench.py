@@ -58,6 +58,38 @@ def warm_gpu(fn, ms=60.0):
         n *= 2
 
 
+_SPACER = {}
+
+
+def queue_ahead(ms=1.5):
+    """Give the GPU about `ms` of work right before a timed region, so that every timed launch is
+    already queued when the GPU reaches it: the events then time the GPU rather than the rate at
+    which Python issues launches (a launch through ctypes costs several microseconds of host time,
+    as much as the few-token kernels timed here). The work is a bf16 matmul. Used only for short,
+    memory-bound kernels: the matmul leaves the clocks where a power-hungry GEMM runs them, which
+    slowed a following fp8 GEMM of 38 us by a fifth."""
+    import torch
+
+    if "n" not in _SPACER:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(3)
+        a = torch.randn((4096, 4096), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        b = torch.randn((4096, 4096), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        c = torch.empty((4096, 4096), device="cuda", dtype=torch.bfloat16)
+        mm = lambda: torch.matmul(a, b, out=c)
+        warm_gpu(mm, ms=20.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(8):
+            mm()
+        e1.record()
+        torch.cuda.synchronize()
+        _SPACER["mm"] = mm
+        _SPACER["n"] = max(1, int(ms / (e0.elapsed_time(e1) / 8)) + 1)
+    for _ in range(_SPACER["n"]):
+        _SPACER["mm"]()
+
+
 def measured_traffic():
     """HBM bytes per launch of the dominant kernel from the committed counter summary, if current."""
     try:
@@ -153,7 +185,8 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
     synthetic adapter of several ranks (down projection + GEMM with the up projection fused),
     warm, in us: medians of 20 alternating pairs of calls; plus the down projection alone (mean
     of `reps` back-to-back calls) and its rate over the bytes it must move (X read once, A read,
-    T written). Also a 16-token nvfp4 linear."""
+    T written). Also a 16-token nvfp4 linear, whose short calls are queued behind other GPU work
+    (queue_ahead) so that the host's launch cost is not timed."""
     import torch
 
     lib = L.lib
@@ -163,7 +196,7 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
     def up_bf16(bits):
         return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
 
-    def paired(plain, call, pairs=20):
+    def paired(plain, call, pairs=20, ahead=False):
         """median us per call of the plain linear and of the linear with the adapter, timed in
         alternating pairs (each call between two events on the stream), so that clock and
         power drift affect both alike"""
@@ -173,6 +206,8 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
                 raise L.BsqError(fn.__name__, st)
         warm_gpu(lambda: (plain[0](*plain[1]), call[0](*call[1])))
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(pairs)]
+        if ahead:
+            queue_ahead()
         for e in ev:
             e[0].record()
             plain[0](*plain[1])
@@ -184,12 +219,14 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
         tl = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
         return tp[pairs // 2], tl[pairs // 2]
 
-    def timed(fn, a):
+    def timed(fn, a, ahead=False):
         st = fn(*a)
         if st != 0:
             raise L.BsqError(fn.__name__, st)
         warm_gpu(lambda: fn(*a), ms=20.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if ahead:
+            queue_ahead()
         e0.record()
         for _ in range(reps):
             fn(*a)
@@ -219,11 +256,12 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
             else:
                 call = (lib.bsq_gemm_fp8r_lora, (P(x), K, P(w2q), P(w2s), P(da), P(db), rank, 1.0, P(y), N, Mx, N,
                                                  K, 0, P(ws), ws.numel(), stream))
-            plain_us, us = paired(plain, call)
+            plain_us, us = paired(plain, call, ahead=Mx <= 64)
             t = torch.empty((Mx, rank), dtype=torch.bfloat16, device=dev)
             dws = torch.empty((max(1, lib.bsq_lora_down_workspace_bytes(Mx, K, rank)),), dtype=torch.uint8,
                               device=dev)
-            down_us = timed(lib.bsq_lora_down, (P(x), K, P(da), Mx, K, rank, 1.0, P(t), P(dws), dws.numel(), stream))
+            down_us = timed(lib.bsq_lora_down, (P(x), K, P(da), Mx, K, rank, 1.0, P(t), P(dws), dws.numel(), stream),
+                            ahead=Mx <= 64)
             down_bytes = Mx * K * 2 + rank * K * 2 + Mx * rank * 2
             entry["ranks"][str(rank)] = {
                 "plain_us": round(plain_us, 2), "us": round(us, 2),
@@ -300,6 +338,7 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
         for i in range(warm):
             calls[i % len(calls)]()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead()
         e0.record()
         for i in range(iters):
             calls[i % len(calls)]()
@@ -356,7 +395,8 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
         del W4, W8
         torch.cuda.empty_cache()
     return {"K": K, "cold": True, "rows": rows,
-            "note": "kernel time per call from events around 24 back-to-back launches (weights rotated over > 600 MB); "
+            "note": "kernel time per call from events around 24 back-to-back launches (weights rotated over > 600 MB), "
+                    "queued behind ~1.5 ms of other GPU work so that host launch cost is not timed; "
                     "hbm_frac = (weights + activations + Y bytes) / time / 8 TB/s"}
 
 

@@ -225,10 +225,21 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w,
   // the L2 -> LDS path that bounds this kernel (measured 7-11 % faster at 16384 tokens); with an
   // adapter the 256 x 192 tile is kept (the adapter epilogue does not fit the square tile's
   // registers).
+  //
+  // Below that, a grid of few tiles leaves compute units idle, and each busy unit is bound by
+  // the latency of its own loads (three stages in flight); more, smaller tiles keep more loads
+  // in flight across the chip. So the smallest tile whose grid still fits one round on the 256
+  // units is taken: 64 x 64 (its 64 KB of LDS lets two workgroups share a unit), then 64 tokens
+  // x 128 weight rows, else 128 x 128. Measured at K = 3072: 512 x 3072 14.8 -> 10.0 us, 320 x
+  // 3072 14.2 -> 8.4 us, 512 x 3072 x 12288 46.4 -> 33.8 us; every tile shape gives the same bits
+  // (the same MFMA sequence per output).
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (t256 >= 512 && !lt) return run<256, 256, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
   if (t192 >= 192) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64), t64x128 = ((M + 63) / 64) * ((N + 127) / 128);
+  if (t64 <= 256) return run<64, 64, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  if (t64x128 <= 256) return run<64, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
   return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
 }
 

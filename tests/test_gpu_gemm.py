@@ -224,3 +224,18 @@ def test_fp8r_square_tiles(M, N, K):
     x = syn.normal_bf16((M, K), 56, M, outlier_frac=0.01)
     w = syn.normal_bf16((N, K), 56, 6000 + N, sigma=0.02)
     run_fp8r(x, w, sample=96, what="fp8r square tiles %dx%dx%d" % (M, N, K))
+
+
+# Small grids (a few hundred tokens) run 64 x 64 or 64 x 128 tiles: ragged M and N tails, two
+# workgroups' worth of tokens, one 64-token block with the ragged 65th row, and the 512-token
+# weight-streaming shape
+SMALL_GRID_SHAPES = [(300, 520, 1024), (65, 12288, 512), (200, 3000, 768), (512, 3072, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_GRID_SHAPES)
+def test_small_grid_tiles(M, N, K):
+    x = syn.normal_bf16((M, K), 60, M + N, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 60, 8000 + N, sigma=0.02)
+    big = M * N > 1 << 20
+    run_fp8r(x, w, sample=64 if big else None, what="fp8r small grid %dx%dx%d" % (M, N, K))
+    run_nvfp4(x, w, sample=64 if big else None, what="nvfp4 small grid %dx%dx%d" % (M, N, K))

@@ -80,17 +80,18 @@ bsq_status check_gemm_common(const uint16_t* x, int64_t ldx, const void* w, uint
 // and walk K serially; with more rows the tiled kernels' operand reuse wins. Per scheme: the
 // skinny kernel always runs up to `always` rows, and up to `most` rows while the tiled
 // kernel would have fewer than 64 tiles of 128 x 128 (crossovers measured on MI355X with
-// cold weights, K = 3072, N = 3072 and 12288; for W4A4 and W8A8 against the tiled kernels'
-// small-grid tiles: at N = 12288 those win from 32 tokens, at N = 3072 the W8A8 one from 192).
+// cold weights, K = 3072, N = 3072 and 12288, against the tiled kernels' small-grid tiles:
+// at N = 12288 those win from 32 tokens (W4A4, W8A8) or 48 (W4A16, W8A16), at N = 3072 from
+// 192 tokens).
 struct SkinnyRule {
   int64_t always, most;
 };
 SkinnyRule skinny_rule(bsq::DecMode mode) {
   switch (mode) {
     case bsq::kW4A4: return {16, 128};
-    case bsq::kW4A16: return {128, 256};
+    case bsq::kW4A16: return {32, 128};
     case bsq::kW8A8: return {16, 128};
-    default: return {128, 256};  // W8A16
+    default: return {32, 128};  // W8A16
   }
 }
 bool route_skinny(bsq::DecMode mode, const bsq::DecArgs& a) {

@@ -83,6 +83,9 @@ struct DecArgs {
 // whether the adapter's T must be divided by gx * gw for this W4A4 launch (tiled kernel)
 bool lora_pre_scaled_w4a4(const DecArgs& a);
 hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s);
+// W4A16 / W8A16 on the LDS-DMA pipeline with in-register weight decode (tiled shapes)
+bool gemm_a16_supported(DecMode mode, const DecArgs& a);
+hipError_t launch_gemm_a16(DecMode mode, const DecArgs& a, hipStream_t s);
 // W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0
 bool gemm_w4a4_supported(const DecArgs& a);
 hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s);

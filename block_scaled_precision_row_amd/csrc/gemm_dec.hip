@@ -363,8 +363,8 @@ hipError_t pick(const DecArgs& a, hipStream_t s) {
 hipError_t launch_gemm_dec(DecMode mode, const DecArgs& a, hipStream_t s) {
   switch (mode) {
     case kW4A4: return gemm_w4a4_supported(a) ? launch_gemm_w4a4(a, s) : pick<kW4A4>(a, s);
-    case kW4A16: return pick<kW4A16>(a, s);
-    default: return pick<kW8A16>(a, s);
+    case kW4A16: return gemm_a16_supported(mode, a) ? launch_gemm_a16(mode, a, s) : pick<kW4A16>(a, s);
+    default: return gemm_a16_supported(mode, a) ? launch_gemm_a16(mode, a, s) : pick<kW8A16>(a, s);
   }
 }
 

@@ -239,3 +239,18 @@ def test_small_grid_tiles(M, N, K):
     big = M * N > 1 << 20
     run_fp8r(x, w, sample=64 if big else None, what="fp8r small grid %dx%dx%d" % (M, N, K))
     run_nvfp4(x, w, sample=64 if big else None, what="nvfp4 small grid %dx%dx%d" % (M, N, K))
+
+
+# Weight-only (W4A16, W8A16) tiled kernel: the large tiles (256 tokens x 128 weight rows for
+# nvfp4, 128 x 256 for E4M3) with ragged M and N, and a K whose last 128-deep stage is half
+# full (the nvfp4 block-scale copies of its second half read as zeros)
+A16_SHAPES = [(2000, 3000, 1024), (300, 700, 2112), (4096, 3072, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", A16_SHAPES)
+def test_weight_only_tiled(M, N, K):
+    x = syn.normal_bf16((M, K), 61, M + N)
+    w = syn.normal_bf16((N, K), 61, 9000 + N, sigma=0.02)
+    sample = 64 if M * N > 1 << 20 else None
+    run_fp8r(x, w, weight_only=True, sample=sample, what="w8a16 %dx%dx%d" % (M, N, K))
+    run_nvfp4(x, w, weight_only=True, sample=sample, what="w4a16 %dx%dx%d" % (M, N, K))

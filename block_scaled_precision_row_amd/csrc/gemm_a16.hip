@@ -204,8 +204,8 @@ void gemm_a16_kernel(DecArgs a) {
   decode(r0, 0, 0, d0);
 
   // Stage s sits in buffer s % 2 and stage s + 1 in the other. Each K step's MFMAs run while
-  // the next step's X chunks are read and its W fragments decoded. After the last step's MFMAs
-  // are issued, every wave waits for stage s + 1, the barrier publishes it (and ends all reads
+  // the next step's X chunks are read and its W fragments decoded. Once the last step's chunks
+  // are read, every wave waits for stage s + 1, the barrier publishes it (and ends all reads
   // of stage s), and stage s + 2 is fetched into buffer s % 2.
   for (int s = 0; s < nk; ++s) {
     const uint8_t* cur = smem + (s & 1) * C::STAGE;
@@ -232,7 +232,9 @@ void gemm_a16_kernel(DecArgs a) {
     read_x(cur, 7, x1);
     decode(r1, 1, 3, d1);
     mfmas(d0, x0);
-    mfmas(d1, x1);
+    // every read of stage s is issued: the barrier (and the refill of its buffer) go between
+    // the last two steps' MFMAs, which run on while the wave waits and the next stage's first
+    // operands are read
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     __syncthreads();
@@ -240,6 +242,8 @@ void gemm_a16_kernel(DecArgs a) {
     read_sc(nxt);
     read_w(nxt, 0, r0);
     read_x(nxt, 0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(d1, x1);
     decode(r0, 0, 0, d0);
   }
 

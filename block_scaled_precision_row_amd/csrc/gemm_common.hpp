@@ -8,11 +8,13 @@
 // accumulator of a lane holds one token m (lane % 32) and, per 4-register
 // group g, the four consecutive outputs n = 8 g + 4 (lane / 32) + (0..3).
 //
-// K is walked in stages of 64 values. Every stage of every operand lands in
-// LDS untouched (packed codes stay packed) through buffer_load ... lds, in a
-// ring of NSTAGE buffers so that several stages are in flight while the
-// MFMAs work on an older one. Operands are read from LDS into registers one
-// stage ahead and, where needed, decoded there right before the MFMA.
+// K is walked in stages (64 to 256 values deep, per kernel). Every stage of
+// every operand lands in LDS untouched (packed codes stay packed) through
+// buffer_load ... lds, in a ring of stage buffers so that the next stages are
+// in flight while the MFMAs work on an older one. Operands are read from LDS
+// into registers ahead of their K step and, where needed, decoded there right
+// before the MFMA. Tile sizes (BM tokens x BN weight rows) are chosen per
+// launch from the grid they give on the 256 compute units.
 #pragma once
 
 #include "bsq_device.hpp"
@@ -21,7 +23,7 @@ namespace bsq {
 namespace gemm {
 
 constexpr int kThreads = 256;
-constexpr int kKS = 64;                  // K values per stage
+constexpr int kKS = 64;                  // default K values per stage of a Region
 constexpr int kOutOfRange = 0x40000000;  // buffer offset beyond any tile's records
 
 // s_waitcnt with vmcnt <= n (n in 0..63), lgkmcnt and expcnt unconstrained (gfx9 encoding)

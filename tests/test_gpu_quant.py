@@ -83,7 +83,7 @@ def test_fp8r_every_bf16_value_at_unit_scale():
     _check_fp8r(x)
 
 
-@pytest.mark.parametrize("M,K,pad", [(77, 96, 0), (5, 32, 8), (64, 4096, 0), (9, 8192, 24), (3, 16384, 0)])
+@pytest.mark.parametrize("M,K,pad", [(77, 96, 0), (5, 32, 8), (64, 4096, 0), (9, 8192, 24), (3, 16384, 0), (2, 20480, 8)])
 def test_fp8r_varied_rows(M, K, pad):
     _check_fp8r(_varied_rows(M, K, M * 7 + K), pad)
 

@@ -244,7 +244,8 @@ def test_small_grid_tiles(M, N, K):
 # Weight-only (W4A16, W8A16) tiled kernel: the large tiles (256 tokens x 128 weight rows for
 # nvfp4, 128 x 256 for E4M3) with ragged M and N, and a K whose last 128-deep stage is half
 # full (the nvfp4 block-scale copies of its second half read as zeros)
-A16_SHAPES = [(2000, 3000, 1024), (300, 700, 2112), (4096, 3072, 3072)]
+A16_SHAPES = [(2000, 3000, 1024), (300, 700, 2112), (4096, 3072, 3072),
+              (300, 200, 64), (257, 136, 32)]  # K below one 128-deep stage (K = 32: W8A16 only here)
 
 
 @pytest.mark.parametrize("M,N,K", A16_SHAPES)

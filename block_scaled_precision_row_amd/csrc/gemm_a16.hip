@@ -307,7 +307,7 @@ template <int MODE>
 hipError_t pick(const DecArgs& args, hipStream_t s) {
   constexpr bool FP4 = MODE == kW4A16;
   DecArgs a = args;
-  a.stream_y = stream_output((a.M + a.N) * (FP4 ? a.K / 2 + a.K / 16 : a.K) + a.M * a.K, a.M, a.N);
+  a.stream_y = stream_output(a.M * 2 * a.K + a.N * (FP4 ? a.K / 2 + a.K / 16 : a.K), a.M, a.N);  // bf16 X + W
   // The large tile once its grid covers most of the 256 compute units (nvfp4: 256 tokens x 128
   // weight rows, which keeps two W fragments to decode per wave and K step; E4M3, cheap to
   // decode: 128 x 256); below that the smallest tile whose grid fits one round, as in the other

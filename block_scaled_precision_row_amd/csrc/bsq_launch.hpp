@@ -32,6 +32,15 @@ inline bool stream_output(int64_t operand_bytes, int64_t M, int64_t N) {
   return bytes > 1.1 * 256.0 * 1024.0 * 1024.0;
 }
 
+// Expected time of a grid of BM x BN tiles, in units of `tile_cost` (one tile's run time):
+// the tiles run in ceil(tiles / 256) rounds on the 256 compute units (one workgroup of a
+// large tile per unit), and a partial last round takes as long as a full one -- the 264
+// tiles of 256 x 192 at 3072 x 4096 take twice the time of 256 tiles.
+inline int64_t rounds_cost(int64_t M, int64_t N, int BM, int BN, int tile_cost) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  return (tiles + 255) / 256 * tile_cost;
+}
+
 // W8A8: y = bf16((sum e4m3(xq) e4m3(w)) * sx[m] * sw[n])
 // (with lt != nullptr, plus the adapter term T B^T; see DecArgs)
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,

@@ -220,26 +220,28 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                            uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,
                            const uint16_t* lb, int rank, hipStream_t s) {
-  // Pick the tile whose grid best fills the 256 compute units. Large grids (two or more rounds
-  // of 256 x 256 tiles) take the square tile: it moves 12 % fewer operand bytes per flop through
-  // the L2 -> LDS path that bounds this kernel (measured 7-11 % faster at 16384 tokens); with an
-  // adapter the 256 x 192 tile is kept (the adapter epilogue does not fit the square tile's
-  // registers).
+  // A grid of few tiles leaves compute units idle, and each busy unit is bound by the latency
+  // of its own loads (three stages in flight); more, smaller tiles keep more loads in flight
+  // across the chip. So while its grid fits one round on the 256 units, the smallest tile is
+  // taken: 64 x 64 (its 64 KB of LDS lets two workgroups share a unit), then 64 tokens x 128
+  // weight rows. Measured at K = 3072: 512 x 3072 14.8 -> 10.0 us, 320 x 3072 14.2 -> 8.4 us,
+  // 512 x 3072 x 12288 46.4 -> 33.8 us.
   //
-  // Below that, a grid of few tiles leaves compute units idle, and each busy unit is bound by
-  // the latency of its own loads (three stages in flight); more, smaller tiles keep more loads
-  // in flight across the chip. So the smallest tile whose grid still fits one round on the 256
-  // units is taken: 64 x 64 (its 64 KB of LDS lets two workgroups share a unit), then 64 tokens
-  // x 128 weight rows, else 128 x 128. Measured at K = 3072: 512 x 3072 14.8 -> 10.0 us, 320 x
-  // 3072 14.2 -> 8.4 us, 512 x 3072 x 12288 46.4 -> 33.8 us; every tile shape gives the same bits
-  // (the same MFMA sequence per output).
-  const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 512 && !lt) return run<256, 256, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
-  if (t192 >= 192) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  // Larger grids take the tile of least expected time over whole rounds, with per-tile times
+  // measured at K = 3072 with every unit busy: 256 x 256 46 us, 256 x 192 36 us, 128 x 128
+  // 15.5 us. The square tile moves 12 % fewer operand bytes per flop through the L2 -> LDS
+  // path that bounds this kernel, so it wins when the rounds come out even (16384 x 3072:
+  // 7-11 % faster); the rounds decide elsewhere -- 3072 x 4096 78 -> 45.5 us on 256 x 256,
+  // 3072 x 12288 131 -> 107 us on 256 x 192, 1024 x 3072 22 -> 14.7 us on 128 x 128. With an
+  // adapter the square tile is left out (its epilogue does not fit the square tile's
+  // registers). Every tile shape gives the same bits (the same MFMA sequence per output).
   const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64), t64x128 = ((M + 63) / 64) * ((N + 127) / 128);
   if (t64 <= 256) return run<64, 64, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
   if (t64x128 <= 256) return run<64, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  const int64_t c256 = lt ? INT64_MAX : rounds_cost(M, N, 256, 256, 92);
+  const int64_t c192 = rounds_cost(M, N, 256, 192, 72), c128 = rounds_cost(M, N, 128, 128, 31);
+  if (c256 <= c192 && c256 <= c128) return run<256, 256, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  if (c192 <= c128) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
   return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
 }
 

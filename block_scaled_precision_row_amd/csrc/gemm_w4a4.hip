@@ -322,16 +322,24 @@ bool lora_pre_scaled_w4a4(const DecArgs& a) { return gemm_w4a4_supported(a); }
 hipError_t launch_gemm_w4a4(const DecArgs& args, hipStream_t s) {
   DecArgs a = args;
   a.stream_y = stream_output((a.M + a.N) * (a.K / 2 + a.K / 16), a.M, a.N);
-  // The 256 x 256 tile once its grid covers most of the 256 compute units; below that, the
-  // smallest tile whose grid still fits one round on them (64 x 64, then 64 tokens x 128 weight
-  // rows, else 128 x 128): a grid of few large tiles leaves units idle while each busy one waits
-  // on its own loads. Measured at K = 3072: 512 x 3072 26.6 -> 19.2 us, 256 x 3072 27 -> 13.3 us,
-  // 64 x 12288 29 -> 14 us, 512 x 3072 x 12288 88 -> 64 us; every tile shape gives the same bits.
-  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (t256 >= 192) return run<256, 256>(a, s);
+  // While its grid fits one round on the 256 compute units, the smallest tile (64 x 64, then
+  // 64 tokens x 128 weight rows): a grid of few large tiles leaves units idle while each busy
+  // one waits on its own loads. Measured at K = 3072: 512 x 3072 26.6 -> 19.2 us, 256 x 3072
+  // 27 -> 13.3 us, 64 x 12288 29 -> 14 us, 512 x 3072 x 12288 88 -> 64 us.
+  //
+  // Larger grids take the tile of least expected time over whole rounds, with per-tile times
+  // measured at K = 3072 with every unit busy: 256 x 256 76 us, 256 x 192 60 us, 128 x 128
+  // 26 us (the square tile does the most work per operand byte and per decode, so it wins when
+  // the rounds come out even, as at 4096 x 12288: 230 vs 240 us). Where they do not:
+  // 3072 x 3072 75 -> 53 us and 4096 x 6144 136 -> 122 us on 256 x 192, 2048 x 3072 54 -> 50
+  // us on 128 x 128. Every tile shape gives the same bits.
   const int64_t t64 = ((a.M + 63) / 64) * ((a.N + 63) / 64), t64x128 = ((a.M + 63) / 64) * ((a.N + 127) / 128);
   if (t64 <= 256) return run<64, 64>(a, s);
   if (t64x128 <= 256) return run<64, 128>(a, s);
+  const int64_t c256 = rounds_cost(a.M, a.N, 256, 256, 76), c192 = rounds_cost(a.M, a.N, 256, 192, 60);
+  const int64_t c128 = rounds_cost(a.M, a.N, 128, 128, 26);
+  if (c256 <= c192 && c256 <= c128) return run<256, 256>(a, s);
+  if (c192 <= c128) return run<256, 192>(a, s);
   return run<128, 128>(a, s);
 }
 

@@ -202,8 +202,9 @@ def test_skinny_all_schemes(M, N, K):
     run_nvfp4(x, w, weight_only=True, what="nvfp4-w4a16 " + tag)
 
 
-# W4A4 shapes with more output tiles than compute units, ragged M and N tails, both tile
-# configurations, and both parities of the number of 256-deep K stages per tile.
+# W4A4 shapes with more output tiles than compute units, ragged M and N tails, the 256 x 192
+# tile over two rounds and over one, the 128 x 128 tile (1000 x 5000), and both parities of
+# the number of 256-deep K stages per tile.
 PERSISTENT_SHAPES = [(4100, 4100, 768), (4100, 4100, 1024), (1000, 5000, 512), (4100, 2300, 1024)]
 
 
@@ -214,8 +215,9 @@ def test_w4a4_several_tiles_per_workgroup(M, N, K):
     run_nvfp4(x, w, sample=96, what="nvfp4 rounds %dx%dx%d" % (M, N, K))
 
 
-# fp8r grids of 512 or more 256 x 256 tiles run the square tile: ragged M and N tails, K of
-# several 128-deep stages and one with a half stage (K % 128 == 64)
+# fp8r grids whose 256 x 256 tiles fill whole rounds on the compute units no worse than the
+# other tiles' run the square tile: ragged M and N tails, K of several 128-deep stages and one
+# with a half stage (K % 128 == 64). 6100 x 5400 runs 256 x 192 tiles over three rounds.
 SQUARE_FP8_SHAPES = [(6100, 5400, 512), (8192, 4096, 320), (16384, 9216, 256)]
 
 
@@ -224,6 +226,21 @@ def test_fp8r_square_tiles(M, N, K):
     x = syn.normal_bf16((M, K), 56, M, outlier_frac=0.01)
     w = syn.normal_bf16((N, K), 56, 6000 + N, sigma=0.02)
     run_fp8r(x, w, sample=96, what="fp8r square tiles %dx%dx%d" % (M, N, K))
+
+
+# The large-grid tile choice counts whole rounds of tiles on the 256 compute units: 3100 x
+# 4000 takes 256 x 256 tiles in one round (256 x 192 would need two), 4100 x 4100 takes 256 x
+# 192 tiles in two rounds (256 x 256 and 128 x 128 would need two and five), 1000 x 5000 takes
+# 128 x 128 tiles, on both the fp8r and the W4A4 GEMM; all with ragged M and N tails.
+ROUND_SHAPES = [(3100, 4000, 768), (4100, 4100, 768), (1000, 5000, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", ROUND_SHAPES)
+def test_large_grid_tile_choice(M, N, K):
+    x = syn.normal_bf16((M, K), 57, M + N, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 57, 7000 + N, sigma=0.02)
+    run_fp8r(x, w, sample=96, what="fp8r rounds %dx%dx%d" % (M, N, K))
+    run_nvfp4(x, w, sample=96, what="nvfp4 rounds %dx%dx%d" % (M, N, K))
 
 
 # Small grids (a few hundred tokens) run 64 x 64 or 64 x 128 tiles: ragged M and N tails, two

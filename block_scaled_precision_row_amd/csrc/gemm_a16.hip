@@ -308,16 +308,23 @@ hipError_t pick(const DecArgs& args, hipStream_t s) {
   constexpr bool FP4 = MODE == kW4A16;
   DecArgs a = args;
   a.stream_y = stream_output(a.M * 2 * a.K + a.N * (FP4 ? a.K / 2 + a.K / 16 : a.K), a.M, a.N);  // bf16 X + W
-  // The large tile once its grid covers most of the 256 compute units (nvfp4: 256 tokens x 128
-  // weight rows, which keeps two W fragments to decode per wave and K step; E4M3, cheap to
-  // decode: 128 x 256); below that the smallest tile whose grid fits one round, as in the other
-  // tiled GEMMs.
-  constexpr int LBM = FP4 ? 256 : 128, LBN = FP4 ? 128 : 256;
-  const int64_t tl = ((a.M + LBM - 1) / LBM) * ((a.N + LBN - 1) / LBN);
-  if (tl >= 192) return run<LBM, LBN, MODE>(a, s);
+  // While its grid fits one round on the 256 compute units, the smallest tile, as in the other
+  // tiled GEMMs. Larger grids take the tile of least expected time over whole rounds (a partial
+  // last round costs a full one), with per-tile times measured at K = 3072 with every unit busy:
+  //   nvfp4 256 x 192 75 us, 256 x 128 55 us, 128 x 128 34 us (the widest tile re-reads X for
+  //     the fewest weight rows: 4096 x 12288 333 -> 299 us, 3072 x 3072 105 -> 73 us);
+  //   E4M3 (cheap to decode) 128 x 256 48 us, 128 x 192 39.5 us, 128 x 128 29 us (3072 x 3072
+  //     90 -> 73 us, 4096 x 3072 92 -> 81 us on 128 x 192).
+  // Costs below are those times in half-microseconds for E4M3, microseconds for nvfp4.
   const int64_t t64 = ((a.M + 63) / 64) * ((a.N + 63) / 64), t64x128 = ((a.M + 63) / 64) * ((a.N + 127) / 128);
   if (t64 <= 256) return run<64, 64, MODE>(a, s);
   if (t64x128 <= 256) return run<64, 128, MODE>(a, s);
+  constexpr int LBM = FP4 ? 256 : 128, LBN = FP4 ? 192 : 256, MBM = FP4 ? 256 : 128, MBN = FP4 ? 128 : 192;
+  const int64_t cl = rounds_cost(a.M, a.N, LBM, LBN, FP4 ? 75 : 96);
+  const int64_t cm = rounds_cost(a.M, a.N, MBM, MBN, FP4 ? 55 : 79);
+  const int64_t cs = rounds_cost(a.M, a.N, 128, 128, FP4 ? 34 : 58);
+  if (cl <= cm && cl <= cs) return run<LBM, LBN, MODE>(a, s);
+  if (cm <= cs) return run<MBM, MBN, MODE>(a, s);
   return run<128, 128, MODE>(a, s);
 }
 

@@ -258,10 +258,13 @@ def test_small_grid_tiles(M, N, K):
     run_nvfp4(x, w, sample=64 if big else None, what="nvfp4 small grid %dx%dx%d" % (M, N, K))
 
 
-# Weight-only (W4A16, W8A16) tiled kernel: the large tiles (256 tokens x 128 weight rows for
-# nvfp4, 128 x 256 for E4M3) with ragged M and N, and a K whose last 128-deep stage is half
-# full (the nvfp4 block-scale copies of its second half read as zeros)
-A16_SHAPES = [(2000, 3000, 1024), (300, 700, 2112), (4096, 3072, 3072),
+# Weight-only (W4A16, W8A16) tiled kernel, tiles chosen by whole rounds on the compute units:
+# nvfp4 256 x 128 (2000 x 3000, 2000 x 4000), 256 x 192 (4096 x 3072, 3000 x 3000), E4M3
+# 128 x 192 (2000 x 3000, 4096 x 3072, 3000 x 3000), 128 x 256 (2000 x 4000), both 128 x 128
+# (1000 x 4000) and the small-grid tiles, with ragged M and N, and a K whose last 128-deep
+# stage is half full (the nvfp4 block-scale copies of its second half read as zeros)
+A16_SHAPES = [(2000, 3000, 1024), (300, 700, 2112), (4096, 3072, 3072), (2000, 4000, 1024), (3000, 3000, 1088),
+              (1000, 4000, 1024),
               (300, 200, 64), (257, 136, 32)]  # K below one 128-deep stage (K = 32: W8A16 only here)
 
 

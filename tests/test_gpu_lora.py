@@ -105,7 +105,9 @@ def test_lora_matches_oracle(scheme, weight_only, M, N, K, rank):
              what="%s%s %dx%dx%d r%d" % (scheme, "-wo" if weight_only else "", M, N, K, rank))
 
 
-# 256 x 256 W4A4 and decode tiles, 256 x 192 fp8 tiles: compared on sampled rows
+# Large tiles, compared on sampled rows: 4096 x 3072 runs W4A4, fp8 and W4A16 on 256 x 192 tiles
+# and W8A16 on 128 x 192; 4096 x 4096 runs W4A4 on 256 x 256, fp8 on 128 x 128 (the square
+# fp8 tile takes no adapter), W4A16 on 256 x 128 and W8A16 on 128 x 256
 BIG_SHAPES = [(4096, 3072, 3072, 32), (4096, 4096, 512, 64)]
 
 

@@ -23,7 +23,7 @@ if torch.cuda.is_available():
 SHAPES = [
     (4096, 3072, 3072),  # 256x192 tiles
     (3100, 4000, 768),   # 256x256 tiles, ragged M and N
-    (1000, 5000, 512),   # 128x128 tiles, ragged M and N
+    (1000, 4960, 512),   # 128x128 tiles, ragged M and N
     (300, 512, 512),     # 64x64 tiles, ragged M
     (20, 1024, 512),     # few tokens
     (300, 512, 96),      # K % 256 != 0: GEMM, then the activation quantizer

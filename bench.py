@@ -260,8 +260,10 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
             t = torch.empty((Mx, rank), dtype=torch.bfloat16, device=dev)
             dws = torch.empty((max(1, lib.bsq_lora_down_workspace_bytes(Mx, K, rank)),), dtype=torch.uint8,
                               device=dev)
+            # two short launches per call: queued behind GPU work at every size, so that the
+            # events time the GPU rather than the host's launch rate
             down_us = timed(lib.bsq_lora_down, (P(x), K, P(da), Mx, K, rank, 1.0, P(t), P(dws), dws.numel(), stream),
-                            ahead=Mx <= 64)
+                            ahead=True)
             down_bytes = Mx * K * 2 + rank * K * 2 + Mx * rank * 2
             entry["ranks"][str(rank)] = {
                 "plain_us": round(plain_us, 2), "us": round(us, 2),

@@ -6,7 +6,8 @@ weight-only tiled kernel, the decode-GEMM fallback for K % 256 != 0 or
 K % 64 != 0), so a sweep over M, N and K that crosses those boundaries checks
 every route against the oracle with the same tolerance as test_gpu_gemm.py.
 Shapes stay small enough that the oracle's fp64 products take seconds. A second
-sweep attaches a LoRA adapter of random rank to every scheme.
+sweep attaches a LoRA adapter of random rank to every scheme; a third runs grids of
+several rounds of large tiles (up to about 6000 x 7000), compared on sampled rows.
 """
 import numpy as np
 import pytest
@@ -97,3 +98,28 @@ def test_every_scheme_with_an_adapter_on_a_ragged_shape(M, N, K, rank):
     torch.cuda.synchronize()
     for name, y, base in runs:
         assert_gemm_close(host(y), lora.lora_linear(base, x, a, b, scale), name + " " + tag, extra=extra)
+
+
+def _large_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(700, 6000)), int(rng.integers(900, 7000)), int(rng.choice([256, 512, 768, 1024, 1088, 1536])))
+            for _ in range(n)]
+
+
+LARGE_SHAPES = _large_shapes(8, 20260303)
+
+
+@pytest.mark.parametrize("M,N,K", LARGE_SHAPES)
+def test_every_scheme_on_a_large_ragged_grid(M, N, K):
+    """Grids of several rounds of large tiles, where the launchers choose among 256 x 256, 256 x 192,
+    128 x 128 (fp8r, W4A4) and the weight-only tiles by whole rounds: every scheme against the
+    oracle on sampled rows (the first and last row always among them)."""
+    from tests.test_gpu_gemm import run_fp8r, run_nvfp4
+
+    x = syn.normal_bf16((M, K), 65, M * 7 + N + K, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 65, 9300 + N * 3 + K, sigma=0.02)
+    tag = "%dx%dx%d" % (M, N, K)
+    run_fp8r(x, w, sample=48, what="w8a8 " + tag)
+    run_fp8r(x, w, weight_only=True, sample=48, what="w8a16 " + tag)
+    run_nvfp4(x, w, sample=48, what="w4a4 " + tag)
+    run_nvfp4(x, w, weight_only=True, sample=48, what="w4a16 " + tag)

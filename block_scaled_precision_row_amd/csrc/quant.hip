@@ -173,14 +173,22 @@ __global__ __launch_bounds__(256) void amax_partial(const uint16_t* __restrict__
                                                      int64_t ldx, float* __restrict__ partials) {
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  float a = 0.0f;
+  const int k8 = K >> 3;  // 8-value chunks per row
+  float a = 0.0f, b = 0.0f, c2 = 0.0f, d = 0.0f;
   for (int64_t row = (int64_t)blockIdx.x * 4 + wv; row < M; row += (int64_t)gridDim.x * 4) {
-    const uint16_t* xr = x + row * ldx;
-    for (int c = lane; c < (K >> 3); c += 64) {
-      a = fmaxf(a, absmax8(*reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)));
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * ldx);
+    int c = lane;
+    // four loads in flight per lane (independent maxima), then the row's remainder
+    for (; c + 192 < k8; c += 256) {
+      const uint4 v0 = xr[c], v1 = xr[c + 64], v2 = xr[c + 128], v3 = xr[c + 192];
+      a = fmaxf(a, absmax8(v0));
+      b = fmaxf(b, absmax8(v1));
+      c2 = fmaxf(c2, absmax8(v2));
+      d = fmaxf(d, absmax8(v3));
     }
+    for (; c < k8; c += 64) a = fmaxf(a, absmax8(xr[c]));
   }
-  a = wave_max(a);
+  a = wave_max(fmaxf(fmaxf(a, b), fmaxf(c2, d)));
   if (lane == 0) red[wv] = a;
   __syncthreads();
   if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));

@@ -136,6 +136,22 @@ def test_calibrate_global_scale(shape, seed):
     assert float(host(z)[0]) == 1.0
 
 
+@pytest.mark.parametrize("K", [3072, 2080])
+def test_calibration_sees_every_chunk(K):
+    """The tensor maximum planted in each of the reduction's per-lane streams (four interleaved
+    8-value chunk streams and the row remainder) and in the last row: found every time."""
+    M = 7
+    base = syn.normal_bf16((M, K), 98, K, sigma=0.02)
+    for row, col in ((0, 0), (1, 8 * 64 + 3), (2, 8 * 128 + 5), (3, 8 * 192 + 7), (4, 8 * 256 + 1), (5, K - 1),
+                     (M - 1, K // 2)):
+        x = base.copy()
+        x[row, col] = np.uint16(0xC2F6)  # bf16 -123.0
+        g = L.bsq_calibrate_global_scale(dev_bf16(x))
+        torch.cuda.synchronize()
+        assert host(g).view(np.uint32)[0] == np.float32(quant.calibrate_global_scale(x)).view(np.uint32), (row, col)
+        assert abs(float(host(g)[0]) * 2688.0 - 123.0) < 1e-3
+
+
 @pytest.mark.parametrize("N,K", [(3072, 3072), (12288, 3072), (77, 96), (1, 32)])
 def test_dequant_bf16_bitexact(N, K):
     w = syn.normal_bf16((N, K), syn.SMALL_M, 10 + N % 7, sigma=0.02)

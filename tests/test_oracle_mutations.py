@@ -133,3 +133,60 @@ def test_lora_down_projection_transposed_caught(monkeypatch):
         return lora.scale_f32(scale) * (oc.bf16_to_f64(x_bits) @ am.reshape(am.shape[1], am.shape[0]))
     monkeypatch.setattr(lora, "lora_down", bad)
     _fails(tl.test_merged_weight_identity)
+
+
+# ---- operation order of the quantizers' fp32 steps ---------------------------------
+# The pages fix the formats, not the order of the fp32 steps; these are the plausible
+# other orders, each of which changes codes on scales that are not powers of two.
+
+def test_fp8r_divides_by_row_scale_caught(monkeypatch):
+    def bad(x_bits):
+        x = codec.bf16_to_f64(x_bits)
+        a = np.max(np.abs(x), axis=-1)
+        d = codec.rn32(a / 448.0)
+        v = codec.rn32(x / np.where(d > 0, d, 1.0)[..., None])   # mistake: x / d, not x * fp32(1/d)
+        return codec.encode_e4m3(v), d.astype(np.float32)
+    monkeypatch.setattr(quant, "quantize_fp8r", bad)
+    _fails(tq.test_fp8r_worked_row_with_inexact_reciprocal)
+
+
+def test_nvfp4_scale_from_one_division_caught(monkeypatch):
+    def bad_scales(x_bits, g):
+        x = codec.bf16_to_f64(x_bits)
+        R, K = x.shape
+        g64 = np.float64(np.float32(g))
+        a = np.abs(x.reshape(R, K // 16, 16)).max(axis=-1)
+        sf = codec.encode_e4m3(codec.rn32(a / (6.0 * g64)))        # mistake: a / (6 g) in one step
+        sfv = codec.e4m3_decode(sf)
+        G = codec.rn32(1.0 / g64)
+        r = np.where(sfv > 0, codec.rn32(G / np.where(sfv > 0, sfv, 1.0)), 0.0)
+        return sf, r
+    monkeypatch.setattr(quant, "nvfp4_block_scales", bad_scales)
+    _fails(tq.test_nvfp4_worked_blocks_with_inexact_global_reciprocal)
+
+
+def test_nvfp4_multiplier_from_scale_times_global_caught(monkeypatch):
+    real = quant.nvfp4_block_scales
+
+    def bad_scales(x_bits, g):
+        sf, _ = real(x_bits, g)
+        sfv = codec.e4m3_decode(sf)
+        sg = codec.rn32(sfv * np.float64(np.float32(g)))
+        r = np.where(sfv > 0, codec.rn32(1.0 / np.where(sfv > 0, sg, 1.0)), 0.0)   # mistake: 1 / (sf g)
+        return sf, r
+    monkeypatch.setattr(quant, "nvfp4_block_scales", bad_scales)
+    _fails(tq.test_nvfp4_worked_blocks_with_inexact_global_reciprocal)
+
+
+def test_nvfp4_both_steps_by_division_caught(monkeypatch):
+    def bad_scales(x_bits, g):
+        x = codec.bf16_to_f64(x_bits)
+        R, K = x.shape
+        g64 = np.float64(np.float32(g))
+        a = np.abs(x.reshape(R, K // 16, 16)).max(axis=-1)
+        sf = codec.encode_e4m3(codec.rn32(a / (6.0 * g64)))
+        sfv = codec.e4m3_decode(sf)
+        r = np.where(sfv > 0, codec.rn32(1.0 / np.where(sfv > 0, sfv * g64, 1.0)), 0.0)
+        return sf, r
+    monkeypatch.setattr(quant, "nvfp4_block_scales", bad_scales)
+    _fails(tq.test_nvfp4_worked_blocks_with_inexact_global_reciprocal)

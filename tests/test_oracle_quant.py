@@ -47,6 +47,16 @@ def test_fp8r_worked_row():
     assert np.array_equal(q[0], codes)
 
 
+def test_fp8r_worked_row_with_inexact_reciprocal():
+    # d is not a power of two, so fp32(1 / d) is inexact and multiplying by it lands on
+    # the other side of E4M3 midpoints than dividing by d would
+    name = "fp8r_row_reciprocal_worked.txt"
+    vals, codes = value_code_table(name)
+    q, d = quant.quantize_fp8r(bf16(vals)[None, :])
+    assert float(d[0]) == float(directives(name)["row_scale"])
+    assert np.array_equal(q[0], codes)
+
+
 def test_fp8r_power_of_two_rows_reduce_to_plain_rounding():
     rng = np.random.default_rng(5)
     for k in (-20, -3, 0, 4, 11):
@@ -100,6 +110,22 @@ def test_nvfp4_worked_block():
     packed, sf = quant.quantize_nvfp4(bf16(vals)[None, :], np.float32(1.0))
     assert sf[0, 0] == int(directives("nvfp4_block_worked.txt")["scale_code"], 16)
     assert np.array_equal(codec.unpack_e2m1(packed)[0], codes)
+
+
+def test_nvfp4_worked_blocks_with_inexact_global_reciprocal():
+    # g is not a power of two: the order of the scale and encode-multiplier steps decides a
+    # scale code (line 1) and an element code (line 2)
+    for ln in lines("nvfp4_global_reciprocal_worked.txt"):
+        parts = ln.split()
+        g, sf_code = np.float32(float.fromhex(parts[0])), int(parts[1], 16)
+        pairs = [(float(a), int(b, 16)) for a, b in (p.split(":") for p in parts[2:])]
+        block = np.zeros(16)
+        block[: len(pairs)] = [v for v, _ in pairs]
+        assert np.max(np.abs(block)) == pairs[0][0]
+        packed, sf = quant.quantize_nvfp4(bf16(block)[None, :], g)
+        assert sf[0, 0] == sf_code, (parts[0], hex(sf[0, 0]))
+        got = codec.unpack_e2m1(packed)[0]
+        assert [int(c) for c in got[: len(pairs)]] == [c for _, c in pairs], parts[0]
 
 
 def test_nvfp4_saturation_worked():

@@ -136,9 +136,28 @@ def cpu_baseline(rows=64, reps=2):
     dt = (time.perf_counter() - t0) / reps
     flops = 2.0 * rows * K * (N_FP8 + N_FP4)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": "%d of %d tokens of both linears per step (weights dequantized in full), %d steps, %.2f s/step"
-                      % (rows, M, reps, dt)}
+                      % (rows, M, reps, dt),
+            "cores_note": "cores = BLAS threads of the fp64 products (the quantizers and dequantization are "
+                          "single-threaded NumPy)",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def quantized_output_comparison(L, dev, y3, gemm_args, operands):
@@ -492,6 +511,9 @@ def main():
     # about 0.2 s of steps, so that the timed steps see the steady state
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=600)
+    ap.add_argument("--warm-ms", type=float, default=100.0,
+                    help="GPU time of back-to-back steps run after the warmup steps and before the timed ones, "
+                         "whatever --warmup says, so that the timed steps see steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-small-m", action="store_true", help="skip the few-token sweep")
     ap.add_argument("--no-joint", action="store_true", help="skip the 16384-token joint-block shapes")
@@ -561,24 +583,34 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     seq = calls(stream)
     DOM = parts.index("gemm_nvfp4")
+    FP8 = parts.index("gemm_fp8r")
 
     def step(ev=None):
         for i, (fn, a) in enumerate(seq):
-            if ev is not None and i == DOM:
-                ev[0].record()
+            if ev is not None and i in (DOM, FP8):
+                ev[0 if i == DOM else 2].record()
             st = fn(*a)
             if st != 0:
                 raise L.BsqError(fn.__name__, st)
-            if ev is not None and i == DOM:
-                ev[1].record()
+            if ev is not None and i in (DOM, FP8):
+                ev[1 if i == DOM else 3].record()
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # then at least --warm-ms of back-to-back steps, timed by events: the clocks need tens of
+    # milliseconds of sustained load to settle, whatever the number of warmup steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    warm_gpu(step, ms=args.warm_ms)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1)
+    log("warmed for %.1f ms of steps" % warm_ms)
 
     log("timing %d steps" % args.steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -586,6 +618,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dom_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    fp8_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
 
     # per-kernel averages (outside the timed region): each call back to back between two events
     per_kernel = {}
@@ -601,6 +634,7 @@ def main():
         torch.cuda.synchronize()
         per_kernel[p] = e0.elapsed_time(e1) / reps  # ms
     per_kernel["gemm_nvfp4"] = dom_ms
+    per_kernel["gemm_fp8r"] = fp8_ms
     ms_per_step = wall * 1e3 / args.steps
     flops = 2.0 * M * K * (N_FP8 + N_FP4)
     value = flops * args.steps / wall / 1e12
@@ -627,6 +661,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_gpu_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -648,8 +683,8 @@ def main():
             "traffic": measured_traffic(),
         },
         "kernels_us": {p: round(v * 1e3, 2) for p, v in per_kernel.items()},
-        "kernels_us_note": "gemm_nvfp4: HIP events around each launch in the timed steps; others: back-to-back "
-                           "launches between two events after the timed region",
+        "kernels_us_note": "gemm_nvfp4, gemm_fp8r: HIP events around each launch in the timed steps (on the "
+                           "launch stream); others: back-to-back launches between two events after the timed region",
         "gemm_fp8r": {"tflops": round(g8_tflops, 1), "frac_fp8_peak": round(g8_tflops / PEAK_FP8_TFLOPS, 4)},
         "gemm_nvfp4": {"tflops": round(g4_tflops, 1), "frac_f16_peak": round(g4_tflops / PEAK_F16_TFLOPS, 4),
                        "frac_fp4_peak": round(g4_tflops / 10100.0, 4)},

@@ -146,7 +146,7 @@ def bsq_calibrate_global_scale(x, out=None, workspace=None):
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=x.device)
     _check("bsq_calibrate_global_scale", lib.bsq_calibrate_global_scale(
-        _ptr(x), M, K, ldx, _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+        _ptr(x), M, K, ldx, _ptr(out), _ptr(workspace), _nbytes(workspace), _stream()))
     return out
 
 
@@ -158,7 +158,12 @@ def _workspace(fmt, M, N, K, flags, workspace, device):
     nbytes = lib.bsq_gemm_workspace_bytes(fmt, M, N, K, flags)
     if workspace is None and nbytes:
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
-    return workspace, (0 if workspace is None else workspace.numel())
+    return workspace, _nbytes(workspace)
+
+
+def _nbytes(t):
+    """Size in bytes of a caller's workspace tensor of any dtype (0 for None)."""
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def bsq_gemm_fp8r(x, w, w_scale, flags=0, y=None, workspace=None):
@@ -204,7 +209,7 @@ def _lora_workspace(fmt, M, N, K, rank, flags, workspace, device):
     nbytes = lib.bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags)
     if workspace is None and nbytes:
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=device)
-    return workspace, (0 if workspace is None else workspace.numel())
+    return workspace, _nbytes(workspace)
 
 
 def bsq_lora_workspace_bytes(fmt, M, N, K, rank, flags=0):
@@ -222,7 +227,7 @@ def bsq_lora_down(x, lora_a, lora_scale, t=None, workspace=None):
     if workspace is None and nbytes:
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
     _check("bsq_lora_down", lib.bsq_lora_down(_ptr(x), ldx, _ptr(lora_a), M, K, rank, float(lora_scale), _ptr(t),
-                                              _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                              _ptr(workspace), _nbytes(workspace),
                                               _stream()))
     return t
 
@@ -327,7 +332,7 @@ def bsq_gemm_nvfp4_q_quantize_y(xq, x_bscale, input_scale, w, w_bscale, w_scale2
                                            _ptr(w_scale2), _ptr(y_scale), _ptr(yq), _ptr(y_bscale),
                                            _ptr(y) if y is not None else None, ldy, M, N, K,
                                            _ptr(workspace) if workspace is not None else None,
-                                           workspace.numel() if workspace is not None else 0, _stream()))
+                                           _nbytes(workspace), _stream()))
     return yq, y_bscale, y
 
 

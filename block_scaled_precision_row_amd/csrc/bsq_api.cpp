@@ -126,12 +126,14 @@ float* lora_part(void* ws, int64_t M, int64_t rank) {
 
 // adapter rules on top of the linear's: rank, scale, pointers, and the 32-bit buffer offsets
 // of the down-projection (32 rows of x) and up-projection (T and B rows) kernels
+// (an empty call, M == 0 or N == 0, passes the shape and scale rules and touches no pointer)
 bsq_status check_lora(int64_t ldx, const uint16_t* a, const uint16_t* b, int64_t rank, float scale, int64_t M,
                       int64_t N) {
   if (rank < 1 || rank > kMaxRank) return BSQ_ERR_SHAPE;
   if (ldx >= ((int64_t)1 << 24)) return BSQ_ERR_SHAPE;
   if (M * rank >= ((int64_t)1 << 29) || N * rank >= ((int64_t)1 << 29)) return BSQ_ERR_SHAPE;
   if (!std::isfinite(scale)) return BSQ_ERR_ARG;
+  if (M == 0 || N == 0) return BSQ_OK;
   if (!a || !b) return BSQ_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16)) return BSQ_ERR_ALIGN;
   return BSQ_OK;

@@ -124,7 +124,10 @@ bsq_status bsq_calibrate_global_scale(const uint16_t* x, int64_t M, int64_t K, i
 
 /* Workspace the GEMM entry points need (quantized activations):
  *   fp8r:  M*K + 4*M bytes, nvfp4: M*K/2 + M*K/16 bytes (each part padded
- *   to 256 bytes); 0 with BSQ_WEIGHT_ONLY. */
+ *   to 256 bytes); 0 with BSQ_WEIGHT_ONLY. The workspace pointer of
+ *   bsq_gemm_fp8r and bsq_gemm_nvfp4 must be 256-byte aligned (BSQ_ERR_ALIGN
+ *   otherwise; torch's and hipMalloc's allocations are); it may be NULL when
+ *   the size is 0. */
 size_t bsq_gemm_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, uint32_t flags);
 
 /*

@@ -58,3 +58,23 @@ def assert_gemm_close(y_gpu_bits, y_ref, what="", extra=None):
     assert np.all(np.isfinite(bf16_to_f64(y_gpu_bits))), what
     assert norm <= REL_TOL, (what, norm)
     assert excess <= 0.0, (what, excess)
+
+
+def assert_gemm_close_by_row(y_gpu_bits, y_ref, what=""):
+    """The tolerance applied to each row on its own (the floor from that row's rms): for inputs
+    whose rows differ in magnitude by many binades, where one rms over the whole output would
+    hide the small rows. A row whose reference is all zero must come out all zero."""
+    y = bf16_to_f64(y_gpu_bits)
+    assert np.all(np.isfinite(y)), what
+    worst = 0.0
+    for m in range(y_ref.shape[0]):
+        r, g = y_ref[m], y[m]
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        if rms == 0.0:
+            assert np.all(g == 0.0), (what, m)
+            continue
+        norm = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        assert norm <= REL_TOL, (what, m, norm)
+        assert np.all(np.abs(g - r) <= REL_TOL * np.abs(r) + FLOOR * rms), (what, m)
+        worst = max(worst, norm)
+    print("%s worst row normwise=%.3e" % (what, worst), flush=True)

@@ -84,7 +84,11 @@ def test_gemm_validation():
     assert g(A, 64, ODD, C, D, 64, 64, 64, 64, 0, A, ws, None) == ALIGN
     assert g(None, 64, None, None, None, 64, 0, 64, 64, 0, None, 0, None) == OK
     assert g(None, 64, None, None, None, 64, 64, 0, 64, 0, None, 0, None) == OK
+    # the workspace must be 256-byte aligned (16-byte aligned is not enough)
+    W16 = P((1 << 20) + 16)
+    assert g(A, 64, B, C, D, 64, 64, 64, 64, 0, W16, ws, None) == ALIGN
     n = L.bsq_gemm_nvfp4
+    assert n(A, 64, B, C, D, D, A, 64, 64, 64, 64, 0, W16, 1 << 20, None) == ALIGN
     assert n(A, 64, B, C, D, None, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == NULL       # W4A4 needs input_scale
     assert n(A, 64, B, C, None, D, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == NULL       # w_scale2
     assert n(A, 64, B, C, D, D, A, 64, 64, 64, 64, 0, None, 0, None) == WS
@@ -137,6 +141,9 @@ def test_lora_validation():
     assert g(A, 1 << 24, B, C, A, B, 16, 1.0, D, 64, 4, 64, 64, 0, A, 1 << 30, None) == SHAPE  # ldx
     assert g(A, 64, B, C, A, B, 128, 1.0, D, 1 << 22, 1 << 22, 64, 64, 0, A, 1 << 40, None) == SHAPE  # M * rank
     assert g(None, 64, None, None, A, B, 16, 1.0, None, 64, 0, 64, 64, 0, None, 0, None) == OK  # empty
+    # an empty call touches no pointer, the adapter's included
+    assert g(None, 64, None, None, None, None, 16, 1.0, None, 64, 0, 64, 64, 0, None, 0, None) == OK
+    assert g(None, 64, None, None, None, None, 16, 1.0, None, 64, 64, 0, 64, 0, None, 0, None) == OK
     n = L.bsq_gemm_nvfp4_lora
     ws = wsb(nv, 64, 64, 64, 16, 0)
     # x, ldx, w, w_bscale, w_scale2, input_scale, a, b, rank, scale, y, ldy, M, N, K, flags, ws, ws_bytes, stream
@@ -144,6 +151,7 @@ def test_lora_validation():
     assert n(A, 64, B, C, D, D, A, B, 16, 1.0, D, 64, 64, 64, 64, 0, A, ws - 1, None) == WS
     assert n(A, 64, B, C, D, None, A, B, 16, 1.0, D, 64, 64, 64, 64, wo, None, 0, None) == WS    # T needs room
     assert n(A, 64, B, C, D, D, A, B, 16, 1.0, D, 64, 64, 64, 64, 8, A, ws, None) == ARG
+    assert n(None, 64, None, None, None, None, None, None, 16, 1.0, None, 64, 0, 64, 64, 0, None, 0, None) == OK
     d = L.bsq_lora_down
     # x, ldx, a, M, K, rank, scale, t, ws, ws_bytes, stream
     assert d(A, 64, B, 4, 64, 0, 1.0, C, None, 0, None) == SHAPE
@@ -175,3 +183,10 @@ def test_binding_checks_tensors_before_calling():
     x = torch.zeros((4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         _lib.bsq_quantize_act_fp8r(x)          # CPU tensor is rejected by the binding
+
+
+def test_binding_counts_workspace_bytes_of_any_dtype():
+    # a caller's workspace of another dtype is passed with its size in bytes, not elements
+    assert _lib._nbytes(torch.empty(10, dtype=torch.float32)) == 40
+    assert _lib._nbytes(torch.empty(10, dtype=torch.uint8)) == 10
+    assert _lib._nbytes(None) == 0

@@ -1,7 +1,8 @@
 """GPU parity of the W4A4 GEMM that also emits its output in nvfp4 for the next linear.
 
 The contract is exact: the fused entry point must return the bf16 Y of
-bsq_gemm_nvfp4_q bit for bit, and its nvfp4 encoding of Y must equal, bit for
+bsq_gemm_nvfp4_q bit for bit (that Y is itself held to the GEMM tolerance against
+the oracle's product), and its nvfp4 encoding of Y must equal, bit for
 bit, both the GPU activation quantizer and the oracle's nvfp4 quantizer ("BFL
 (fp8r / nvfp4)", nvfp4 bullet) applied to that bf16 Y. Shapes cover the
 256x256 and 128x128 tiled kernels, the few-token kernel and the unfused path
@@ -12,8 +13,8 @@ import pytest
 import torch
 
 from block_scaled_precision_row_amd import synthetic as syn
-from oracle import quant
-from tests.gpu_util import dev, dev_bf16, dev_scalar, host
+from oracle import gemm, quant
+from tests.gpu_util import assert_gemm_close, dev, dev_bf16, dev_scalar, host
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +51,12 @@ def test_quantized_output_matches_gemm_then_quantizer(M, N, K):
     gy = quant.calibrate_global_scale(y_host)
     yq_gpu, ys_gpu = L.bsq_quantize_act_nvfp4(y_ref, dev_scalar(gy))
     yq_ora, ys_ora = quant.quantize_nvfp4(y_host, gy)
+
+    # the bf16 Y itself against the oracle's product of the dequantized operands (X quantized by
+    # the oracle; the GPU quantizer's codes equal the oracle's, checked elsewhere)
+    xq_o, xs_o = quant.quantize_nvfp4(x, gx)
+    assert np.array_equal(_bits(xq), xq_o) and np.array_equal(_bits(xs), xs_o)
+    assert_gemm_close(y_host, gemm.gemm_nvfp4(xq_o, xs_o, gx, wq, ws, gw), "w4a4 %dx%dx%d" % (M, N, K))
 
     yq, ys, y = L.bsq_gemm_nvfp4_q_quantize_y(*args, dev_scalar(gy), with_y=True)
     torch.cuda.synchronize()

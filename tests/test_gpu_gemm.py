@@ -12,7 +12,7 @@ import torch
 
 from block_scaled_precision_row_amd import synthetic as syn
 from oracle import codec, gemm, quant
-from tests.gpu_util import assert_gemm_close, dev, dev_bf16, dev_scalar, host
+from tests.gpu_util import assert_gemm_close, assert_gemm_close_by_row, dev, dev_bf16, dev_scalar, host
 
 pytestmark = pytest.mark.gpu
 
@@ -275,3 +275,59 @@ def test_weight_only_tiled(M, N, K):
     sample = 64 if M * N > 1 << 20 else None
     run_fp8r(x, w, weight_only=True, sample=sample, what="w8a16 %dx%dx%d" % (M, N, K))
     run_nvfp4(x, w, weight_only=True, sample=sample, what="w4a16 %dx%dx%d" % (M, N, K))
+
+
+# ---- edge inputs through the GEMM entry points ----------------------------------------------
+# The quantizers' edge rows (zero rows, signed zeros, zero blocks, row magnitudes spread over
+# 2^-40 .. 2^40) fed to whole linears, on shapes that take the few-token, small-grid and tiled
+# kernels; each row is held to the tolerance on its own.
+EDGE_SHAPES = [(16, 384, 512), (96, 320, 512), (600, 1024, 1024)]
+
+
+def _edge_rows(M, K, seed):
+    from tests.test_gpu_quant import _varied_rows
+    return _varied_rows(M, K, seed)
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_fp8r_edge_rows(M, N, K):
+    x = _edge_rows(M, K, 60 + M)
+    w = syn.normal_bf16((N, K), 60, 1000 + N, sigma=0.02)
+    wq, sw = quant.quantize_fp8r(w)
+    y = host(L.bsq_gemm_fp8r(dev_bf16(x), dev(wq), dev(sw)))
+    xq, sx = quant.quantize_fp8r(x)
+    assert_gemm_close_by_row(y, gemm.gemm_fp8r(xq, sx, wq, sw), "fp8r edge rows %dx%dx%d" % (M, N, K))
+    y = host(L.bsq_gemm_fp8r(dev_bf16(x), dev(wq), dev(sw), flags=L.BSQ_WEIGHT_ONLY))
+    assert_gemm_close_by_row(y, gemm.gemm_fp8r_weight_only(x, wq, sw), "fp8r-w8a16 edge rows %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_nvfp4_edge_rows(M, N, K):
+    """W4A4 with the global scale calibrated on the whole X: rows far below the largest ones
+    quantize to zero blocks (scale code 0), as the oracle's do."""
+    x = _edge_rows(M, K, 70 + M)
+    w = syn.normal_bf16((N, K), 70, 1000 + N, sigma=0.02)
+    gw = quant.calibrate_global_scale(w)
+    wq, sfw = quant.quantize_nvfp4(w, gw)
+    gx = quant.calibrate_global_scale(x)
+    y = host(L.bsq_gemm_nvfp4(dev_bf16(x), dev(wq), dev(sfw), dev_scalar(gw), dev_scalar(gx)))
+    xq, sfx = quant.quantize_nvfp4(x, gx)
+    assert_gemm_close_by_row(y, gemm.gemm_nvfp4(xq, sfx, gx, wq, sfw, gw), "nvfp4 edge rows %dx%dx%d" % (M, N, K))
+    y = host(L.bsq_gemm_nvfp4(dev_bf16(x), dev(wq), dev(sfw), dev_scalar(gw), None, flags=L.BSQ_WEIGHT_ONLY))
+    assert_gemm_close_by_row(y, gemm.gemm_nvfp4_weight_only(x, wq, sfw, gw),
+                             "nvfp4-w4a16 edge rows %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 384, 512), (300, 520, 1056), (1024, 1536, 3072)])
+def test_w4a4_saturating_input_scale(M, N, K):
+    """An input_scale 64x below the data's calibrated one: block scales saturate at 448 and
+    codes at +-6 inside the linear, exactly as the oracle's quantizer saturates them."""
+    x = syn.normal_bf16((M, K), 80, M)
+    w = syn.normal_bf16((N, K), 80, 1000 + N, sigma=0.02)
+    gw = quant.calibrate_global_scale(w)
+    wq, sfw = quant.quantize_nvfp4(w, gw)
+    gx = np.float32(quant.calibrate_global_scale(x) / 64)
+    xq, sfx = quant.quantize_nvfp4(x, gx)
+    assert (sfx == 0x7E).mean() > 0.5          # most blocks saturate
+    y = host(L.bsq_gemm_nvfp4(dev_bf16(x), dev(wq), dev(sfw), dev_scalar(gw), dev_scalar(gx)))
+    assert_gemm_close(y, gemm.gemm_nvfp4(xq, sfx, gx, wq, sfw, gw), "w4a4 saturating %dx%dx%d" % (M, N, K))

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsq.so")
 BSQ_FMT_FP8R = 1
 BSQ_FMT_NVFP4 = 2
 BSQ_WEIGHT_ONLY = 0x1
+BSQ_NOALLOC_MAX_BYTES = 64 << 20  # scratch of bsq_gemm_fp8r_noalloc (include/bsq.h)
 
 STATUS = {0: "BSQ_OK", 1: "BSQ_ERR_NULL", 2: "BSQ_ERR_SHAPE", 3: "BSQ_ERR_ALIGN", 4: "BSQ_ERR_WORKSPACE",
           5: "BSQ_ERR_DEVICE", 6: "BSQ_ERR_HIP", 7: "BSQ_ERR_ARG"}
@@ -37,6 +38,7 @@ SIGNATURES = {
     "bsq_calibrate_global_scale": (_int, [_p, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "bsq_gemm_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _u32]),
     "bsq_gemm_fp8r": (_int, [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz, _p]),
+    "bsq_gemm_fp8r_noalloc": (_int, [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p]),
     "bsq_gemm_nvfp4": (_int, [_p, _i64, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz, _p]),
     "bsq_dequant_to_bf16": (_int, [_int, _p, _p, _p, _i64, _i64, _p, _p]),
     "bsq_gemm_fp8r_q": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
@@ -177,6 +179,20 @@ def bsq_gemm_fp8r(x, w, w_scale, flags=0, y=None, workspace=None):
     ws, nbytes = _workspace(BSQ_FMT_FP8R, M, N, K, flags, workspace, x.device)
     _check("bsq_gemm_fp8r", lib.bsq_gemm_fp8r(_ptr(x), ldx, _ptr(w), _ptr(w_scale), _ptr(y), ldy, M, N, K, flags,
                                               _ptr(ws), nbytes, _stream()))
+    return y
+
+
+def bsq_gemm_fp8r_noalloc(x, w, w_scale, flags=0, y=None):
+    """bsq_gemm_fp8r on the library's own device scratch (no workspace; y must be passed in to
+    allocate nothing at all)."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N = w.shape[0]
+    _dense(w, torch.uint8, (N, K), "w")
+    _dense(w_scale, torch.float32, (N,), "w_scale")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _, _, ldy = _rows(y, torch.bfloat16, "y")
+    _check("bsq_gemm_fp8r_noalloc", lib.bsq_gemm_fp8r_noalloc(_ptr(x), ldx, _ptr(w), _ptr(w_scale), _ptr(y), ldy,
+                                                              M, N, K, flags, _stream()))
     return y
 
 

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "dequant.hip", "gemm_fp8.hip", "gemm_dec.hip", "gemm_w4a4.hip", "gemm_skinny.hip", "gemm_a16.hip", "lora.hip", "bsq_api.cpp"]
+SOURCES = ["quant.hip", "dequant.hip", "gemm_fp8.hip", "gemm_dec.hip", "gemm_w4a4.hip", "gemm_skinny.hip", "gemm_a16.hip", "lora.hip", "scratch.hip", "bsq_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",

@@ -243,6 +243,32 @@ bsq_status bsq_gemm_fp8r(const uint16_t* x, int64_t ldx, const uint8_t* w, const
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
+static_assert(BSQ_NOALLOC_MAX_BYTES == bsq::kScratchBytes, "the header states the scratch size");
+
+bsq_status bsq_gemm_fp8r_noalloc(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* w_scale,
+                                 uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                                 hipStream_t stream) {
+  bsq_status st = check_gemm_common(x, ldx, w, y, ldy, M, N, K, flags);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!w_scale) return BSQ_ERR_NULL;
+  if (!aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
+  const bool weight_only = flags & BSQ_WEIGHT_ONLY;
+  if (!weight_only && ws_fp8r(M, K) > bsq::kScratchBytes) return BSQ_ERR_WORKSPACE;
+  if ((st = check_device()) != BSQ_OK) return st;
+  if (weight_only)  // no scratch needed: the plain entry point allocates nothing either
+    return bsq_gemm_fp8r(x, ldx, w, w_scale, y, ldy, M, N, K, flags, nullptr, 0, stream);
+  void* ws = nullptr;
+  hipError_t e = bsq::scratch_buffer(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  // the same launches as bsq_gemm_fp8r with the library's scratch as its workspace: the
+  // quantizer overwrites every byte the GEMM reads, so nothing needs clearing
+  uint8_t* xq = static_cast<uint8_t*>(ws);
+  float* sx = reinterpret_cast<float*>(xq + pad256((size_t)(M * K)));
+  e = bsq::launch_quant_fp8r(x, M, K, ldx, xq, sx, stream);
+  if (e == hipSuccess) e = launch_w8a8(xq, sx, w, w_scale, y, ldy, M, N, K, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
 bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint8_t* w_bscale,
                           const float* w_scale2, const float* input_scale, uint16_t* y, int64_t ldy, int64_t M,
                           int64_t N, int64_t K, uint32_t flags, void* workspace, size_t workspace_bytes,

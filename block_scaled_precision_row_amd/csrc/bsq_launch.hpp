@@ -9,6 +9,12 @@
 
 namespace bsq {
 
+// Device scratch owned by the library (scratch.hip): kScratchBytes per GPU, 256-byte aligned,
+// held until the process ends. scratch_buffer() returns the current device's copy (looked up
+// once per device). Every user on one GPU shares it.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_buffer(void** out);
+
 hipError_t launch_quant_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
                              float* sx, hipStream_t s);
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* g,

@@ -144,6 +144,23 @@ bsq_status bsq_gemm_fp8r(const uint16_t* x, int64_t ldx, const uint8_t* w, const
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * bsq_gemm_fp8r for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and output bits as bsq_gemm_fp8r, without the
+ * workspace arguments. The quantized activations go to a scratch array that
+ * the library holds on each GPU it runs on, of BSQ_NOALLOC_MAX_BYTES (64 MiB),
+ * until the process ends; a shape whose workspace (bsq_gemm_workspace_bytes)
+ * exceeds it returns BSQ_ERR_WORKSPACE and enqueues nothing. Calls no hipMalloc / hipFree.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller. With BSQ_WEIGHT_ONLY no scratch is used.
+ */
+#define BSQ_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+bsq_status bsq_gemm_fp8r_noalloc(const uint16_t* x, int64_t ldx, const uint8_t* w, const float* w_scale,
+                                 uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                                 hipStream_t stream);
+
+/*
  * nvfp4 linear ("BFL (fp8r / nvfp4)", nvfp4 bullet and "Kernels" table).
  * Default (W4A4): quantizes X to nvfp4 with *input_scale into the workspace
  * (as bsq_quantize_act_nvfp4), then

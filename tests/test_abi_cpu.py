@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 20
+    assert len(syms) == 21
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
@@ -87,6 +87,16 @@ def test_gemm_validation():
     # the workspace must be 256-byte aligned (16-byte aligned is not enough)
     W16 = P((1 << 20) + 16)
     assert g(A, 64, B, C, D, 64, 64, 64, 64, 0, W16, ws, None) == ALIGN
+    # the no-allocation variant: same rules, no workspace; shapes beyond its scratch are refused
+    z = L.bsq_gemm_fp8r_noalloc
+    with open(os.path.join(ROOT, "include", "bsq.h")) as f:
+        assert "#define BSQ_NOALLOC_MAX_BYTES ((size_t)64 << 20)" in f.read()
+    assert z(A, 64, B, None, D, 64, 64, 64, 64, 0, None) == NULL
+    assert z(A, 64, B, C, D, 64, 64, 64, 48, 0, None) == SHAPE
+    assert z(A, 64, B, C, D, 64, 64, 64, 64, 2, None) == ARG
+    assert z(None, 64, None, None, None, 64, 0, 64, 64, 0, None) == OK
+    big_m = _lib.BSQ_NOALLOC_MAX_BYTES // 4096 + 1                                      # M * K just over 64 MiB
+    assert z(A, 4096, B, C, D, 64, big_m, 64, 4096, 0, None) == WS
     n = L.bsq_gemm_nvfp4
     assert n(A, 64, B, C, D, D, A, 64, 64, 64, 64, 0, W16, 1 << 20, None) == ALIGN
     assert n(A, 64, B, C, D, None, A, 64, 64, 64, 64, 0, A, 1 << 20, None) == NULL       # W4A4 needs input_scale

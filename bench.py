@@ -160,42 +160,96 @@ def cpu_model():
     return None
 
 
-def quantized_output_comparison(L, dev, y3, gemm_args, operands):
-    """The W4A4 linear 4096x12288x3072 feeding another nvfp4 linear: GEMM, then the activation
-    quantizer over the bf16 Y, against the GEMM that quantizes Y in its epilogue (bit-identical
-    codes), with and without writing the bf16 Y. Ten back-to-back repetitions each, in us."""
+def quantized_output_comparison(L, dev, y3, y2, gemm3_args, gemm2_args, operands3, operands2):
+    """Linears feeding another quantized linear, in both producers and both output formats: the
+    GEMM followed by the activation quantizer over its bf16 Y, against the GEMM that encodes Y
+    itself (nvfp4 in its epilogue; fp8r from per-segment row maxima written by the epilogue and
+    one encoding pass), with and without writing the bf16 Y. Ten back-to-back repetitions each
+    after warming, us per linear; the codes are bit-identical (GPU tests)."""
     import torch
 
     lib = L.lib
     stream = torch.cuda.current_stream().cuda_stream
     P = lambda t: t.data_ptr()
-    xq, xs, gx, wq, ws, gw = operands
-    gy = L.bsq_calibrate_global_scale(y3)
-    yq = torch.empty((M, N_FP4 // 2), dtype=torch.uint8, device=dev)
-    ys = torch.empty((M, N_FP4 // 16), dtype=torch.uint8, device=dev)
-    fused_args = (P(xq), P(xs), P(gx), P(wq), P(ws), P(gw), P(gy), P(yq), P(ys))
-    variants = {
-        "gemm_then_quantizer": [(lib.bsq_gemm_nvfp4_q, gemm_args),
-                                (lib.bsq_quantize_act_nvfp4, (P(y3), M, N_FP4, N_FP4, P(gy), P(yq), P(ys), stream))],
-        "fused_no_bf16_y": [(lib.bsq_gemm_nvfp4_q_quantize_y, fused_args + (None, 0, M, N_FP4, K, None, 0, stream))],
-        "fused_with_bf16_y": [(lib.bsq_gemm_nvfp4_q_quantize_y,
-                               fused_args + (P(y3), N_FP4, M, N_FP4, K, None, 0, stream))],
-    }
-    out = {}
-    for name, calls in variants.items():
+    x3q, x3s, gx3, w3q, w3s, g3 = operands3
+    x2q, x2s, w2q, w2s = operands2
+    fp8, nv = L.BSQ_FMT_FP8R, L.BSQ_FMT_NVFP4
+
+    def ws(fmt, Mo, No, with_y):
+        n = lib.bsq_gemm_quantize_y_workspace_bytes(fmt, Mo, No, 1 if with_y else 0)
+        return torch.empty((max(n, 256),), dtype=torch.uint8, device=dev), n
+
+    def time_calls(calls):
         for fn, a in calls:
-            fn(*a)
+            st = fn(*a)
+            if st != 0:
+                raise L.BsqError(fn.__name__, st)
         warm_gpu(lambda: [fn(*a) for fn, a in calls])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(10):
             for fn, a in calls:
-                st = fn(*a)
-                if st != 0:
-                    raise L.BsqError(fn.__name__, st)
+                fn(*a)
         e1.record()
         torch.cuda.synchronize()
-        out[name] = round(e0.elapsed_time(e1) / 10 * 1e3, 2)
+        return round(e0.elapsed_time(e1) / 10 * 1e3, 2)
+
+    out = {}
+    # nvfp4 W4A4 linear 4096 x 12288 x 3072 as the producer
+    gy3 = L.bsq_calibrate_global_scale(y3)
+    q4 = torch.empty((M, N_FP4 // 2), dtype=torch.uint8, device=dev)
+    s4 = torch.empty((M, N_FP4 // 16), dtype=torch.uint8, device=dev)
+    q8 = torch.empty((M, N_FP4), dtype=torch.uint8, device=dev)
+    d8 = torch.empty((M,), dtype=torch.float32, device=dev)
+    w3 = (P(x3q), P(x3s), P(gx3), P(w3q), P(w3s), P(g3))
+    wsy, nwsy = ws(fp8, M, N_FP4, True)
+    wsn, nwsn = ws(fp8, M, N_FP4, False)
+    out["w4a4_4096x12288x3072"] = {
+        "to_nvfp4": {
+            "gemm_then_quantizer": time_calls([
+                (lib.bsq_gemm_nvfp4_q, gemm3_args),
+                (lib.bsq_quantize_act_nvfp4, (P(y3), M, N_FP4, N_FP4, P(gy3), P(q4), P(s4), stream))]),
+            "fused_no_bf16_y": time_calls([(lib.bsq_gemm_nvfp4_q_quantize_y, w3 + (
+                P(gy3), P(q4), P(s4), None, 0, M, N_FP4, K, None, 0, stream))]),
+            "fused_with_bf16_y": time_calls([(lib.bsq_gemm_nvfp4_q_quantize_y, w3 + (
+                P(gy3), P(q4), P(s4), P(y3), N_FP4, M, N_FP4, K, None, 0, stream))]),
+        },
+        "to_fp8r": {
+            "gemm_then_quantizer": time_calls([
+                (lib.bsq_gemm_nvfp4_q, gemm3_args),
+                (lib.bsq_quantize_act_fp8r, (P(y3), M, N_FP4, N_FP4, P(q8), P(d8), stream))]),
+            "fused_no_bf16_y": time_calls([(lib.bsq_gemm_nvfp4_q_quantize_y_fp8r, w3 + (
+                P(q8), P(d8), None, 0, M, N_FP4, K, P(wsn), nwsn, stream))]),
+            "fused_with_bf16_y": time_calls([(lib.bsq_gemm_nvfp4_q_quantize_y_fp8r, w3 + (
+                P(q8), P(d8), P(y3), N_FP4, M, N_FP4, K, P(wsy), nwsy, stream))]),
+        },
+    }
+    # fp8r W8A8 linear 4096 x 3072 x 3072 as the producer
+    gy2 = L.bsq_calibrate_global_scale(y2)
+    q4 = torch.empty((M, N_FP8 // 2), dtype=torch.uint8, device=dev)
+    s4 = torch.empty((M, N_FP8 // 16), dtype=torch.uint8, device=dev)
+    q8 = torch.empty((M, N_FP8), dtype=torch.uint8, device=dev)
+    d8 = torch.empty((M,), dtype=torch.float32, device=dev)
+    w2 = (P(x2q), P(x2s), P(w2q), P(w2s))
+    entry = {}
+    for name, fmt in (("to_nvfp4", nv), ("to_fp8r", fp8)):
+        qq, qs = (q4, s4) if fmt == nv else (q8, d8)
+        gy = P(gy2) if fmt == nv else None
+        quantizer = ((lib.bsq_quantize_act_nvfp4, (P(y2), M, N_FP8, N_FP8, P(gy2), P(q4), P(s4), stream)) if fmt == nv
+                     else (lib.bsq_quantize_act_fp8r, (P(y2), M, N_FP8, N_FP8, P(q8), P(d8), stream)))
+        wy, nwy = ws(fmt, M, N_FP8, True)
+        wn, nwn = ws(fmt, M, N_FP8, False)
+        entry[name] = {
+            "gemm_then_quantizer": time_calls([(lib.bsq_gemm_fp8r_q, gemm2_args), quantizer]),
+            "fused_no_bf16_y": time_calls([(lib.bsq_gemm_fp8r_q_quantize_y, w2 + (
+                fmt, gy, P(qq), P(qs), None, 0, M, N_FP8, K, P(wn), nwn, stream))]),
+            "fused_with_bf16_y": time_calls([(lib.bsq_gemm_fp8r_q_quantize_y, w2 + (
+                fmt, gy, P(qq), P(qs), P(y2), N_FP8, M, N_FP8, K, P(wy), nwy, stream))]),
+        }
+    out["fp8r_4096x3072x3072"] = entry
+    out["note"] = ("us per linear (GEMM on pre-quantized activations + the next linear's input encoding); "
+                   "fused = the producer encodes its own output (nvfp4 in the epilogue, fp8r from the "
+                   "epilogue's per-segment row maxima and one encoding pass)")
     return out
 
 
@@ -693,8 +747,8 @@ def main():
     }
     if not args.no_quant_out:
         log("quantized-output comparison")
-        result["w4a4_quantized_output_us"] = quantized_output_comparison(
-            L, dev, y3, seq[DOM][1], (x3q, x3s, gx3, w3q, w3s, g3))
+        result["quantized_output_us"] = quantized_output_comparison(
+            L, dev, y3, y2, seq[DOM][1], seq[FP8][1], (x3q, x3s, gx3, w3q, w3s, g3), (x2q, x2s, w2q, w2s))
     if not args.no_vendor:
         log("vendor-library GEMM context")
         result["vendor_gemm_context"] = vendor_gemm_context(dev)

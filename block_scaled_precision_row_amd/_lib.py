@@ -46,6 +46,11 @@ SIGNATURES = {
     "bsq_gemm_nvfp4_quantize_y_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "bsq_gemm_nvfp4_q_quantize_y": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
                                            _p]),
+    "bsq_gemm_quantize_y_workspace_bytes": (_sz, [_int, _i64, _i64, _int]),
+    "bsq_gemm_fp8r_q_quantize_y": (_int, [_p, _p, _p, _p, _int, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
+                                          _p]),
+    "bsq_gemm_nvfp4_q_quantize_y_fp8r": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
+                                                _p]),
     "bsq_lora_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _u32]),
     "bsq_gemm_fp8r_lora": (_int, [_p, _i64, _p, _p, _p, _p, _i64, _f32, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz,
                                   _p]),
@@ -350,6 +355,74 @@ def bsq_gemm_nvfp4_q_quantize_y(xq, x_bscale, input_scale, w, w_bscale, w_scale2
                                            _ptr(workspace) if workspace is not None else None,
                                            _nbytes(workspace), _stream()))
     return yq, y_bscale, y
+
+
+def _quantized_output(out_format, M, N, y_global, with_y, yq, yq_scale, y, dev):
+    """Output tensors of the quantized-output linears: (yq, yq_scale, y or None, ldy)."""
+    if out_format == BSQ_FMT_NVFP4:
+        _scalar(y_global, "y_global")
+        yq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev) if yq is None else yq
+        yq_scale = torch.empty((M, N // 16), dtype=torch.uint8, device=dev) if yq_scale is None else yq_scale
+        _dense(yq, torch.uint8, (M, N // 2), "yq")
+        _dense(yq_scale, torch.uint8, (M, N // 16), "yq_scale")
+    else:
+        if y_global is not None:
+            raise ValueError("an fp8r output takes no global scale")
+        yq = torch.empty((M, N), dtype=torch.uint8, device=dev) if yq is None else yq
+        yq_scale = torch.empty((M,), dtype=torch.float32, device=dev) if yq_scale is None else yq_scale
+        _dense(yq, torch.uint8, (M, N), "yq")
+        _dense(yq_scale, torch.float32, (M,), "yq_scale")
+    ldy = 0
+    if with_y or y is not None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+        _, _, ldy = _rows(y, torch.bfloat16, "y")
+    return yq, yq_scale, y, ldy
+
+
+def _quantize_y_workspace(out_format, M, N, y, workspace, dev):
+    n = lib.bsq_gemm_quantize_y_workspace_bytes(out_format, M, N, 1 if y is not None else 0)
+    if workspace is None and n:
+        workspace = torch.empty((n,), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def bsq_gemm_fp8r_q_quantize_y(xq, x_scale, w, w_scale, out_format, y_global=None, with_y=False, yq=None,
+                               yq_scale=None, y=None, workspace=None):
+    """W8A8 GEMM as bsq_gemm_fp8r_q whose output is also returned encoded for the next linear:
+    (yq, yq_scale, bf16 y or None) -- nvfp4 (uint8 [M, N/2], uint8 [M, N/16]; y_global [1]) or
+    fp8r (uint8 [M, N], fp32 [M])."""
+    M, K = xq.shape
+    N = w.shape[0]
+    _dense(xq, torch.uint8, (M, K), "xq")
+    _dense(x_scale, torch.float32, (M,), "x_scale")
+    _dense(w, torch.uint8, (N, K), "w")
+    _dense(w_scale, torch.float32, (N,), "w_scale")
+    yq, yq_scale, y, ldy = _quantized_output(out_format, M, N, y_global, with_y, yq, yq_scale, y, xq.device)
+    ws = _quantize_y_workspace(out_format, M, N, y, workspace, xq.device)
+    _check("bsq_gemm_fp8r_q_quantize_y", lib.bsq_gemm_fp8r_q_quantize_y(
+        _ptr(xq), _ptr(x_scale), _ptr(w), _ptr(w_scale), out_format, _ptr(y_global), _ptr(yq), _ptr(yq_scale),
+        _ptr(y), ldy, M, N, K, _ptr(ws), _nbytes(ws), _stream()))
+    return yq, yq_scale, y
+
+
+def bsq_gemm_nvfp4_q_quantize_y_fp8r(xq, x_bscale, input_scale, w, w_bscale, w_scale2, with_y=False, yq=None,
+                                     y_rowscale=None, y=None, workspace=None):
+    """W4A4 GEMM as bsq_gemm_nvfp4_q whose output is also returned in fp8r for the next linear:
+    (E4M3 yq uint8 [M, N], fp32 row scales [M], bf16 y or None)."""
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = w.shape[0]
+    _dense(xq, torch.uint8, (M, K // 2), "xq")
+    _dense(x_bscale, torch.uint8, (M, K // 16), "x_bscale")
+    _scalar(input_scale, "input_scale")
+    _dense(w, torch.uint8, (N, K // 2), "w")
+    _dense(w_bscale, torch.uint8, (N, K // 16), "w_bscale")
+    _scalar(w_scale2, "w_scale2")
+    yq, y_rowscale, y, ldy = _quantized_output(BSQ_FMT_FP8R, M, N, None, with_y, yq, y_rowscale, y, xq.device)
+    ws = _quantize_y_workspace(BSQ_FMT_FP8R, M, N, y, workspace, xq.device)
+    _check("bsq_gemm_nvfp4_q_quantize_y_fp8r", lib.bsq_gemm_nvfp4_q_quantize_y_fp8r(
+        _ptr(xq), _ptr(x_bscale), _ptr(input_scale), _ptr(w), _ptr(w_bscale), _ptr(w_scale2), _ptr(yq),
+        _ptr(y_rowscale), _ptr(y), ldy, M, N, K, _ptr(ws), _nbytes(ws), _stream()))
+    return yq, y_rowscale, y
 
 
 def bsq_dequant_to_bf16(fmt, w, w_scale, w_scale2=None, out=None):

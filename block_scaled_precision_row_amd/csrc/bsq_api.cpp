@@ -381,6 +381,121 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscal
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
+size_t bsq_gemm_quantize_y_workspace_bytes(bsq_format out_format, int64_t M, int64_t N, int with_y) {
+  if ((out_format != BSQ_FMT_FP8R && out_format != BSQ_FMT_NVFP4) || M <= 0 || N <= 0) return 0;
+  size_t n = with_y ? 0 : pad256((size_t)M * (size_t)N * 2);  // bf16 Y when the caller takes none
+  if (out_format == BSQ_FMT_FP8R) n += pad256((size_t)bsq::ypmax_segments(N) * (size_t)M * 4);
+  return n;
+}
+
+namespace {
+// shared checks of the quantized-output entry points; on success *ybuf / *ldb / *pmax point at
+// where the bf16 Y and the fp8r row maxima go
+bsq_status check_quantize_y(bsq_format out_format, const float* y_global, uint8_t* yq, void* yq_scale, uint16_t* y,
+                            int64_t ldy, int64_t M, int64_t N, void* workspace, size_t workspace_bytes,
+                            uint16_t** ybuf, int64_t* ldb, float** pmax) {
+  if (out_format != BSQ_FMT_FP8R && out_format != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;
+  if (out_format == BSQ_FMT_FP8R && y_global) return BSQ_ERR_ARG;
+  if (N % 32 != 0 || (y && ldy % 8 != 0)) return BSQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return BSQ_OK;
+  if (!yq || !yq_scale || (out_format == BSQ_FMT_NVFP4 && !y_global)) return BSQ_ERR_NULL;
+  if (!aligned(yq, 16) || !aligned(yq_scale, 4) || (y_global && !aligned(y_global, 4))) return BSQ_ERR_ALIGN;
+  if (M * (N / 16) >= kMaxThreads) return BSQ_ERR_SHAPE;
+  const size_t need = bsq_gemm_quantize_y_workspace_bytes(out_format, M, N, y != nullptr);
+  if (need && (!workspace || workspace_bytes < need)) return BSQ_ERR_WORKSPACE;
+  if (need && !aligned(workspace, 256)) return BSQ_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  *ybuf = y;
+  *ldb = ldy;
+  if (!y) {
+    *ybuf = reinterpret_cast<uint16_t*>(ws);
+    *ldb = N;
+    ws += pad256((size_t)M * (size_t)N * 2);
+  }
+  *pmax = out_format == BSQ_FMT_FP8R ? reinterpret_cast<float*>(ws) : nullptr;
+  return BSQ_OK;
+}
+
+// the next linear's encoding of a bf16 Y already in memory (routes without a fused epilogue)
+hipError_t quantize_y_after(bsq_format out_format, const uint16_t* ybuf, int64_t ldb, int64_t M, int64_t N,
+                            const float* y_global, uint8_t* yq, void* yq_scale, hipStream_t stream) {
+  if (out_format == BSQ_FMT_NVFP4)
+    return bsq::launch_quant_nvfp4(ybuf, M, N, ldb, y_global, yq, static_cast<uint8_t*>(yq_scale), stream);
+  return bsq::launch_quant_fp8r(ybuf, M, N, ldb, yq, static_cast<float*>(yq_scale), stream);
+}
+}  // namespace
+
+bsq_status bsq_gemm_fp8r_q_quantize_y(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
+                                      bsq_format out_format, const float* y_global, uint8_t* yq, void* yq_scale,
+                                      uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  // without a bf16 output the shape is checked as for a dense [M][N] one, with yq standing in
+  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w,
+                                    y ? y : reinterpret_cast<uint16_t*>(yq), y ? ldy : N, M, N, K, 0);
+  if (st != BSQ_OK) return st;
+  uint16_t* ybuf = nullptr;
+  int64_t ldb = 0;
+  float* pmax = nullptr;
+  st = check_quantize_y(out_format, y_global, yq, yq_scale, y, ldy, M, N, workspace, workspace_bytes, &ybuf, &ldb,
+                        &pmax);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!x_scale || !w_scale) return BSQ_ERR_NULL;
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  bsq::DecArgs a{};
+  a.xq = xq; a.sx = x_scale; a.w = w; a.sw = w_scale; a.M = M; a.N = N; a.K = K;
+  hipError_t e;
+  if (route_skinny(bsq::kW8A8, a)) {  // few tokens: the GEMM, then the quantizer over its Y
+    a.y = ybuf; a.ldy = ldb;
+    e = bsq::launch_gemm_skinny(bsq::kW8A8, a, stream);
+    if (e == hipSuccess) e = quantize_y_after(out_format, ybuf, ldb, M, N, y_global, yq, yq_scale, stream);
+  } else if (out_format == BSQ_FMT_NVFP4) {  // encoded in the epilogue; bf16 Y only if asked for
+    bsq::YQuant q;
+    q.yq = yq; q.ys = static_cast<uint8_t*>(yq_scale); q.gy = y_global;
+    e = bsq::launch_gemm_fp8(xq, x_scale, w, w_scale, y, ldy, M, N, K, nullptr, nullptr, 0, stream, &q);
+  } else {  // row maxima in the epilogue, then the encoding pass over Y
+    bsq::YQuant q;
+    q.pmax = pmax;
+    e = bsq::launch_gemm_fp8(xq, x_scale, w, w_scale, ybuf, ldb, M, N, K, nullptr, nullptr, 0, stream, &q);
+    if (e == hipSuccess)
+      e = bsq::launch_encode_fp8r_rows(ybuf, M, N, ldb, pmax, yq, static_cast<float*>(yq_scale), stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+bsq_status bsq_gemm_nvfp4_q_quantize_y_fp8r(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
+                                            const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2,
+                                            uint8_t* yq, float* y_rowscale, uint16_t* y, int64_t ldy, int64_t M,
+                                            int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w,
+                                    y ? y : reinterpret_cast<uint16_t*>(yq), y ? ldy : N, M, N, K, 0);
+  if (st != BSQ_OK) return st;
+  uint16_t* ybuf = nullptr;
+  int64_t ldb = 0;
+  float* pmax = nullptr;
+  st = check_quantize_y(BSQ_FMT_FP8R, nullptr, yq, y_rowscale, y, ldy, M, N, workspace, workspace_bytes, &ybuf, &ldb,
+                        &pmax);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!x_bscale || !input_scale || !w_bscale || !w_scale2) return BSQ_ERR_NULL;
+  if (!aligned(x_bscale, 4) || !aligned(input_scale, 4) || !aligned(w_bscale, 4) || !aligned(w_scale2, 4))
+    return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  bsq::DecArgs a{};
+  a.xq = xq; a.xs = x_bscale; a.gx = input_scale; a.w = w; a.ws = w_bscale; a.gw = w_scale2;
+  a.y = ybuf; a.ldy = ldb; a.M = M; a.N = N; a.K = K;
+  hipError_t e;
+  if (!route_skinny(bsq::kW4A4, a) && bsq::gemm_w4a4_supported(a)) {  // row maxima in the epilogue
+    a.ypmax = pmax;
+    e = bsq::launch_gemm_w4a4(a, stream);
+    if (e == hipSuccess) e = bsq::launch_encode_fp8r_rows(ybuf, M, N, ldb, pmax, yq, y_rowscale, stream);
+  } else {
+    e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
+    if (e == hipSuccess) e = quantize_y_after(BSQ_FMT_FP8R, ybuf, ldb, M, N, nullptr, yq, y_rowscale, stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
 size_t bsq_lora_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, int64_t rank, uint32_t flags) {
   if ((f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) || M <= 0 || K <= 0 || rank <= 0) return 0;
   return bsq_gemm_workspace_bytes(f, M, N, K, flags) + ws_lora_down(M, K, rank);

@@ -47,11 +47,30 @@ inline int64_t rounds_cost(int64_t M, int64_t N, int BM, int BN, int tile_cost) 
   return (tiles + 255) / 256 * tile_cost;
 }
 
+// Optional quantized form of a tiled GEMM's output for the next linear (N % 32 == 0):
+//   nvfp4: yq [M][N/2] packed E2M1 and ys [M][N/16] E4M3 with global scale *gy, encoded in the
+//          epilogue (the 16-blocks along N lie inside a tile);
+//   fp8r:  pmax [M][ceil(N/64)], each row's maximum |y| over each 64-column segment, for
+//          launch_encode_fp8r_rows to finish once every tile of the row has written its part.
+struct YQuant {
+  uint8_t* yq = nullptr;
+  uint8_t* ys = nullptr;
+  const float* gy = nullptr;
+  float* pmax = nullptr;
+};
+inline int64_t ypmax_segments(int64_t N) { return (N + 63) / 64; }
+
 // W8A8: y = bf16((sum e4m3(xq) e4m3(w)) * sx[m] * sw[n])
-// (with lt != nullptr, plus the adapter term T B^T; see DecArgs)
+// (with lt != nullptr, plus the adapter term T B^T; see DecArgs). y may be null when q asks
+// for the nvfp4 encoding.
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                            uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,
-                           const uint16_t* lb, int rank, hipStream_t s);
+                           const uint16_t* lb, int rank, hipStream_t s, const YQuant* q = nullptr);
+// fp8r encoding of a bf16 Y [M][ldy] (N % 32 == 0) whose row maxima per 64-column segment are
+// in pmax [M][ceil(N/64)]: with a = the row's maximum, d = fp32(a / 448), r = fp32(1 / d),
+// yq[m][n] = E4M3(fp32(y * r)), yd[m] = d -- what launch_quant_fp8r computes for the same Y.
+hipError_t launch_encode_fp8r_rows(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const float* pmax,
+                                   uint8_t* yq, float* yd, hipStream_t s);
 // LoRA down projection: t [M][rank] = bf16(f * X A^T), X bf16 [M][ldx], A bf16 [rank][K], with
 // f = scale, or scale / (*ga * *gb) when ga != nullptr (T for a GEMM that scales its
 // accumulators by *ga * *gb). K is cut into lora_down_slices(M, K, rank) slices; with more than
@@ -87,6 +106,8 @@ struct DecArgs {
   uint8_t* yq;         // optional nvfp4 copy of Y for the next linear: packed E2M1 [M][N/2] (W4A4)
   uint8_t* ys;         // its E4M3 block scales [M][N/16]
   const float* gy;     // its global scale (the next linear's input_scale)
+  float* ypmax;        // optional row maxima of |Y| per 64-column segment [M][ceil(N/64)], for an
+                       // fp8r encoding of Y (tiled W4A4 kernel)
   // optional low-rank adapter: y += T B^T with T = s X A^T [M][rank] (bf16, scaled) and
   // B [N][rank] (bf16); lt == nullptr means none. The tiled W4A4 kernel instead takes
   // T / (gx gw) and adds T B^T to its accumulators before the K loop.

@@ -215,6 +215,34 @@ __device__ __forceinline__ void quant_tile_rows(const uint8_t* tile, uint8_t* __
   }
 }
 
+// Row maxima of |y| over 64-column segments of a bf16 output tile [BM][BN] (rows TROW bytes
+// apart in LDS), for an fp8r encoding of Y whose per-row scale needs the whole row: segment s
+// of row m goes to pmax[m][s] (s counted over the whole row, ceil(N/64) per row, N % 32 == 0),
+// and a later pass takes each row's maximum over its segments, reading them contiguously.
+// Consecutive threads take consecutive segments of a row. The bf16 bit pattern with the sign
+// cleared orders magnitudes as unsigned integers, so the maximum is exact and order-free.
+template <int BM, int BN, int TROW>
+__device__ __forceinline__ void rowmax_tile(const uint8_t* tile, float* __restrict__ pmax, int M, int N, int m0,
+                                            int n0, int tid) {
+  constexpr int SEG = BN / 64;
+  static_assert(BN % 64 == 0, "tiles cover whole 64-column segments");
+  const int nseg = (N + 63) >> 6;
+  for (int idx = tid; idx < BM * SEG; idx += kThreads) {
+    const int ml = idx / SEG, sg = idx % SEG;
+    const int m = m0 + ml, n = n0 + 64 * sg;
+    if (m >= M || n >= N) continue;
+    const int nc = (N - n < 64 ? N - n : 64) >> 3;  // whole 8-value chunks (N % 32 == 0)
+    uint32_t mx = 0;
+    for (int c = 0; c < nc; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * TROW + (64 * sg + 8 * c) * 2);
+      const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = max(mx, max(w[e] & 0xFFFFu, w[e] >> 16));
+    }
+    pmax[(int64_t)m * nseg + (n0 >> 6) + sg] = __uint_as_float(mx << 16);
+  }
+}
+
 // ---- low-rank adapter (LoRA) up-projection on the accumulators ---------------------------
 // An adapter adds T B^T to the layer's output, with T = s X A^T [M][rank] (bf16, the adapter's
 // scale already applied by the down-projection kernel) and B [N][rank] (bf16). The tiled GEMMs

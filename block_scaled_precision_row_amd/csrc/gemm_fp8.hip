@@ -81,12 +81,14 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
 }
 
-template <int BM, int BN, int NS, bool LORA>
+// OQ: quantized output for the next linear -- 0 none, 1 nvfp4 blocks in the epilogue, 2 the
+// row maxima of the fp8r encoding (YQuant)
+template <int BM, int BN, int NS, bool LORA, int OQ = 0>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                      const uint8_t* __restrict__ w, const float* __restrict__ sw,
                      uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, const uint16_t* lt,
-                     const uint16_t* lb, int rank, int stream_y) {
+                     const uint16_t* lb, int rank, int stream_y, YQuant q) {
   using C = Cfg<BM, BN, NS>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -197,21 +199,33 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     }
   }
   __syncthreads();
-  store_tile_rows<BM, BN, C::TROW>(smem, y, ldy, M, N, m0, n0, tid, stream_y != 0);
+  if (y) store_tile_rows<BM, BN, C::TROW>(smem, y, ldy, M, N, m0, n0, tid, stream_y != 0);
+  // the next linear's input, quantized from the same bf16 tile ("BFL (fp8r / nvfp4)": every
+  // quantized linear quantizes its input at run time)
+  if constexpr (OQ == 1) quant_tile_rows<BM, BN, C::TROW>(smem, q.yq, q.ys, 1.0f / q.gy[0], M, N, m0, n0, tid);
+  if constexpr (OQ == 2) rowmax_tile<BM, BN, C::TROW>(smem, q.pmax, M, N, m0, n0, tid);
 }
 
 template <int BM, int BN, int NS>
 hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw, uint16_t* y,
                int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt, const uint16_t* lb, int rank,
-               hipStream_t s) {
+               hipStream_t s, const YQuant* q) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   constexpr bool kAdapter = !(BM == 256 && BN == 256);  // the 256 x 256 tile never carries one (launch_gemm_fp8)
+  const int st = (int)stream_output((M + N) * K, M, N);
+  const YQuant qv = q ? *q : YQuant{};
   if (kAdapter && lt)
     hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
-                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, (int)stream_output((M + N) * K, M, N));
+                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+  else if (qv.yq)
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 1>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
+                       y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+  else if (qv.pmax)
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 2>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
+                       y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
   else
     hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
-                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, (int)stream_output((M + N) * K, M, N));
+                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
   return hipGetLastError();
 }
 
@@ -219,7 +233,7 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
 
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                            uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,
-                           const uint16_t* lb, int rank, hipStream_t s) {
+                           const uint16_t* lb, int rank, hipStream_t s, const YQuant* q) {
   // A grid of few tiles leaves compute units idle, and each busy unit is bound by the latency
   // of its own loads (three stages in flight); more, smaller tiles keep more loads in flight
   // across the chip. So while its grid fits one round on the 256 units, the smallest tile is
@@ -236,13 +250,13 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w,
   // adapter the square tile is left out (its epilogue does not fit the square tile's
   // registers). Every tile shape gives the same bits (the same MFMA sequence per output).
   const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64), t64x128 = ((M + 63) / 64) * ((N + 127) / 128);
-  if (t64 <= 256) return run<64, 64, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
-  if (t64x128 <= 256) return run<64, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  if (t64 <= 256) return run<64, 64, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
+  if (t64x128 <= 256) return run<64, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
   const int64_t c256 = lt ? INT64_MAX : rounds_cost(M, N, 256, 256, 92);
   const int64_t c192 = rounds_cost(M, N, 256, 192, 72), c128 = rounds_cost(M, N, 128, 128, 31);
-  if (c256 <= c192 && c256 <= c128) return run<256, 256, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
-  if (c192 <= c128) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
-  return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s);
+  if (c256 <= c192 && c256 <= c128) return run<256, 256, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
+  if (c192 <= c128) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
+  return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
 }
 
 }  // namespace bsq

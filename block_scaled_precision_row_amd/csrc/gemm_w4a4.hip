@@ -302,6 +302,8 @@ void gemm_w4a4_kernel(DecArgs a) {
   // quantized linear quantizes its input at run time); its 16-blocks run along this N, inside
   // the tile
   if (a.yq) quant_tile_rows<BM, BN, C::TROW>(smem, a.yq, a.ys, 1.0f / a.gy[0], M, N, m0, n0, tid);
+  // or the row maxima of an fp8r encoding, whose per-row scale spans every tile of the row
+  if (a.ypmax) rowmax_tile<BM, BN, C::TROW>(smem, a.ypmax, M, N, m0, n0, tid);
 }
 
 template <int BM, int BN>

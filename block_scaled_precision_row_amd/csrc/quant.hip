@@ -70,10 +70,15 @@ __global__ __launch_bounds__(256) void quant_fp8r_rows(const uint16_t* __restric
 // 16-byte store out -- and the row maximum is combined across the row's waves through LDS.
 // Measured against quant_fp8r_rows: 4096 x 3072 7.2 -> 6.5 us, 512 x 3072 3.7 -> 3.1 us, with
 // identical bits.
-template <int NP, int TPR>
+//
+// With PM, the row's maximum is not taken over the row but over pmax[row][s], s < nseg: the
+// maxima of the row's 64-value segments that a GEMM epilogue already wrote (the same value,
+// since the maximum is exact); everything else is unchanged.
+template <int NP, int TPR, bool PM = false>
 __global__ __launch_bounds__(256) void quant_fp8r_pairs(const uint16_t* __restrict__ x, int64_t M, int K,
                                                          int64_t ldx, uint8_t* __restrict__ xq,
-                                                         float* __restrict__ sx) {
+                                                         float* __restrict__ sx, const float* __restrict__ pmax,
+                                                         int nseg) {
   constexpr int WPR = TPR / 64;  // waves per row
   __shared__ float red[4];
   const int t = threadIdx.x % TPR, lane = threadIdx.x & 63;
@@ -84,13 +89,16 @@ __global__ __launch_bounds__(256) void quant_fp8r_pairs(const uint16_t* __restri
   const int np = K >> 4;
   uint4 buf[NP][2];
   float amax = 0.0f;
+  if constexpr (PM) {
+    for (int sg = t; live && sg < nseg; sg += TPR) amax = fmaxf(amax, pmax[row * nseg + sg]);
+  }
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int c = t + TPR * i;
     if (live && c < np) {
       buf[i][0] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 16);
       buf[i][1] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 16 + 8);
-      amax = fmaxf(amax, fmaxf(absmax8(buf[i][0]), absmax8(buf[i][1])));
+      if constexpr (!PM) amax = fmaxf(amax, fmaxf(absmax8(buf[i][0]), absmax8(buf[i][1])));
     }
   }
   amax = wave_max(amax);
@@ -118,11 +126,12 @@ hipError_t launch_quant_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ld
                              float* sx, hipStream_t s) {
   if (K <= 64 * 16 * 4) {  // a wave per row, four rows per workgroup
     hipLaunchKernelGGL((quant_fp8r_pairs<4, 64>), dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, x, M, (int)K,
-                       ldx, xq, sx);
+                       ldx, xq, sx, nullptr, 0);
     return hipGetLastError();
   }
   if (K <= 256 * 16 * 4) {  // a workgroup per row
-    hipLaunchKernelGGL((quant_fp8r_pairs<4, 256>), dim3((unsigned)M), dim3(256), 0, s, x, M, (int)K, ldx, xq, sx);
+    hipLaunchKernelGGL((quant_fp8r_pairs<4, 256>), dim3((unsigned)M), dim3(256), 0, s, x, M, (int)K, ldx, xq, sx,
+                       nullptr, 0);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((M + 3) / 4)), block(256);
@@ -131,6 +140,23 @@ hipError_t launch_quant_fp8r(const uint16_t* x, int64_t M, int64_t K, int64_t ld
   else
     hipLaunchKernelGGL(quant_fp8r_rows<24>, grid, block, 0, s, x, M, (int)K, ldx, xq, sx);
   return hipGetLastError();
+}
+
+hipError_t launch_encode_fp8r_rows(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const float* pmax,
+                                   uint8_t* yq, float* yd, hipStream_t s) {
+  const int nseg = (int)ypmax_segments(N);
+  if (N <= 64 * 16 * 4) {
+    hipLaunchKernelGGL((quant_fp8r_pairs<4, 64, true>), dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, y, M,
+                       (int)N, ldy, yq, yd, pmax, nseg);
+    return hipGetLastError();
+  }
+  if (N <= 256 * 16 * 4) {
+    hipLaunchKernelGGL((quant_fp8r_pairs<4, 256, true>), dim3((unsigned)M), dim3(256), 0, s, y, M, (int)N, ldy, yq,
+                       yd, pmax, nseg);
+    return hipGetLastError();
+  }
+  // longer rows: the quantizer's own maximum (one more read of each row; same bits)
+  return launch_quant_fp8r(y, M, N, ldy, yq, yd, s);
 }
 
 // ---- nvfp4: one thread per 16-element block ---------------------------------

@@ -217,6 +217,45 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y(const uint8_t* xq, const uint8_t* x_bscal
                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Quantized-output linears in either format ("BFL (fp8r / nvfp4)": every
+ * quantized linear quantizes its input at run time -- fp8r per row to E4M3,
+ * nvfp4 per 16-block with its calibrated input_scale; here the producing GEMM
+ * hands the next linear its input already encoded):
+ *   bsq_gemm_fp8r_q_quantize_y       : the W8A8 linear of bsq_gemm_fp8r_q,
+ *   bsq_gemm_nvfp4_q_quantize_y_fp8r : the W4A4 linear of bsq_gemm_nvfp4_q,
+ * whose bf16 output Y (bit for bit that entry point's) is also returned
+ * encoded for the next linear, exactly as the activation quantizers encode
+ * that Y:
+ *   out_format BSQ_FMT_NVFP4: y_global [1] fp32 = the next linear's
+ *     input_scale; yq [M][N/2] packed E2M1; yq_scale uint8 [M][N/16] E4M3
+ *     (= bsq_quantize_act_nvfp4(Y, y_global));
+ *   out_format BSQ_FMT_FP8R: y_global must be NULL; yq [M][N] E4M3;
+ *     yq_scale fp32 [M] row scales (= bsq_quantize_act_fp8r(Y)).
+ * (bsq_gemm_nvfp4_q_quantize_y above is the W4A4 producer with nvfp4 output.)
+ * The nvfp4 blocks lie inside an output tile and are encoded in the GEMM's
+ * epilogue. An fp8r row scale needs the whole row: the epilogue records each
+ * row's maximum over every 64-column segment of its tile, and one pass then
+ * takes each row's maximum of those (exact, so the result does not depend on
+ * the order) and encodes Y. Few-token shapes (and W4A4 with K % 256 != 0) run
+ * the GEMM and then the quantizer.
+ *   y [M][ldy] bf16 (ldy % 8 == 0), or NULL to skip writing it; yq 16-byte
+ *   aligned; N % 32 == 0 (BSQ_ERR_SHAPE otherwise).
+ * Workspace: bsq_gemm_quantize_y_workspace_bytes(out_format, M, N, y != NULL)
+ * bytes, 256-byte aligned (NULL when 0): a bf16 Y when y is NULL, and for
+ * fp8r output the fp32 row maxima [M][ceil(N/64)].
+ */
+size_t bsq_gemm_quantize_y_workspace_bytes(bsq_format out_format, int64_t M, int64_t N, int with_y);
+bsq_status bsq_gemm_fp8r_q_quantize_y(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
+                                      bsq_format out_format, const float* y_global, uint8_t* yq, void* yq_scale,
+                                      uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+bsq_status bsq_gemm_nvfp4_q_quantize_y_fp8r(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
+                                            const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2,
+                                            uint8_t* yq, float* y_rowscale, uint16_t* y, int64_t ldy, int64_t M,
+                                            int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
+/*
  * Low-rank adapter (LoRA) side path on the quantized linear. "FLUX 3 Image
  * Klein vs Qwen-Image-2.1" (model overview) and the FLUX 3 Image Klein
  * open-source release page (section three, speed figures): the quantized

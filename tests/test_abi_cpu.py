@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 21
+    assert len(syms) == 24
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
@@ -121,6 +121,35 @@ def test_quantize_y_validation():
     assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(4096, 1024, 512, 0) == 0
     assert L.bsq_gemm_nvfp4_quantize_y_workspace_bytes(16, 1024, 96, 0) == 0
     assert q(A, B, C, A, B, C, D, A, B, None, 0, 4096, 1024, 96, None, 0, None) == WS
+
+
+def test_quantized_output_validation():
+    fp8, nv = _lib.BSQ_FMT_FP8R, _lib.BSQ_FMT_NVFP4
+    pad = lambda n: (n + 255) // 256 * 256
+    wsb = L.bsq_gemm_quantize_y_workspace_bytes
+    assert wsb(fp8, 4096, 3072, 1) == pad(48 * 4096 * 4)                    # row maxima per 64 columns
+    assert wsb(fp8, 4096, 3072, 0) == pad(4096 * 3072 * 2) + pad(48 * 4096 * 4)
+    assert wsb(nv, 4096, 3072, 1) == 0 and wsb(nv, 4096, 3072, 0) == pad(4096 * 3072 * 2)
+    assert wsb(fp8, 0, 3072, 0) == 0 and wsb(3, 64, 64, 0) == 0
+    g = L.bsq_gemm_fp8r_q_quantize_y
+    ws = wsb(fp8, 64, 64, 0)
+    # xq, x_scale, w, w_scale, out_fmt, y_global, yq, yq_scale, y, ldy, M, N, K, ws, ws_bytes, stream
+    assert g(A, B, C, D, 3, None, A, B, None, 0, 64, 64, 64, A, ws, None) == ARG          # format
+    assert g(A, B, C, D, fp8, D, A, B, None, 0, 64, 64, 64, A, ws, None) == ARG           # fp8r takes no global
+    assert g(A, B, C, D, nv, None, A, B, None, 0, 64, 64, 64, A, ws, None) == NULL         # nvfp4 needs one
+    assert g(A, B, C, D, fp8, None, A, B, None, 0, 64, 48, 64, A, ws, None) == SHAPE       # N % 32
+    assert g(A, B, C, D, fp8, None, ODD, B, None, 0, 64, 64, 64, A, ws, None) == ALIGN     # yq
+    assert g(A, B, C, D, fp8, None, A, B, None, 0, 64, 64, 64, A, ws - 1, None) == WS
+    assert g(A, B, C, D, fp8, None, A, B, None, 0, 64, 64, 64, P((1 << 20) + 16), ws, None) == ALIGN
+    assert g(A, None, C, D, fp8, None, A, B, None, 0, 64, 64, 64, A, ws, None) == NULL     # x_scale
+    assert g(None, None, None, None, fp8, None, None, None, None, 0, 0, 64, 64, None, 0, None) == OK  # empty
+    n = L.bsq_gemm_nvfp4_q_quantize_y_fp8r
+    # xq, x_bscale, input_scale, w, w_bscale, w_scale2, yq, y_rowscale, y, ldy, M, N, K, ws, ws_bytes, stream
+    assert n(A, B, None, A, B, C, A, B, None, 0, 64, 64, 256, A, ws, None) == NULL         # input_scale
+    assert n(A, B, C, A, B, C, A, None, None, 0, 64, 64, 256, A, ws, None) == NULL         # row scales
+    assert n(A, B, C, A, B, C, A, B, None, 0, 64, 64, 256, None, 0, None) == WS
+    assert n(A, B, C, A, B, C, A, B, D, 68, 64, 64, 256, A, ws, None) == SHAPE             # ldy % 8
+    assert n(None, None, None, None, None, None, None, None, None, 0, 0, 64, 256, None, 0, None) == OK
 
 
 def test_lora_validation():

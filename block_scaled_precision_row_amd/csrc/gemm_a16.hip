@@ -35,35 +35,19 @@ using namespace gemm;
 
 constexpr int kAK = 128;  // K values per stage
 
-template <int BM, int BN, bool FP4>
-struct ACfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int WR = FP4 ? 64 : 128;  // weight bytes per row and stage
-  using RX = Region<256, BM, kAK>;           // X rows: 128 bf16 values
-  using RW = Region<WR, BN, kAK>;            // W rows: packed E2M1 or E4M3
-  static constexpr int X_OFF = 0, W_OFF = BM * 256, S_OFF = W_OFF + BN * WR;
-  static constexpr int STAGE = S_OFF + (FP4 ? BN * 8 : 0);  // nvfp4: 8 block scales per row
-  static constexpr int TROW = BN * 2 + 16;  // bytes per row of the bf16 output tile in LDS
-  static constexpr int LDS = 2 * STAGE > BM * TROW ? 2 * STAGE : BM * TROW;
-  static_assert(LDS + 4 * BN <= 160 * 1024, "LDS budget");
-};
-
 // nvfp4 block scales of a stage: 8 bytes (the stage's 8 blocks of 16) per W row, copied by
 // dword LDS DMA, two lanes per row and 32 rows per load, spread over the waves. Loads of K
 // past the end read zeros (their offset is out of range).
 template <int ROWS>
 __device__ __forceinline__ void dma_scales8(const v4i& rsrc, uint32_t lds_base, int wave, int lane, int ks, int kb,
                                             int K) {
-  constexpr int LOADS = ROWS / 32;
-  static_assert(ROWS % 32 == 0, "whole scale loads");
-  const int half = lane & 1, lrow = lane >> 1;
-  const int voff = (kb + 64 * half < K) ? lrow * ks + 4 * half : kOutOfRange;
+  constexpr int LOADS = Scales8<ROWS>::LOADS;
 #pragma unroll
   for (int i = 0; i < (LOADS + 3) / 4; ++i) {
     const int ld = wave + 4 * i;
     if (ld >= LOADS) break;  // wave-uniform
-    dma4(rsrc, lds_base + ld * 256, voff, ld * 32 * ks + (kb >> 4));
+    const DmaAddr d = scales8_load(ld, lane, ks, kb, K);
+    dma4(rsrc, lds_base + ld * 256, d.voff, d.soff);
   }
 }
 

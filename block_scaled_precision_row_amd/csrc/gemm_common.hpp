@@ -18,14 +18,13 @@
 #pragma once
 
 #include "bsq_device.hpp"
+#include "gemm_tiles.hpp"
 
 namespace bsq {
 namespace gemm {
 
 constexpr int kThreads = 256;
 constexpr int kKS = 64;                  // default K values per stage of a Region
-constexpr int kOutOfRange = 0x40000000;  // buffer offset beyond any tile's records
-
 // s_waitcnt with vmcnt <= n (n in 0..63), lgkmcnt and expcnt unconstrained (gfx9 encoding)
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -33,76 +32,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// LDS rows of R bytes hold R/16 chunks of 16 bytes. A ds_read_b128 serves 16
-// lanes per 256-byte LDS window; 16 consecutive rows reading the same logical
-// chunk must land on 16 distinct 16-byte slots of the window, so the physical
-// chunk is the logical one XOR-ed with (row / rows-per-window) mod chunks.
-template <int R>
-__device__ __forceinline__ int swz_chunk(int row, int c) {
-  constexpr int C = R / 16, RPW = 16 / C;
-  return c ^ ((row / RPW) % C);
-}
-template <int R>
-__device__ __forceinline__ int swz_off(int row, int c) {
-  return row * R + (swz_chunk<R>(row, c) << 4);
-}
-
-// One operand region of a stage: ROWS rows of R bytes each, holding KSTAGE K
-// values per row (for a 64-deep stage: 128 bytes of bf16, 64 of E4M3, 32 of
-// packed E2M1, 4 of E4M3 block scales). A 1 KB
-// DMA load covers 1024 / R rows; lane l writes physical chunk l % C of row
-// l / C, so it fetches the logical chunk that the swizzle places there.
-// Loads are spread round-robin over the 4 waves.
-template <int R, int ROWS, int KSTAGE = kKS>
-struct Region {
-  static constexpr int C = R / 16;
-  static constexpr int RPL = 1024 / R;            // rows per load
-  static constexpr int LOADS = ROWS / RPL;        // loads per stage
-  static constexpr int MIN_PER_WAVE = LOADS / 4;  // loads issued by every wave
-  static constexpr int MAX_PER_WAVE = (LOADS + 3) / 4;
-  static_assert(ROWS % RPL == 0, "region rows must fill whole loads");
-  static constexpr int VPC = 16 * KSTAGE / R;     // K values per 16-byte chunk
-};
-
 // Issue this wave's loads of region `Rg` for the stage starting at K value kb.
 // rsrc covers the tile's rows (rows past the matrix read as zeros), `stride`
 // is the row pitch in bytes, `kbyte` the byte offset of the stage in a row.
 template <class Rg>
 __device__ __forceinline__ void dma_region(const v4i& rsrc, uint32_t lds_base, int wave, int lane, int stride,
                                            int kbyte, int kb, int K) {
-  const int lrow = lane / Rg::C, phys = lane % Rg::C;
 #pragma unroll
   for (int i = 0; i < Rg::MAX_PER_WAVE; ++i) {
     const int ld = wave + 4 * i;
     if (i >= Rg::MIN_PER_WAVE && ld >= Rg::LOADS) break;  // wave-uniform
-    const int row = ld * Rg::RPL + lrow;
-    const int c = swz_chunk<Rg::C * 16>(row, phys);  // the swizzle is an involution
-    const int voff = (kb + c * Rg::VPC < K) ? lrow * stride + (c << 4) : kOutOfRange;
-    dma16(rsrc, lds_base + ld * 1024, voff, ld * Rg::RPL * stride + kbyte);
+    const DmaAddr d = region_load<Rg>(ld, lane, stride, kbyte, kb, K);
+    dma16(rsrc, lds_base + ld * 1024, d.voff, d.soff);
   }
 }
 
-// E4M3 block scales of a stage: 4 bytes (4 blocks of 16) per row, 64 rows per
-// 4-byte-per-lane DMA load.
+// dword LDS DMA: lane l's 4 bytes land at M0 + 4 l
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
   asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
-}
-template <int ROWS>
-struct ScaleRegion {
-  static constexpr int LOADS = (ROWS + 63) / 64;
-  static constexpr int MIN_PER_WAVE = LOADS / 4;
-  static constexpr int MAX_PER_WAVE = (LOADS + 3) / 4;
-  static_assert(ROWS % 64 == 0, "scale rows must fill whole loads");
-};
-template <class Sg>
-__device__ __forceinline__ void dma_scales(const v4i& rsrc, uint32_t lds_base, int wave, int lane, int kstride,
-                                           int kb) {
-#pragma unroll
-  for (int i = 0; i < Sg::MAX_PER_WAVE; ++i) {
-    const int ld = wave + 4 * i;
-    if (i >= Sg::MIN_PER_WAVE && ld >= Sg::LOADS) break;
-    dma4(rsrc, lds_base + ld * 256, lane * kstride, ld * 64 * kstride + (kb >> 4));
-  }
 }
 
 // ---- bf16 epilogue --------------------------------------------------------------

@@ -35,21 +35,7 @@ using namespace gemm;
 constexpr int kStageK = 128;  // K values (bytes) per row per stage
 
 template <int BM, int BN, int NS>
-struct Cfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int TM = WM / 32, TN = WN / 32;
-  using RA = Region<128, BN, kStageK>;  // W rows
-  using RB = Region<128, BM, kStageK>;  // Xq rows
-  static constexpr int A_BYTES = BN * 128, STAGE = (BN + BM) * 128;
-  static constexpr int LOADS_MIN = RA::MIN_PER_WAVE + RB::MIN_PER_WAVE;  // per wave per stage
-  static constexpr int TROW = BN * 2 + 16;  // bytes per row of the bf16 output tile in LDS (padded)
-  static constexpr int LDS = NS * STAGE > BM * TROW ? NS * STAGE : BM * TROW;
-  static_assert(NS >= 2, "one stage in flight behind the one being multiplied");
-  static_assert(RA::MIN_PER_WAVE == RA::MAX_PER_WAVE && RB::MIN_PER_WAVE == RB::MAX_PER_WAVE,
-                "every wave issues the same number of loads (exact vmcnt accounting)");
-  static_assert((NS - 1) * LOADS_MIN < 64, "vmcnt range");
-  static_assert(LDS + 4 * (BM + BN) <= 160 * 1024, "LDS budget");
-};
+using Cfg = Fp8Cfg<BM, BN, NS>;
 
 // operands of K step t (0 or 1) of a stage: W rows from region A at `base`, Xq rows from region B at `bbase`
 template <int TN, int TM>
@@ -161,18 +147,20 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     constexpr int RPM = NM >= 16 ? 1 : 2;  // fragment reads per MFMA
     constexpr int KD = 8;                  // K-step-1 MFMAs before the next stage's reads start
     static_assert(C::RA::C == 8 && C::RB::C == 8, "128-byte rows");
-    const int drow = lane >> 3, dphys = lane & 7;
-    int voff[LD];
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
+    // load i of a stage: this wave's loads of region A (W) then of region B (Xq)
+    auto load_addr = [&](int i, int kb) {
       const int ld = wave + 4 * (i < LA ? i : i - LA);
-      voff[i] = drow * K + (swz_chunk<128>(ld * 8 + drow, dphys) << 4);
-    }
+      return i < LA ? region_load<typename C::RA>(ld, lane, K, kb, kb, K)
+                    : region_load<typename C::RB>(ld, lane, K, kb, kb, K);
+    };
+    int voff[LD];  // every chunk of a real stage lies inside K: the lane offsets of stage 0 hold
+#pragma unroll
+    for (int i = 0; i < LD; ++i) voff[i] = load_addr(i, 0).voff;
     auto dma = [&](int i, int kt) {
       const bool isA = i < LA;
       const int ld = wave + 4 * (isA ? i : i - LA);
       const uint32_t lb = lds0 + (uint32_t)((kt % NS) * C::STAGE) + (isA ? 0u : (uint32_t)C::A_BYTES) + ld * 1024;
-      dma16(isA ? rw : rx, lb, voff[i], ld * 8 * K + kt * kStageK);
+      dma16(isA ? rw : rx, lb, voff[i], load_addr(i, kt * kStageK).soff);
     };
     auto abuf = [&](int kt) { return smem + (kt % NS) * C::STAGE; };
     const int nk = K / kStageK;

@@ -39,8 +39,6 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kSkK = 128;  // K values per stage
-constexpr int kSkRing = 2;  // stage buffers per wave
 
 // ---- operands of one stage for one lane -------------------------------------------
 // nvfp4: 64 values = 32 packed bytes (q[g] holds values 32 g .. 32 g + 31 of the lane's
@@ -489,20 +487,8 @@ __global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel
 // ---- LDS-DMA variant (E4M3 weights): stage layout of one wave -----------------------
 // A code region holds 32 rows of R bytes (R = 128 for E4M3, 256 for bf16 at a 128-deep
 // stage), 16-byte chunks XOR-swizzled as in gemm_common.hpp.
-template <int R>
-struct CodeRegion {
-  static constexpr int C = R / 16, RPL = 1024 / R, LOADS = 32 / RPL, BYTES = 32 * R;
-};
-
 template <int MODE>
-struct Layout {
-  static_assert(MODE == kW8A8 || MODE == kW8A16, "E4M3 weights only");
-  static constexpr bool XBF = MODE == kW8A16;
-  using WC = CodeRegion<128>;
-  using XC = CodeRegion<XBF ? 256 : 128>;
-  static constexpr int W_BYTES = WC::BYTES, X_BYTES = XC::BYTES;  // X per M block
-  static constexpr int W_LOADS = WC::LOADS, X_LOADS = XC::LOADS;
-};
+using Layout = SkLayout<MODE>;
 
 // a buffer resource as the scalar operand the DMA instruction takes (the values are
 // wave-uniform; this keeps them in scalar registers when they come from an array)
@@ -521,14 +507,11 @@ __device__ __forceinline__ void dma_codes(const v4i& r, uint32_t lds, int lane, 
                                           int K, int rows) {
   using G = CodeRegion<R>;
   const v4i rs = sgpr(r);
-  const int lrow = lane / G::C, phys = lane % G::C;
 #pragma unroll
   for (int ld = 0; ld < G::LOADS; ++ld) {
     if (ld * G::RPL >= rows) break;  // uniform
-    const int row = ld * G::RPL + lrow;
-    const int c = swz_chunk<R>(row, phys);
-    const int voff = kv + c * vpc < K ? row * pitch + kbyte + 16 * c : kOutOfRange;
-    dma16(rs, lds + ld * 1024, voff, 0);
+    const DmaAddr d = code_load<R>(ld, lane, pitch, kbyte, kv, vpc, K);
+    dma16(rs, lds + ld * 1024, d.voff, d.soff);
   }
 }
 
@@ -555,14 +538,9 @@ template <int MODE, int MB, int NW, bool LORA>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   using S = Scheme<MODE>;
   using L = Layout<MODE>;
-  constexpr int STAGE = L::W_BYTES + MB * L::X_BYTES;
-  constexpr int WAVE = kSkRing * STAGE;
-  constexpr int LOADS = L::W_LOADS + MB * L::X_LOADS;  // DMA instructions per stage
-  constexpr int RED = NW * MB * 16 * 64 * 4 + (LORA ? MB * 16 * 64 * 4 : 0);  // partial tiles, adapter tiles
-  constexpr int LDS = NW * WAVE > RED ? NW * WAVE : RED;
-  static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert((kSkRing - 1) * LOADS < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  using SC = SkCfg<MODE, MB, NW, LORA>;
+  constexpr int STAGE = SC::STAGE, WAVE = SC::WAVE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SC::LDS];
 
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   const int nblk = (N + 31) / 32;

@@ -40,23 +40,6 @@ using namespace gemm;
 
 constexpr int kStageK = 256;  // K values per stage
 
-template <int BM, int BN>
-struct W4Cfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int TM = WM / 32, TN = WN / 32;
-  using RA = Region<128, BN, kStageK>;  // packed W rows, 128 bytes per stage
-  using RB = Region<128, BM, kStageK>;  // packed Xq rows
-  using SA = Region<16, BN, kStageK>;   // W block scales, 16 bytes per stage
-  using SB = Region<16, BM, kStageK>;   // Xq block scales
-  static constexpr int A_OFF = 0, B_OFF = BN * 128, SA_OFF = (BN + BM) * 128, SB_OFF = SA_OFF + BN * 16;
-  static constexpr int STAGE = (BN + BM) * 144;
-  static constexpr int LOADS = RA::MAX_PER_WAVE + RB::MAX_PER_WAVE + SA::MAX_PER_WAVE + SB::MAX_PER_WAVE;
-  static constexpr int TROW = BN * 2 + 16;  // bytes per row of the bf16 output tile in LDS
-  static constexpr int LDS = 2 * STAGE > BM * TROW ? 2 * STAGE : BM * TROW;
-  static_assert(LOADS < 64, "vmcnt range");
-  static_assert(LDS <= 160 * 1024, "LDS budget");
-};
-
 // packed operand bytes of one K group for one lane: 32 E2M1 values (4 dwords)
 struct Raw {
   uint4 q;

@@ -77,7 +77,7 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
 
 // The K loop, two ways. The general loop (any K, any ring depth) leaves the order of its
 // LDS reads, DMAs and MFMAs to the compiler, within scheduling groups. The hand-ordered loop
-// (two stage buffers, K % 128 == 0) fixes the order per MFMA, which took the large tiles 8-13 %
+// (two stage buffers, K % 128 == 0, with or without an adapter) fixes the order per MFMA, which took the large tiles 8-13 %
 // faster (4096 x 3072 x 3072 on 256 x 192: 38 -> 34 us; 16384 x 3072 x 3072 and
 // 4096 x 12288 x 3072 on 256 x 256: 147 -> 128 us, same bits):
 //  * K step 0 of stage s: one MFMA, then the LDS reads of RPM fragments of K step 1 (B
@@ -90,8 +90,8 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
 //    is ever loaded).
 // Without the fixed order the compiler bunched the DMAs' address arithmetic between the two
 // K steps (the matrix pipe drained there) and waited for every read at the loop head.
-template <int NS, bool LORA>
-constexpr bool hand_ordered() { return NS == 2 && !LORA; }
+template <int NS>
+constexpr bool hand_ordered() { return NS == 2; }
 
 // OQ: quantized output for the next linear -- 0 none, 1 nvfp4 blocks in the epilogue, 2 the
 // row maxima of the fp8r encoding (YQuant). HS: the hand-ordered K loop (K % 128 == 0).
@@ -335,13 +335,17 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
   const int st = (int)stream_output((M + N) * K, M, N);
   const YQuant qv = q ? *q : YQuant{};
   if (kAdapter && lt) {
-    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw, y,
-                       ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    if (hand_ordered<NS>() && K % kStageK == 0)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, hand_ordered<NS>()>), dim3(tiles), dim3(kThreads),
+                         0, s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    else
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
+                         y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
     return hipGetLastError();
   }
   const int oq = qv.yq ? 1 : qv.pmax ? 2 : 0;
-  if (hand_ordered<NS, false>() && K % kStageK == 0)
-    return launch_oq<BM, BN, NS, hand_ordered<NS, false>()>(oq, tiles, xq, sx, w, sw, y, ldy, M, N, K, st, qv, s);
+  if (hand_ordered<NS>() && K % kStageK == 0)
+    return launch_oq<BM, BN, NS, hand_ordered<NS>()>(oq, tiles, xq, sx, w, sw, y, ldy, M, N, K, st, qv, s);
   return launch_oq<BM, BN, NS, false>(oq, tiles, xq, sx, w, sw, y, ldy, M, N, K, st, qv, s);
 }
 

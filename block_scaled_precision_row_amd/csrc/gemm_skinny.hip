@@ -651,8 +651,14 @@ hipError_t run_staged(const DecArgs& a, hipStream_t s) {
 
 template <int MODE>
 hipError_t pick(const DecArgs& a, hipStream_t s) {
+  // One 32-token activation block per workgroup while two per workgroup would leave the grid
+  // short of the 256 compute units (measured with cold weights, K = 3072, N = 3072: W4A4 48 and
+  // 64 tokens 15.9 / 16.7 -> 9.4 / 11.1 us, W8A8 48 / 64 / 96 / 128 tokens 9.1 / 9.8 / 9.2 / 9.9
+  // -> 7.1 / 7.6 / 8.8 / 9.3 us); past 64 tokens W4A4 does better with two blocks (96 tokens
+  // 13.1 vs 14.2 us), which halve its weight decodes per output.
+  const bool short_grid = ((a.N + 31) / 32) * ((a.M + 63) / 64) < 256;
   if constexpr (MODE == kW4A4) {
-    if (a.M <= 32) return run_staged<MODE, 1>(a, s);
+    if (a.M <= 64) return run_staged<MODE, 1>(a, s);
     return run_staged<MODE, 2>(a, s);
   } else if constexpr (MODE == kW4A16) {
     // bf16 activations fill registers and LDS fastest: one activation block per workgroup
@@ -660,7 +666,7 @@ hipError_t pick(const DecArgs& a, hipStream_t s) {
   } else if constexpr (MODE == kW8A16) {
     return run<MODE, 1, 4>(a, s);
   } else {
-    if (a.M <= 32) return run<MODE, 1, 4>(a, s);
+    if (a.M <= 32 || short_grid) return run<MODE, 1, 4>(a, s);
     return run<MODE, 2, 4>(a, s);
   }
 }

@@ -345,7 +345,9 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
         out[name] = entry
     out["note"] = ("whole linear from bf16 X in both columns (activation quantizer + GEMM; with the adapter also "
                    "its down projection), synthetic adapter with scale 1; the pages report about 5 % more "
-                   "generation time with a LoRA attached (whole model, other hardware)")
+                   "generation time with a LoRA attached (whole model, other hardware). down_us: the down "
+                   "projection alone (bsq_lora_down); in the linears it is fused with the activation "
+                   "encoding (nvfp4: K-sliced kernel; fp8r: whole-row kernel, K <= 3072)")
     return out
 
 

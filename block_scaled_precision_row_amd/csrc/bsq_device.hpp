@@ -63,6 +63,20 @@ __device__ __forceinline__ uint32_t enc_e4m3(float a) {
   a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0u, false) & 0xFFu;
 }
+// fp8r per-chunk steps on 8 bf16 values (one 16-byte chunk of a row): the largest magnitude,
+// and the E4M3 codes of fp32(x * r) for the row's reciprocal scale r
+__device__ __forceinline__ float absmax8(uint4 v) {
+  return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                     fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
+               fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                     fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+}
+__device__ __forceinline__ uint2 encode8_fp8(uint4 v, float r) {
+  uint2 o;
+  o.x = enc_e4m3x4(bf16_lo(v.x) * r, bf16_hi(v.x) * r, bf16_lo(v.y) * r, bf16_hi(v.y) * r);
+  o.y = enc_e4m3x4(bf16_lo(v.z) * r, bf16_hi(v.z) * r, bf16_lo(v.w) * r, bf16_hi(v.w) * r);
+  return o;
+}
 // decode byte `sel` of w
 template <int sel>
 __device__ __forceinline__ float dec_e4m3(uint32_t w) { return __builtin_amdgcn_cvt_f32_fp8((int)w, sel); }

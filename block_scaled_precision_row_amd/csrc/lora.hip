@@ -241,6 +241,143 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
   }
 }
 
+// ---- fp8r linears: the down projection fused with the activation encoding ---------
+// The fp8r encoding of a row needs the row's maximum before any value is encoded, so it
+// cannot ride on the K-sliced kernel above. Here a workgroup owns 16 whole rows: each of its
+// (at most 8) waves holds 384 consecutive K values of all 16 rows in registers (six 64-deep
+// chunks; lane (lr, lg) holds the 16 values kc + 16 lg .. + 15 of row lr of chunk kc, the
+// layout of the kernel above), so X is read from HBM once and K <= 3072. (Twelve chunks a
+// wave, for K <= 6144, spill registers: longer rows take the unfused kernels.) The row maxima combine across the four lanes of a
+// row and then across the waves through LDS; each wave then encodes its values with the
+// quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))) and
+// multiplies the same registers into T on the matrix cores, with the adapter's chunks
+// read from L2 (A is the MFMA A operand, X the B operand). The waves' fp32 tiles are
+// added in wave order through LDS, one rank tile at a time, scaled and rounded to bf16.
+// One launch replaces the quantizer, the sliced down projection and its finishing pass.
+constexpr int kFusedWaves = 8;   // at most; 256 registers a lane
+constexpr int kFusedChunks = 6;  // 64-deep chunks a wave
+constexpr int kRingSlots = 4;    // adapter pieces (16 rows x 64 values) staged at a time per wave
+
+template <int RT>
+__global__ __launch_bounds__(64 * kFusedWaves) void lora_down_fp8r_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                   const uint16_t* __restrict__ a, int M, int K,
+                                                                   int rank, float scale,
+                                                                   uint16_t* __restrict__ t,
+                                                                   uint8_t* __restrict__ xq,
+                                                                   float* __restrict__ sx) {
+  constexpr int WMAX = kFusedWaves, NC = kFusedChunks, KW = 64 * NC;
+  __shared__ float red[WMAX][16];
+  __shared__ __attribute__((aligned(16))) float part[WMAX][16 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t aring[WMAX][kRingSlots][2048];
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const int rows = __builtin_amdgcn_readfirstlane(M - m0 < 16 ? M - m0 : 16);
+  const int kw0 = wave * KW;
+  // rows past M and values past K read as zeros: they raise no maximum and add nothing to T
+  const rsrc_t rx = make_rsrc(x + (int64_t)m0 * ldx, (uint32_t)rows * (uint32_t)ldx * 2u);
+  const rsrc_t ra = make_rsrc(a, (uint32_t)rank * (uint32_t)K * 2u);
+  const uint32_t xrow = (uint32_t)lr * (uint32_t)ldx * 2u;
+
+  // The adapter: piece i = RT c + r is rank tile r's 16 rows x 64 values of chunk c. Read with
+  // eight lanes per 128-byte row segment (whole lines per load; in the MFMA layout the lanes
+  // of a quarter wave would each address a different row) and staged through a ring of
+  // kRingSlots pieces in this wave's LDS, XOR-swizzled by row, from which each lane reads its
+  // MFMA operands. The
+  // first PRE pieces are requested with X, so that they arrive while the row maxima are
+  // combined and X is encoded.
+  constexpr int NP = NC * RT, PRE = NP <= 12 ? NP : 8;
+  const int gr = lane >> 3, gp = lane & 7;  // this lane's row (and row + 8) and piece of a load
+  uint4 xr[NC][2], ga[NP][2];
+  auto load_a = [&](int i) {
+    const int c = i / RT, r = i % RT;
+    const int k = kw0 + 64 * c + 8 * gp;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ga[i][h] = bload16(ra, k < K ? (uint32_t)((16 * r + 8 * h + gr) * K + k) * 2u : kBufOut);
+  };
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k = kw0 + 64 * c + 16 * lg;  // K % 32 == 0: all 16 values inside K or none
+#pragma unroll
+    for (int q = 0; q < 2; ++q) xr[c][q] = bload16(rx, k < K ? xrow + (uint32_t)k * 2u + 16u * q : kBufOut);
+  }
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) load_a(i);
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) amax = fmaxf(amax, fmaxf(absmax8(xr[c][0]), absmax8(xr[c][1])));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  if (lg == 0) red[wave][lr] = amax;
+  __syncthreads();  // every wave's row maxima are in red
+
+  for (int w = 0; w < waves; ++w) amax = fmaxf(amax, red[w][lr]);
+  if (lr < rows) {
+    const float d = amax / kE4M3Max;
+    const float rc = d > 0.0f ? 1.0f / d : 0.0f;
+    uint8_t* qrow = xq + (int64_t)(m0 + lr) * K;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int k = kw0 + 64 * c + 16 * lg;
+      if (k < K) {
+        const uint2 lo = encode8_fp8(xr[c][0], rc), hi = encode8_fp8(xr[c][1], rc);
+        *reinterpret_cast<uint4*>(qrow + k) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+    if (wave == 0 && lg == 0) sx[m0 + lr] = d;
+  }
+
+  v4f acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  uint8_t* ring = aring[wave][0];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int c = i / RT, r = i % RT;
+    if (i + PRE < NP) load_a(i + PRE);  // PRE pieces in flight
+    uint8_t* slot = ring + (i % kRingSlots) * 2048;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + gr;
+      *reinterpret_cast<uint4*>(slot + row * 128 + ((gp ^ (row & 7)) << 4)) = ga[i][h];
+    }
+    // lane (lr, lg): row lr, values 16 lg + 8 q of the chunk, as in xr[c][q]
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 av = *reinterpret_cast<const uint4*>(slot + lr * 128 + (((2 * lg + q) ^ (lr & 7)) << 4));
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(av), as_v8bf(xr[c][q]), acc[r], 0, 0, 0);
+    }
+    if constexpr (NP > PRE) __builtin_amdgcn_sched_barrier(0);  // no loads hoisted past the window
+  }
+
+  // T: lane (lr, lg) holds token lr, adapter rows 16 r + 4 lg + e; stage [wave][token][16]
+  // and add the waves in order
+  for (int r = 0; r < RT; ++r) {
+    *reinterpret_cast<float4*>(&part[wave][lr * 16 + 4 * lg]) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+    __syncthreads();
+    for (int i = tid; i < 256; i += 64 * waves) {  // i = 16 token + adapter row within the tile
+      const int n = i >> 4, j = i & 15;
+      float s = part[0][i];
+      for (int w = 1; w < waves; ++w) s += part[w][i];
+      if (n < rows && 16 * r + j < rank)
+        t[(int64_t)(m0 + n) * rank + 16 * r + j] = (uint16_t)(pack_bf16x2(scale * s, 0.0f) & 0xFFFFu);
+    }
+    __syncthreads();  // part is rewritten for the next tile
+  }
+}
+
+template <int RT>
+hipError_t run_down_fp8r(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+                         float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s) {
+  const int waves = (int)((K + 64 * kFusedChunks - 1) / (64 * kFusedChunks));
+  hipLaunchKernelGGL((lora_down_fp8r_kernel<RT>), dim3((unsigned)((M + 15) / 16)), dim3((unsigned)(64 * waves)), 0, s,
+                     x, ldx, a, (int)M, (int)K, rank, scale, t, xq, sx);
+  return hipGetLastError();
+}
+
 template <int RT>
 hipError_t run_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank, float scale,
                     const float* ga, const float* gb, float* part, uint16_t* t, const float* gq, uint8_t* xq,
@@ -282,6 +419,17 @@ int lora_down_slices(int64_t M, int64_t K, int rank) {
   if (z < 1) z = 1;
   const int64_t kr = lora_down_slice_k(K, (int)z);
   return (int)((K + kr - 1) / kr);  // no empty slice
+}
+
+bool lora_down_fp8r_supported(int64_t K) { return K <= 64 * kFusedChunks * kFusedWaves; }
+
+hipError_t launch_lora_down_fp8r(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+                                 float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s) {
+  if (!lora_down_fp8r_supported(K)) return hipErrorInvalidValue;
+  if (rank <= 16) return run_down_fp8r<1>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  if (rank <= 32) return run_down_fp8r<2>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  if (rank <= 64) return run_down_fp8r<4>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  return run_down_fp8r<8>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
 }
 
 hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,

@@ -16,19 +16,8 @@ namespace bsq {
 // Each lane owns the 16-byte chunks (8 bf16) c = lane + 64 i of the row. The
 // first NCH of them stay in registers between the amax pass and the encode
 // pass; chunks beyond 64 * NCH (rows longer than 512 * NCH) are read twice.
-__device__ __forceinline__ float absmax8(uint4 v) {
-  return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
-                     fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
-               fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
-                     fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
-}
-__device__ __forceinline__ uint2 encode8_fp8(uint4 v, float r) {
-  uint2 o;
-  o.x = enc_e4m3x4(bf16_lo(v.x) * r, bf16_hi(v.x) * r, bf16_lo(v.y) * r, bf16_hi(v.y) * r);
-  o.y = enc_e4m3x4(bf16_lo(v.z) * r, bf16_hi(v.z) * r, bf16_lo(v.w) * r, bf16_hi(v.w) * r);
-  return o;
-}
-
+// (absmax8 and encode8_fp8, the per-chunk steps, are shared with the fused
+// adapter kernel.)
 template <int NCH>
 __global__ __launch_bounds__(256) void quant_fp8r_rows(const uint16_t* __restrict__ x, int64_t M, int K,
                                                         int64_t ldx, uint8_t* __restrict__ xq,

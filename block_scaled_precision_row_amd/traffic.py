@@ -24,7 +24,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # the W4A4 kernel and every header it includes: a change to any of them makes a stored count stale
-SOURCES = [os.path.join(CSRC, f) for f in ("gemm_w4a4.hip", "gemm_common.hpp", "bsq_device.hpp", "bsq_launch.hpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("gemm_w4a4.hip", "gemm_common.hpp", "gemm_tiles.hpp", "bsq_device.hpp",
+                                            "bsq_launch.hpp")]
 
 
 def source_hash():

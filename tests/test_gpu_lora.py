@@ -201,3 +201,33 @@ def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, ran
     assert np.array_equal(got[:M * K // 2], host(xq).reshape(-1))
     off = pad(M * K // 2)
     assert np.array_equal(got[off:off + M * K // 16], host(xs).reshape(-1))
+
+
+# fp8r linears with K <= 3072 encode X and compute T in one kernel (16 whole rows a workgroup,
+# up to 8 waves of 384 K values); longer rows take the quantizer and the K-sliced projection.
+# Shapes: one wave with a half chunk (K = 96), ragged rows, 2 waves with a partial last chunk
+# (K = 544), a full workgroup (K = 3072) at 4096 tokens, and the unfused path (K = 4096).
+@pytest.mark.parametrize("M,N,K,rank", [(1, 64, 96, 5), (33, 128, 544, 16), (300, 256, 1056, 48),
+                                        (4096, 3072, 3072, 32), (70, 256, 3072, 128), (40, 128, 4096, 24)])
+def test_fp8r_workspace_holds_the_quantizer_output_and_t(M, N, K, rank):
+    """The fp8r W8A8 adapter path leaves in its workspace X's fp8r codes and row scales (bit for
+    bit what the activation quantizer writes) and T = bf16(s X A^T) (within the down
+    projection's bound), whichever kernels produced them."""
+    x, w, a, b = _inputs(M, N, K, rank, 4)
+    wq, sw = quant.quantize_fp8r(w)
+    dx = dev_bf16(x)
+    nbytes = L.bsq_lora_workspace_bytes(L.BSQ_FMT_FP8R, M, N, K, rank)
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    L.bsq_gemm_fp8r_lora(dx, dev(wq), dev(sw), dev_bf16(a), dev_bf16(b), SCALE, workspace=ws)
+    xq, sx = L.bsq_quantize_act_fp8r(dx)
+    torch.cuda.synchronize()
+    pad = lambda n: (n + 255) // 256 * 256
+    got = host(ws)
+    assert np.array_equal(got[:M * K], host(xq).reshape(-1))
+    off = pad(M * K)
+    assert np.array_equal(got[off:off + 4 * M].view(np.float32), host(sx).reshape(-1))
+    toff = L.bsq_gemm_workspace_bytes(L.BSQ_FMT_FP8R, M, N, K)
+    t = got[toff:toff + 2 * M * rank].view(np.uint16).reshape(M, rank)
+    ref = lora.lora_down(x, a, SCALE)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(np.abs(codec.bf16_to_f64(t) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms)

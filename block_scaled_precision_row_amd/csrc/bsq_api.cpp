@@ -522,8 +522,11 @@ bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a,
   if (need && (!workspace || workspace_bytes < need)) return BSQ_ERR_WORKSPACE;
   if (need && !aligned(workspace, 16)) return BSQ_ERR_ALIGN;
   if ((st = check_device()) != BSQ_OK) return st;
-  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr,
-                                       static_cast<float*>(workspace), t, stream);
+  hipError_t e = bsq::lora_down_rows_better(M, K, (int)rank)
+                     ? bsq::launch_lora_down_rows(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, nullptr, nullptr,
+                                                  stream)
+                     : bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr,
+                                             static_cast<float*>(workspace), t, stream);
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
@@ -544,10 +547,10 @@ bsq_status bsq_gemm_fp8r_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, 
   const bool weight_only = flags & BSQ_WEIGHT_ONLY;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* t = reinterpret_cast<uint16_t*>(ws + bsq_gemm_workspace_bytes(BSQ_FMT_FP8R, M, N, K, flags));
-  if (!weight_only && bsq::lora_down_fp8r_supported(K)) {
+  if (!weight_only && bsq::lora_down_fp8r_fused(M, K, (int)rank)) {
     // one kernel encodes X to fp8r (into the workspace, as the quantizer would) and computes T
     float* sx = reinterpret_cast<float*>(ws + pad256((size_t)(M * K)));
-    hipError_t e = bsq::launch_lora_down_fp8r(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, ws, sx, stream);
+    hipError_t e = bsq::launch_lora_down_rows(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, ws, sx, stream);
     if (e == hipSuccess) e = launch_w8a8(ws, sx, w, w_scale, y, ldy, M, N, K, stream, t, lora_b, (int)rank);
     return e == hipSuccess ? BSQ_OK : hip_fail(e);
   }

@@ -82,11 +82,15 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, i
                             float scale, const float* ga, const float* gb, float* part, uint16_t* t, hipStream_t s,
                             const float* gq = nullptr, uint8_t* xq = nullptr, uint8_t* xs = nullptr);
 
-// fp8r linears: the same down projection (f = scale) fused with X's fp8r encoding, one launch
-// that writes t, xq [M][K] and sx [M] (xq and sx bit for bit what launch_quant_fp8r writes);
-// K <= 3072 (lora_down_fp8r_supported), else hipErrorInvalidValue.
-bool lora_down_fp8r_supported(int64_t K);
-hipError_t launch_lora_down_fp8r(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+// The same down projection (f = scale) from whole rows, K <= 3072 (lora_down_rows_fits, else
+// hipErrorInvalidValue): one launch that writes t and, with xq != nullptr, X's fp8r encoding
+// xq [M][K] and sx [M] (bit for bit what launch_quant_fp8r writes). lora_down_fp8r_fused: the
+// fp8r linear takes it in place of the quantizer and the sliced kernel; lora_down_rows_better:
+// the down projection alone takes it in place of the sliced kernel.
+bool lora_down_rows_fits(int64_t K);
+bool lora_down_fp8r_fused(int64_t M, int64_t K, int rank);
+bool lora_down_rows_better(int64_t M, int64_t K, int rank);
+hipError_t launch_lora_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
                                  float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s);
 
 // Decode-to-16-bit GEMMs on the bf16 / f16 matrix cores.

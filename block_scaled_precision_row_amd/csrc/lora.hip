@@ -241,25 +241,29 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
   }
 }
 
-// ---- fp8r linears: the down projection fused with the activation encoding ---------
+// ---- whole rows: the down projection, optionally fused with the fp8r encoding ------------
 // The fp8r encoding of a row needs the row's maximum before any value is encoded, so it
 // cannot ride on the K-sliced kernel above. Here a workgroup owns 16 whole rows: each of its
 // (at most 8) waves holds 384 consecutive K values of all 16 rows in registers (six 64-deep
 // chunks; lane (lr, lg) holds the 16 values kc + 16 lg .. + 15 of row lr of chunk kc, the
-// layout of the kernel above), so X is read from HBM once and K <= 3072. (Twelve chunks a
-// wave, for K <= 6144, spill registers: longer rows take the unfused kernels.) The row maxima combine across the four lanes of a
-// row and then across the waves through LDS; each wave then encodes its values with the
-// quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))) and
-// multiplies the same registers into T on the matrix cores, with the adapter's chunks
-// read from L2 (A is the MFMA A operand, X the B operand). The waves' fp32 tiles are
-// added in wave order through LDS, one rank tile at a time, scaled and rounded to bf16.
-// One launch replaces the quantizer, the sliced down projection and its finishing pass.
+// layout of the kernel above), so X is read from HBM once and K <= 3072 (twelve chunks a
+// wave, for K <= 6144, spill registers). With ENC the row maxima combine across the four
+// lanes of a row and then across the waves through LDS, and each wave encodes its values
+// with the quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))).
+// Every wave multiplies the same registers into T on the matrix cores, with the adapter read
+// from L2 (A is the MFMA A operand, X the B operand). The waves' fp32 tiles are added in wave
+// order through LDS, one rank tile at a time, scaled and rounded to bf16. For an fp8r linear
+// one launch replaces the quantizer, the sliced down projection and its finishing pass.
+// Measured at 4096 x 3072 (us, no profiler): the quantizer alone 6.5; this kernel 9.1 / 11.7 /
+// 15.2 / 20.8 at rank 16 / 32 / 64 / 128; without the encoding 6.5 / 8.8 / 11.6 / 17.7; without
+// the adapter part 9.3 (rank 32). The phases add up because each compute unit holds one
+// workgroup (256 of them at 4096 rows): X's loads, then the encoded stores, then the adapter.
 constexpr int kFusedWaves = 8;   // at most; 256 registers a lane
 constexpr int kFusedChunks = 6;  // 64-deep chunks a wave
 constexpr int kRingSlots = 4;    // adapter pieces (16 rows x 64 values) staged at a time per wave
 
-template <int RT>
-__global__ __launch_bounds__(64 * kFusedWaves) void lora_down_fp8r_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+template <int RT, bool ENC>
+__global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                    const uint16_t* __restrict__ a, int M, int K,
                                                                    int rank, float scale,
                                                                    uint16_t* __restrict__ t,
@@ -306,28 +310,30 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_fp8r_kernel(const 
   }
 #pragma unroll
   for (int i = 0; i < PRE; ++i) load_a(i);
-  float amax = 0.0f;
+  if constexpr (ENC) {
+    float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) amax = fmaxf(amax, fmaxf(absmax8(xr[c][0]), absmax8(xr[c][1])));
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  if (lg == 0) red[wave][lr] = amax;
-  __syncthreads();  // every wave's row maxima are in red
+    for (int c = 0; c < NC; ++c) amax = fmaxf(amax, fmaxf(absmax8(xr[c][0]), absmax8(xr[c][1])));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    if (lg == 0) red[wave][lr] = amax;
+    __syncthreads();  // every wave's row maxima are in red
 
-  for (int w = 0; w < waves; ++w) amax = fmaxf(amax, red[w][lr]);
-  if (lr < rows) {
-    const float d = amax / kE4M3Max;
-    const float rc = d > 0.0f ? 1.0f / d : 0.0f;
-    uint8_t* qrow = xq + (int64_t)(m0 + lr) * K;
+    for (int w = 0; w < waves; ++w) amax = fmaxf(amax, red[w][lr]);
+    if (lr < rows) {
+      const float d = amax / kE4M3Max;
+      const float rc = d > 0.0f ? 1.0f / d : 0.0f;
+      uint8_t* qrow = xq + (int64_t)(m0 + lr) * K;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int k = kw0 + 64 * c + 16 * lg;
-      if (k < K) {
-        const uint2 lo = encode8_fp8(xr[c][0], rc), hi = encode8_fp8(xr[c][1], rc);
-        *reinterpret_cast<uint4*>(qrow + k) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      for (int c = 0; c < NC; ++c) {
+        const int k = kw0 + 64 * c + 16 * lg;
+        if (k < K) {
+          const uint2 lo = encode8_fp8(xr[c][0], rc), hi = encode8_fp8(xr[c][1], rc);
+          *reinterpret_cast<uint4*>(qrow + k) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
       }
+      if (wave == 0 && lg == 0) sx[m0 + lr] = d;
     }
-    if (wave == 0 && lg == 0) sx[m0 + lr] = d;
   }
 
   v4f acc[RT];
@@ -370,11 +376,16 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_fp8r_kernel(const 
 }
 
 template <int RT>
-hipError_t run_down_fp8r(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+hipError_t run_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
                          float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s) {
   const int waves = (int)((K + 64 * kFusedChunks - 1) / (64 * kFusedChunks));
-  hipLaunchKernelGGL((lora_down_fp8r_kernel<RT>), dim3((unsigned)((M + 15) / 16)), dim3((unsigned)(64 * waves)), 0, s,
-                     x, ldx, a, (int)M, (int)K, rank, scale, t, xq, sx);
+  const dim3 grid((unsigned)((M + 15) / 16)), block((unsigned)(64 * waves));
+  if (xq)
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, true>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank, scale,
+                       t, xq, sx);
+  else
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, false>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank, scale,
+                       t, xq, sx);
   return hipGetLastError();
 }
 
@@ -421,15 +432,30 @@ int lora_down_slices(int64_t M, int64_t K, int rank) {
   return (int)((K + kr - 1) / kr);  // no empty slice
 }
 
-bool lora_down_fp8r_supported(int64_t K) { return K <= 64 * kFusedChunks * kFusedWaves; }
+// Whole-row kernel or K-sliced kernel. Each whole-row workgroup reads all of A (r x K) from L2,
+// so its cost grows with rank x rounds of 256 workgroups (4096 rows), while the sliced kernel
+// shares each adapter stage among 128 rows but needs a finishing pass (and, on the fp8r path,
+// the separate quantizer). Measured at K = 3072 (us, sliced vs whole-row without encoding):
+// 4096 rows 10.2 / 12.1 / 15.1 / 27.3 vs 6.5 / 8.8 / 11.6 / 17.7 at rank 16 / 32 / 64 / 128;
+// 16384 rows 20.8 / 23.0 / 28.6 / 36.8 vs 19.9 / 33.7 / 44.9 / 67.8; 256-1024 rows about 7 / 8 /
+// 12 / 25 vs 6.4 / 8.4 / 11.2 / 17.0; 16 rows 5.6 / 6.0 / 8.3 / 17.0 vs 6.2 / 8.1 / 10.8 / 16.4.
+bool lora_down_rows_fits(int64_t K) { return K <= 64 * kFusedChunks * kFusedWaves; }
+bool lora_down_fp8r_fused(int64_t M, int64_t K, int rank) {
+  // with the encoding it replaces the quantizer too: up to 4096 rows at any rank, beyond that
+  // while one rank tile keeps the adapter reads short
+  return lora_down_rows_fits(K) && (M <= 4096 || rank <= 16);
+}
+bool lora_down_rows_better(int64_t M, int64_t K, int rank) {
+  return lora_down_rows_fits(K) && M >= 256 && M <= 4096 && (rank <= 16 || rank > 32 || M >= 2048);
+}
 
-hipError_t launch_lora_down_fp8r(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+hipError_t launch_lora_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
                                  float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s) {
-  if (!lora_down_fp8r_supported(K)) return hipErrorInvalidValue;
-  if (rank <= 16) return run_down_fp8r<1>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
-  if (rank <= 32) return run_down_fp8r<2>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
-  if (rank <= 64) return run_down_fp8r<4>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
-  return run_down_fp8r<8>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  if (!lora_down_rows_fits(K)) return hipErrorInvalidValue;
+  if (rank <= 16) return run_down_rows<1>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  if (rank <= 32) return run_down_rows<2>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  if (rank <= 64) return run_down_rows<4>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  return run_down_rows<8>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
 }
 
 hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,

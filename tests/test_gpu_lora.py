@@ -139,8 +139,11 @@ def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K
     assert np.array_equal(host(with_lora), host(plain))
 
 
+# The down projection alone takes the K-sliced kernel or, for 256-4096 rows with K <= 3072 (rank
+# 17-32 from 2048 rows), the whole-row kernel without the encoding.
 DOWN_SHAPES = [(1, 32, 1), (17, 96, 4), (64, 256, 48), (40, 512, 64), (33, 128, 128), (300, 3072, 32),
-               (4096, 3072, 32), (77, 12288, 16)]
+               (4096, 3072, 32), (77, 12288, 16), (256, 1024, 64), (2048, 544, 24), (512, 96, 128),
+               (300, 2048, 100), (1000, 3072, 16)]
 
 
 @pytest.mark.parametrize("M,K,rank", DOWN_SHAPES)
@@ -204,11 +207,13 @@ def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, ran
 
 
 # fp8r linears with K <= 3072 encode X and compute T in one kernel (16 whole rows a workgroup,
-# up to 8 waves of 384 K values); longer rows take the quantizer and the K-sliced projection.
-# Shapes: one wave with a half chunk (K = 96), ragged rows, 2 waves with a partial last chunk
-# (K = 544), a full workgroup (K = 3072) at 4096 tokens, and the unfused path (K = 4096).
+# up to 8 waves of 384 K values) up to 4096 rows, and beyond that at rank <= 16; otherwise the
+# quantizer and the K-sliced projection run. Shapes: one wave with a half chunk (K = 96), ragged
+# rows, 2 waves with a partial last chunk (K = 544), a full workgroup (K = 3072) at 4096 tokens,
+# 5000 tokens on both paths, and the unfused path for long rows (K = 4096).
 @pytest.mark.parametrize("M,N,K,rank", [(1, 64, 96, 5), (33, 128, 544, 16), (300, 256, 1056, 48),
-                                        (4096, 3072, 3072, 32), (70, 256, 3072, 128), (40, 128, 4096, 24)])
+                                        (4096, 3072, 3072, 32), (70, 256, 3072, 128), (40, 128, 4096, 24),
+                                        (5000, 256, 1024, 16), (5000, 256, 1024, 32)])
 def test_fp8r_workspace_holds_the_quantizer_output_and_t(M, N, K, rank):
     """The fp8r W8A8 adapter path leaves in its workspace X's fp8r codes and row scales (bit for
     bit what the activation quantizer writes) and T = bf16(s X A^T) (within the down
@@ -231,3 +236,22 @@ def test_fp8r_workspace_holds_the_quantizer_output_and_t(M, N, K, rank):
     ref = lora.lora_down(x, a, SCALE)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     assert np.all(np.abs(codec.bf16_to_f64(t) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms)
+
+
+def test_fp8r_fused_path_strided_input_and_determinism():
+    """The whole-row kernel reads X through its leading dimension (a column slice of a wider
+    tensor) and gives the same bits twice; the linear matches the oracle."""
+    M, N, K, ldx, rank = 45, 192, 1024, 1280, 20
+    xf = syn.normal_bf16((M, ldx), 63, 2)
+    w = syn.normal_bf16((N, K), 63, 3, sigma=0.02)
+    a, b = syn.lora_adapter(63, rank, N, K)
+    x = np.ascontiguousarray(xf[:, :K])
+    wq, sw = quant.quantize_fp8r(w)
+    dx = dev_bf16(xf)[:, :K]
+    y1 = host(L.bsq_gemm_fp8r_lora(dx, dev(wq), dev(sw), dev_bf16(a), dev_bf16(b), SCALE))
+    y2 = host(L.bsq_gemm_fp8r_lora(dx, dev(wq), dev(sw), dev_bf16(a), dev_bf16(b), SCALE))
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2)
+    xq, sx = quant.quantize_fp8r(x)
+    ref = lora.lora_linear(gemm.gemm_fp8r(xq, sx, wq, sw), x, a, b, SCALE)
+    assert_gemm_close(y1, ref, "fp8r strided x", extra=t_rounding_bound(x, a, b, SCALE))

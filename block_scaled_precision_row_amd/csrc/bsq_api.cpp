@@ -123,6 +123,13 @@ size_t ws_lora_down(int64_t M, int64_t K, int64_t rank) {
 float* lora_part(void* ws, int64_t M, int64_t rank) {
   return reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pad256((size_t)(M * rank * 2)));
 }
+// T = bf16(s X A^T) alone (no encoding of X), by whichever kernel is faster at this shape
+hipError_t lora_down_plain(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int64_t rank,
+                           float scale, uint16_t* t, float* part, hipStream_t s) {
+  if (bsq::lora_down_rows_pick(M, K, (int)rank, bsq::kDownPlain))
+    return bsq::launch_lora_down_rows(x, ldx, a, M, K, (int)rank, scale, nullptr, nullptr, t, bsq::RowsEncode{}, s);
+  return bsq::launch_lora_down(x, ldx, a, M, K, (int)rank, scale, nullptr, nullptr, part, t, s);
+}
 
 // adapter rules on top of the linear's: rank, scale, pointers, and the 32-bit buffer offsets
 // of the down-projection (32 rows of x) and up-projection (T and B rows) kernels
@@ -522,11 +529,7 @@ bsq_status bsq_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* lora_a,
   if (need && (!workspace || workspace_bytes < need)) return BSQ_ERR_WORKSPACE;
   if (need && !aligned(workspace, 16)) return BSQ_ERR_ALIGN;
   if ((st = check_device()) != BSQ_OK) return st;
-  hipError_t e = bsq::lora_down_rows_better(M, K, (int)rank)
-                     ? bsq::launch_lora_down_rows(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, nullptr, nullptr,
-                                                  stream)
-                     : bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr,
-                                             static_cast<float*>(workspace), t, stream);
+  hipError_t e = lora_down_plain(x, ldx, lora_a, M, K, rank, lora_scale, t, static_cast<float*>(workspace), stream);
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
@@ -547,15 +550,18 @@ bsq_status bsq_gemm_fp8r_lora(const uint16_t* x, int64_t ldx, const uint8_t* w, 
   const bool weight_only = flags & BSQ_WEIGHT_ONLY;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* t = reinterpret_cast<uint16_t*>(ws + bsq_gemm_workspace_bytes(BSQ_FMT_FP8R, M, N, K, flags));
-  if (!weight_only && bsq::lora_down_fp8r_fused(M, K, (int)rank)) {
+  if (!weight_only && bsq::lora_down_rows_pick(M, K, (int)rank, bsq::kDownFp8r)) {
     // one kernel encodes X to fp8r (into the workspace, as the quantizer would) and computes T
-    float* sx = reinterpret_cast<float*>(ws + pad256((size_t)(M * K)));
-    hipError_t e = bsq::launch_lora_down_rows(x, ldx, lora_a, M, K, (int)rank, lora_scale, t, ws, sx, stream);
-    if (e == hipSuccess) e = launch_w8a8(ws, sx, w, w_scale, y, ldy, M, N, K, stream, t, lora_b, (int)rank);
+    bsq::RowsEncode en;
+    en.enc = bsq::kDownFp8r;
+    en.xq = ws;
+    en.sx = reinterpret_cast<float*>(ws + pad256((size_t)(M * K)));
+    hipError_t e = bsq::launch_lora_down_rows(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr, t, en,
+                                              stream);
+    if (e == hipSuccess) e = launch_w8a8(ws, en.sx, w, w_scale, y, ldy, M, N, K, stream, t, lora_b, (int)rank);
     return e == hipSuccess ? BSQ_OK : hip_fail(e);
   }
-  hipError_t e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr,
-                                       lora_part(t, M, rank), t, stream);
+  hipError_t e = lora_down_plain(x, ldx, lora_a, M, K, rank, lora_scale, t, lora_part(t, M, rank), stream);
   if (e == hipSuccess) {
     if (weight_only) {
       bsq::DecArgs a{};
@@ -598,15 +604,25 @@ bsq_status bsq_gemm_nvfp4_lora(const uint16_t* x, int64_t ldx, const uint8_t* w,
   const bool pre = !weight_only && !route_skinny(bsq::kW4A4, a) && bsq::lora_pre_scaled_w4a4(a);
   hipError_t e;
   if (weight_only) {
-    e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, nullptr, nullptr, lora_part(t, M, rank), t,
-                              stream);
+    e = lora_down_plain(x, ldx, lora_a, M, K, rank, lora_scale, t, lora_part(t, M, rank), stream);
     if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A16, a, stream);
   } else {
     // one pass over X: the down projection also writes X's nvfp4 encoding for the GEMM
     uint8_t* xs = ws + pad256((size_t)(M * K / 2));
     a.xq = ws; a.xs = xs; a.gx = input_scale;
-    e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, pre ? input_scale : nullptr,
-                              pre ? w_scale2 : nullptr, lora_part(t, M, rank), t, stream, input_scale, ws, xs);
+    const float* ga = pre ? input_scale : nullptr;
+    const float* gb = pre ? w_scale2 : nullptr;
+    if (bsq::lora_down_rows_pick(M, K, (int)rank, bsq::kDownNvfp4)) {
+      bsq::RowsEncode en;
+      en.enc = bsq::kDownNvfp4;
+      en.xq = ws;
+      en.xs = xs;
+      en.gq = input_scale;
+      e = bsq::launch_lora_down_rows(x, ldx, lora_a, M, K, (int)rank, lora_scale, ga, gb, t, en, stream);
+    } else {
+      e = bsq::launch_lora_down(x, ldx, lora_a, M, K, (int)rank, lora_scale, ga, gb, lora_part(t, M, rank), t, stream,
+                                input_scale, ws, xs);
+    }
     if (e == hipSuccess) e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
   }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);

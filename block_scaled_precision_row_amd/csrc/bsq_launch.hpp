@@ -82,16 +82,24 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, i
                             float scale, const float* ga, const float* gb, float* part, uint16_t* t, hipStream_t s,
                             const float* gq = nullptr, uint8_t* xq = nullptr, uint8_t* xs = nullptr);
 
-// The same down projection (f = scale) from whole rows, K <= 3072 (lora_down_rows_fits, else
-// hipErrorInvalidValue): one launch that writes t and, with xq != nullptr, X's fp8r encoding
-// xq [M][K] and sx [M] (bit for bit what launch_quant_fp8r writes). lora_down_fp8r_fused: the
-// fp8r linear takes it in place of the quantizer and the sliced kernel; lora_down_rows_better:
-// the down projection alone takes it in place of the sliced kernel.
+// The same down projection (same f) from whole rows of X, K <= 3072 (lora_down_rows_fits, else
+// hipErrorInvalidValue), optionally writing X's encoding for the GEMM in the same pass, bit
+// for bit what the activation quantizers write: fp8r (xq [M][K], sx [M]) or nvfp4 (xq
+// [M][K/2], xs [M][K/16], global scale *gq). lora_down_rows_pick: whether it beats the sliced
+// kernel (with the encoding, the sliced kernel plus the quantizer for fp8r) at this shape.
+enum DownEnc : int { kDownPlain = 0, kDownFp8r = 1, kDownNvfp4 = 2 };
+struct RowsEncode {
+  DownEnc enc = kDownPlain;
+  uint8_t* xq = nullptr;
+  float* sx = nullptr;
+  uint8_t* xs = nullptr;
+  const float* gq = nullptr;
+};
 bool lora_down_rows_fits(int64_t K);
-bool lora_down_fp8r_fused(int64_t M, int64_t K, int rank);
-bool lora_down_rows_better(int64_t M, int64_t K, int rank);
+bool lora_down_rows_pick(int64_t M, int64_t K, int rank, DownEnc enc);
 hipError_t launch_lora_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
-                                 float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s);
+                                 float scale, const float* ga, const float* gb, uint16_t* t, const RowsEncode& en,
+                                 hipStream_t s);
 
 // Decode-to-16-bit GEMMs on the bf16 / f16 matrix cores.
 enum DecMode : int {

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
   }
 }
 
-// ---- whole rows: the down projection, optionally fused with the fp8r encoding ------------
+// ---- whole rows: the down projection, optionally fused with X's encoding -----------------
 // The fp8r encoding of a row needs the row's maximum before any value is encoded, so it
 // cannot ride on the K-sliced kernel above. Here a workgroup owns 16 whole rows: each of its
 // (at most 8) waves holds 384 consecutive K values of all 16 rows in registers (six 64-deep
@@ -250,7 +250,9 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
 // wave, for K <= 6144, spill registers). With ENC the row maxima combine across the four
 // lanes of a row and then across the waves through LDS, and each wave encodes its values
 // with the quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))).
-// Every wave multiplies the same registers into T on the matrix cores, with the adapter read
+// The nvfp4 encoding needs no row maximum: a lane's 16 values of a chunk are one block, encoded
+// by the quantizer's block function (and without the K slices' finishing pass this kernel
+// beats the sliced one at most shapes). Every wave multiplies the same registers into T on the matrix cores, with the adapter read
 // from L2 (A is the MFMA A operand, X the B operand). The waves' fp32 tiles are added in wave
 // order through LDS, one rank tile at a time, scaled and rounded to bf16. For an fp8r linear
 // one launch replaces the quantizer, the sliced down projection and its finishing pass.
@@ -262,13 +264,13 @@ constexpr int kFusedWaves = 8;   // at most; 256 registers a lane
 constexpr int kFusedChunks = 6;  // 64-deep chunks a wave
 constexpr int kRingSlots = 4;    // adapter pieces (16 rows x 64 values) staged at a time per wave
 
-template <int RT, bool ENC>
+template <int RT, DownEnc ENC>
 __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                    const uint16_t* __restrict__ a, int M, int K,
-                                                                   int rank, float scale,
-                                                                   uint16_t* __restrict__ t,
-                                                                   uint8_t* __restrict__ xq,
-                                                                   float* __restrict__ sx) {
+                                                                   int rank, float scale, const float* ga,
+                                                                   const float* gb, uint16_t* __restrict__ t,
+                                                                   uint8_t* __restrict__ xq, float* __restrict__ sx,
+                                                                   uint8_t* __restrict__ xs, const float* gq) {
   constexpr int WMAX = kFusedWaves, NC = kFusedChunks, KW = 64 * NC;
   __shared__ float red[WMAX][16];
   __shared__ __attribute__((aligned(16))) float part[WMAX][16 * 16];
@@ -294,13 +296,13 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   // combined and X is encoded.
   constexpr int NP = NC * RT, PRE = NP <= 12 ? NP : 8;
   const int gr = lane >> 3, gp = lane & 7;  // this lane's row (and row + 8) and piece of a load
-  uint4 xr[NC][2], ga[NP][2];
+  uint4 xr[NC][2], aw[NP][2];
   auto load_a = [&](int i) {
     const int c = i / RT, r = i % RT;
     const int k = kw0 + 64 * c + 8 * gp;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      ga[i][h] = bload16(ra, k < K ? (uint32_t)((16 * r + 8 * h + gr) * K + k) * 2u : kBufOut);
+      aw[i][h] = bload16(ra, k < K ? (uint32_t)((16 * r + 8 * h + gr) * K + k) * 2u : kBufOut);
   };
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   }
 #pragma unroll
   for (int i = 0; i < PRE; ++i) load_a(i);
-  if constexpr (ENC) {
+  if constexpr (ENC == kDownFp8r) {
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) amax = fmaxf(amax, fmaxf(absmax8(xr[c][0]), absmax8(xr[c][1])));
@@ -335,6 +337,25 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
       if (wave == 0 && lg == 0) sx[m0 + lr] = d;
     }
   }
+  if constexpr (ENC == kDownNvfp4) {
+    // a lane's 16 values of a chunk are one 16-element block: encoded as the quantizer does
+    if (lr < rows) {
+      const float G = 1.0f / gq[0];
+      const int64_t row = m0 + lr;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int k = kw0 + 64 * c + 16 * lg;
+        if (k < K) {
+          float fv[16];
+          bf16x16_to_f32(xr[c][0], xr[c][1], fv);
+          uint2 codes;
+          const uint32_t sf = quant_block16_nvfp4(fv, G, codes);
+          *reinterpret_cast<uint2*>(xq + row * (K >> 1) + (k >> 1)) = codes;
+          xs[row * (K >> 4) + (k >> 4)] = (uint8_t)sf;
+        }
+      }
+    }
+  }
 
   v4f acc[RT];
 #pragma unroll
@@ -348,7 +369,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 8 * h + gr;
-      *reinterpret_cast<uint4*>(slot + row * 128 + ((gp ^ (row & 7)) << 4)) = ga[i][h];
+      *reinterpret_cast<uint4*>(slot + row * 128 + ((gp ^ (row & 7)) << 4)) = aw[i][h];
     }
     // lane (lr, lg): row lr, values 16 lg + 8 q of the chunk, as in xr[c][q]
 #pragma unroll
@@ -361,6 +382,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
 
   // T: lane (lr, lg) holds token lr, adapter rows 16 r + 4 lg + e; stage [wave][token][16]
   // and add the waves in order
+  const float f = out_factor(scale, ga, gb);
   for (int r = 0; r < RT; ++r) {
     *reinterpret_cast<float4*>(&part[wave][lr * 16 + 4 * lg]) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
     __syncthreads();
@@ -369,7 +391,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
       float s = part[0][i];
       for (int w = 1; w < waves; ++w) s += part[w][i];
       if (n < rows && 16 * r + j < rank)
-        t[(int64_t)(m0 + n) * rank + 16 * r + j] = (uint16_t)(pack_bf16x2(scale * s, 0.0f) & 0xFFFFu);
+        t[(int64_t)(m0 + n) * rank + 16 * r + j] = (uint16_t)(pack_bf16x2(f * s, 0.0f) & 0xFFFFu);
     }
     __syncthreads();  // part is rewritten for the next tile
   }
@@ -377,15 +399,19 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
 
 template <int RT>
 hipError_t run_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
-                         float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s) {
+                         float scale, const float* ga, const float* gb, uint16_t* t, const RowsEncode& en,
+                         hipStream_t s) {
   const int waves = (int)((K + 64 * kFusedChunks - 1) / (64 * kFusedChunks));
   const dim3 grid((unsigned)((M + 15) / 16)), block((unsigned)(64 * waves));
-  if (xq)
-    hipLaunchKernelGGL((lora_down_rows_kernel<RT, true>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank, scale,
-                       t, xq, sx);
+  if (en.enc == kDownFp8r)
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownFp8r>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
+                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
+  else if (en.enc == kDownNvfp4)
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownNvfp4>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
+                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
   else
-    hipLaunchKernelGGL((lora_down_rows_kernel<RT, false>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank, scale,
-                       t, xq, sx);
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownPlain>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
+                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
   return hipGetLastError();
 }
 
@@ -440,22 +466,26 @@ int lora_down_slices(int64_t M, int64_t K, int rank) {
 // 16384 rows 20.8 / 23.0 / 28.6 / 36.8 vs 19.9 / 33.7 / 44.9 / 67.8; 256-1024 rows about 7 / 8 /
 // 12 / 25 vs 6.4 / 8.4 / 11.2 / 17.0; 16 rows 5.6 / 6.0 / 8.3 / 17.0 vs 6.2 / 8.1 / 10.8 / 16.4.
 bool lora_down_rows_fits(int64_t K) { return K <= 64 * kFusedChunks * kFusedWaves; }
-bool lora_down_fp8r_fused(int64_t M, int64_t K, int rank) {
-  // with the encoding it replaces the quantizer too: up to 4096 rows at any rank, beyond that
-  // while one rank tile keeps the adapter reads short
-  return lora_down_rows_fits(K) && (M <= 4096 || rank <= 16);
-}
-bool lora_down_rows_better(int64_t M, int64_t K, int rank) {
-  return lora_down_rows_fits(K) && M >= 256 && M <= 4096 && (rank <= 16 || rank > 32 || M >= 2048);
+bool lora_down_rows_pick(int64_t M, int64_t K, int rank, DownEnc enc) {
+  if (!lora_down_rows_fits(K)) return false;
+  if (M > 4096) return rank <= 16;  // one rank tile keeps the adapter reads short
+  // fp8r: the fused kernel also replaces the quantizer's launch
+  if (enc == kDownFp8r) return true;
+  // nvfp4 (the sliced kernel encodes too, with a finishing pass) and no encoding: below 256
+  // rows the sliced kernel's spread over K wins up to rank 64 (16 x 12288 x 3072 nvfp4 linear,
+  // rank 16: 23.0 us against 25.2), and without an encoding at ranks 17-32 below 2048 rows
+  if (M < 256) return rank > 64;
+  return enc == kDownNvfp4 || rank <= 16 || rank > 32 || M >= 2048;
 }
 
 hipError_t launch_lora_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
-                                 float scale, uint16_t* t, uint8_t* xq, float* sx, hipStream_t s) {
+                                 float scale, const float* ga, const float* gb, uint16_t* t, const RowsEncode& en,
+                                 hipStream_t s) {
   if (!lora_down_rows_fits(K)) return hipErrorInvalidValue;
-  if (rank <= 16) return run_down_rows<1>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
-  if (rank <= 32) return run_down_rows<2>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
-  if (rank <= 64) return run_down_rows<4>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
-  return run_down_rows<8>(x, ldx, a, M, K, rank, scale, t, xq, sx, s);
+  if (rank <= 16) return run_down_rows<1>(x, ldx, a, M, K, rank, scale, ga, gb, t, en, s);
+  if (rank <= 32) return run_down_rows<2>(x, ldx, a, M, K, rank, scale, ga, gb, t, en, s);
+  if (rank <= 64) return run_down_rows<4>(x, ldx, a, M, K, rank, scale, ga, gb, t, en, s);
+  return run_down_rows<8>(x, ldx, a, M, K, rank, scale, ga, gb, t, en, s);
 }
 
 hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,

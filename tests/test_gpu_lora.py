@@ -139,8 +139,8 @@ def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K
     assert np.array_equal(host(with_lora), host(plain))
 
 
-# The down projection alone takes the K-sliced kernel or, for 256-4096 rows with K <= 3072 (rank
-# 17-32 from 2048 rows), the whole-row kernel without the encoding.
+# The down projection alone takes the K-sliced kernel or, with K <= 3072, the whole-row kernel
+# without the encoding: for 256-4096 rows (rank 17-32 from 2048 rows), below 256 rows from rank 65.
 DOWN_SHAPES = [(1, 32, 1), (17, 96, 4), (64, 256, 48), (40, 512, 64), (33, 128, 128), (300, 3072, 32),
                (4096, 3072, 32), (77, 12288, 16), (256, 1024, 64), (2048, 544, 24), (512, 96, 128),
                (300, 2048, 100), (1000, 3072, 16)]
@@ -183,12 +183,15 @@ def test_empty_batch_is_a_noop():
     assert y.shape == (0, 64)
 
 
+# The K-sliced kernel (20 x 512 r32, 130 x 160 r48, 5000 x 1024 r32) or the whole-row kernel
+# (the others) writes the encoding.
 @pytest.mark.parametrize("M,N,K,rank", [(300, 512, 512, 16), (4096, 3072, 3072, 32), (20, 1024, 512, 32),
-                                        (130, 200, 160, 48), (257, 300, 544, 128)])
+                                        (130, 200, 160, 48), (257, 300, 544, 128), (16, 256, 96, 100),
+                                        (5000, 256, 1024, 16), (5000, 256, 1024, 32)])
 def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, rank):
     """The W4A4 path encodes X to nvfp4 inside its down projection: the workspace's first two
     parts (packed codes, then block scales, each padded to 256 bytes) must equal the activation
-    quantizer's output bit for bit."""
+    quantizer's output bit for bit, and the linear must match the oracle."""
     x, w, a, b = _inputs(M, N, K, rank, 3)
     gw = quant.calibrate_global_scale(w)
     wq, sfw = quant.quantize_nvfp4(w, gw)
@@ -196,7 +199,8 @@ def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, ran
     dx = dev_bf16(x)
     nbytes = L.bsq_lora_workspace_bytes(L.BSQ_FMT_NVFP4, M, N, K, rank)
     ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
-    L.bsq_gemm_nvfp4_lora(dx, dev(wq), dev(sfw), dev_scalar(gw), gx, dev_bf16(a), dev_bf16(b), SCALE, workspace=ws)
+    y = L.bsq_gemm_nvfp4_lora(dx, dev(wq), dev(sfw), dev_scalar(gw), gx, dev_bf16(a), dev_bf16(b), SCALE,
+                              workspace=ws)
     xq, xs = L.bsq_quantize_act_nvfp4(dx, gx)
     torch.cuda.synchronize()
     pad = lambda n: (n + 255) // 256 * 256
@@ -204,6 +208,12 @@ def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, ran
     assert np.array_equal(got[:M * K // 2], host(xq).reshape(-1))
     off = pad(M * K // 2)
     assert np.array_equal(got[off:off + M * K // 16], host(xs).reshape(-1))
+    rows = _rows_subset(M, 300, 11)
+    gxh = quant.calibrate_global_scale(x)
+    xq_o, sfx_o = quant.quantize_nvfp4(x[rows], gxh)
+    ref = lora.lora_linear(gemm.gemm_nvfp4(xq_o, sfx_o, gxh, wq, sfw, gw), x[rows], a, b, SCALE)
+    assert_gemm_close(host(y)[rows], ref, "nvfp4 %dx%dx%d r%d" % (M, N, K, rank),
+                      extra=t_rounding_bound(x[rows], a, b, SCALE))
 
 
 # fp8r linears with K <= 3072 encode X and compute T in one kernel (16 whole rows a workgroup,

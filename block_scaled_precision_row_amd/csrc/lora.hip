@@ -291,9 +291,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   // eight lanes per 128-byte row segment (whole lines per load; in the MFMA layout the lanes
   // of a quarter wave would each address a different row) and staged through a ring of
   // kRingSlots pieces in this wave's LDS, XOR-swizzled by row, from which each lane reads its
-  // MFMA operands. The
-  // first PRE pieces are requested with X, so that they arrive while the row maxima are
-  // combined and X is encoded.
+  // MFMA operands. The first PRE pieces are requested with X, so that they arrive while the
+  // row maxima are combined and X is encoded.
   constexpr int NP = NC * RT, PRE = NP <= 12 ? NP : 8;
   const int gr = lane >> 3, gp = lane & 7;  // this lane's row (and row + 8) and piece of a load
   uint4 xr[NC][2], aw[NP][2];

@@ -369,11 +369,11 @@ __device__ __forceinline__ void read_bf16(OpBf& o, const uint8_t* codes, int lr,
   for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
 }
 
-template <int MODE, int MB, bool LORA>
-__global__ __launch_bounds__(64 * kSkStagedWaves) void gemm_skinny_staged_kernel(DecArgs a) {
+template <int MODE, int MB, bool LORA, int NWV = kSkStagedWaves>
+__global__ __launch_bounds__(64 * NWV) void gemm_skinny_staged_kernel(DecArgs a) {
   static_assert(MODE == kW4A4 || MODE == kW4A16, "nvfp4 weights only");
   using S = Scheme<MODE>;
-  constexpr int NW = kSkStagedWaves;
+  constexpr int NW = NWV;
   constexpr bool XBF = MODE == kW4A16;
   using RawX = typename std::conditional<XBF, RawBf, RawNv>::type;
   constexpr int NV_BYTES = 32 * 64 + 256;                   // codes + scales of one nvfp4 operand
@@ -637,15 +637,15 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gemm_skinny_kernel<MODE, MB, NW, false>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
-template <int MODE, int MB>
+template <int MODE, int MB, int NW = kSkStagedWaves>
 hipError_t run_staged(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = ((a.N + 31) / 32) * ((a.M + 32 * MB - 1) / (32 * MB));
   if (a.lt)
-    hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB, true>), dim3((unsigned)blocks),
-                       dim3(64 * kSkStagedWaves), 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB, true, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB, false>), dim3((unsigned)blocks),
-                       dim3(64 * kSkStagedWaves), 0, s, a);
+    hipLaunchKernelGGL((gemm_skinny_staged_kernel<MODE, MB, false, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s,
+                       a);
   return hipGetLastError();
 }
 
@@ -658,7 +658,14 @@ hipError_t pick(const DecArgs& a, hipStream_t s) {
   // 13.1 vs 14.2 us), which halve its weight decodes per output.
   const bool short_grid = ((a.N + 31) / 32) * ((a.M + 63) / 64) < 256;
   if constexpr (MODE == kW4A4) {
-    if (a.M <= 64) return run_staged<MODE, 1>(a, s);
+    // With a full grid (>= 256 workgroups) and 16 or more tokens, four waves per workgroup
+    // (twice the stages each, more workgroups per compute unit) beat eight: cold weights,
+    // K = 3072, N = 12288: 16 / 32 / 64 tokens 12.7 / 15.8 / 20.5 -> 12.3 / 14.5 / 19.3 us; at
+    // N = 3072 (96 workgroups) and for a single token eight stay ahead (8.0 vs 8.5, 10.7 vs 11.3).
+    if (a.M <= 64) {
+      if (a.M >= 16 && (a.N + 31) / 32 >= 256) return run_staged<MODE, 1, 4>(a, s);
+      return run_staged<MODE, 1>(a, s);
+    }
     return run_staged<MODE, 2>(a, s);
   } else if constexpr (MODE == kW4A16) {
     // bf16 activations fill registers and LDS fastest: one activation block per workgroup

@@ -186,9 +186,10 @@ def test_prequantized_activation_entry_points(M, N, K):
 
 # Few tokens: these shapes run on the skinny kernel (K split over the waves of a workgroup);
 # K values chosen so that stages end inside a lane's window (544 = 4 * 128 + 32) and waves
-# without any stage exist (K = 96, 224).
+# without any stage exist (K = 96, 224). 40 x 8200 x 544 runs the four-wave W4A4 variant
+# (>= 256 workgroups, >= 16 tokens) with a ragged weight block.
 SKINNY_SHAPES = [(16, 3072, 3072), (33, 1000, 544), (64, 3072, 3072), (96, 520, 224), (160, 3072, 3072),
-                 (256, 1056, 96), (5, 12288, 3072)]
+                 (256, 1056, 96), (5, 12288, 3072), (40, 8200, 544)]
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)

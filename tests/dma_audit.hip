@@ -270,6 +270,8 @@ int main() {
     audit_skinny<kW8A8, 1, 4>(s[0], s[1], s[2], s[3]);
     audit_skinny<kW8A8, 2, 4>(s[0], s[1], s[2], s[3]);
     audit_skinny<kW8A16, 1, 4>(s[0], s[1], s[2], s[3]);
+    audit_skinny<kW8A8, 1, 8>(s[0], s[1], s[2], s[3]);
+    audit_skinny<kW8A16, 1, 2>(s[0], s[1], s[2], s[3]);
   }
   std::printf("all LDS-DMA loads in bounds: %ld lanes checked\n", g_lanes);
   return 0;

@@ -265,3 +265,27 @@ def test_fp8r_fused_path_strided_input_and_determinism():
     xq, sx = quant.quantize_fp8r(x)
     ref = lora.lora_linear(gemm.gemm_fp8r(xq, sx, wq, sw), x, a, b, SCALE)
     assert_gemm_close(y1, ref, "fp8r strided x", extra=t_rounding_bound(x, a, b, SCALE))
+
+
+def test_nvfp4_whole_row_path_strided_input():
+    """The nvfp4 linear's whole-row down projection (300 rows, rank 16) reads X through its
+    leading dimension, encodes it as the quantizer does and matches the oracle."""
+    M, N, K, ldx, rank = 300, 256, 512, 640, 16
+    xf = syn.normal_bf16((M, ldx), 64, 4)
+    w = syn.normal_bf16((N, K), 64, 5, sigma=0.02)
+    a, b = syn.lora_adapter(64, rank, N, K)
+    x = np.ascontiguousarray(xf[:, :K])
+    gw = quant.calibrate_global_scale(w)
+    wq, sfw = quant.quantize_nvfp4(w, gw)
+    gxh = quant.calibrate_global_scale(x)
+    dx = dev_bf16(xf)[:, :K]
+    nbytes = L.bsq_lora_workspace_bytes(L.BSQ_FMT_NVFP4, M, N, K, rank)
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
+    y = L.bsq_gemm_nvfp4_lora(dx, dev(wq), dev(sfw), dev_scalar(gw), dev_scalar(gxh), dev_bf16(a), dev_bf16(b),
+                              SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    xq_o, sfx_o = quant.quantize_nvfp4(x, gxh)
+    got = host(ws)
+    assert np.array_equal(got[:M * K // 2], xq_o.reshape(-1))
+    ref = lora.lora_linear(gemm.gemm_nvfp4(xq_o, sfx_o, gxh, wq, sfw, gw), x, a, b, SCALE)
+    assert_gemm_close(host(y), ref, "nvfp4 strided x", extra=t_rounding_bound(x, a, b, SCALE))

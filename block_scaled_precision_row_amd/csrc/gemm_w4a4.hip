@@ -67,10 +67,10 @@ __device__ __forceinline__ void read_scales(const uint8_t* st, int sa_off, int s
   for (int j = 0; j < TM; ++j) sb[j] = *reinterpret_cast<const uint2*>(st + sb_off + (rowb + j * 32) * 16 + 8 * lh);
 }
 
-// block scale byte b (0..3) of `s` as an f16 pair (E4M3 -> f16 is exact)
-__device__ __forceinline__ v2h scale_pair(uint32_t s, int b) {
-  const uint32_t dup = __builtin_amdgcn_perm(s, s, 0x01010101u * (uint32_t)b);
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dup, 1.0f, false);
+// block scale bytes 2 hi and 2 hi + 1 of `s` as f16 (E4M3 -> f16 is exact)
+__device__ __forceinline__ v2h scale_pairs(uint32_t s, int hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
 }
 
 __device__ __forceinline__ uint32_t h2u(v2h v) {
@@ -140,18 +140,19 @@ void gemm_w4a4_kernel(DecArgs a) {
   v2h spa[TN][2], spb[TM][2];              // block-scale pairs of the K group being decoded
 
   // scale pairs of K group q from the stage's scale bytes (bytes 2q, 2q + 1 of the lane's 8)
+  // (one conversion gives both scales of the group; the multiplies broadcast one half of it)
   auto scales_of = [&](const uint2 (&sa)[TN], const uint2 (&sb)[TM], int q) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-      const uint32_t w = q < 2 ? sa[i].x : sa[i].y;
-      spa[i][0] = scale_pair(w, (2 * q) & 3);
-      spa[i][1] = scale_pair(w, (2 * q + 1) & 3);
+      const v2h p = scale_pairs(q < 2 ? sa[i].x : sa[i].y, q & 1);
+      spa[i][0] = v2h{p.x, p.x};
+      spa[i][1] = v2h{p.y, p.y};
     }
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const uint32_t w = q < 2 ? sb[j].x : sb[j].y;
-      spb[j][0] = scale_pair(w, (2 * q) & 3);
-      spb[j][1] = scale_pair(w, (2 * q + 1) & 3);
+      const v2h p = scale_pairs(q < 2 ? sb[j].x : sb[j].y, q & 1);
+      spb[j][0] = v2h{p.x, p.x};
+      spb[j][1] = v2h{p.y, p.y};
     }
   };
   auto decode_step = [&](auto tc, const Raw (&ra)[TN], const Raw (&rb)[TM], v8h (&da)[TN], v8h (&db)[TM]) {

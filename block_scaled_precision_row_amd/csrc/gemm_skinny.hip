@@ -668,7 +668,10 @@ hipError_t pick(const DecArgs& a, hipStream_t s) {
     }
     return run_staged<MODE, 2>(a, s);
   } else if constexpr (MODE == kW4A16) {
-    // bf16 activations fill registers and LDS fastest: one activation block per workgroup
+    // bf16 activations fill registers and LDS fastest: one activation block per workgroup; on a
+    // full grid four waves (N = 12288: 1 / 16 / 32 tokens 14.4 / 17.4 / 21.1 -> 13.0 / 14.8 /
+    // 17.4 us; at N = 3072 eight stay ahead, 9.2 vs 10.4 at 16 tokens)
+    if ((a.N + 31) / 32 >= 256) return run_staged<MODE, 1, 4>(a, s);
     return run_staged<MODE, 1>(a, s);
   } else if constexpr (MODE == kW8A16) {
     // two waves per workgroup once the grid fills the compute units (cold weights, K = 3072,

@@ -187,7 +187,7 @@ def test_prequantized_activation_entry_points(M, N, K):
 # Few tokens: these shapes run on the skinny kernel (K split over the waves of a workgroup);
 # K values chosen so that stages end inside a lane's window (544 = 4 * 128 + 32) and waves
 # without any stage exist (K = 96, 224). Wave counts per workgroup other than the default:
-# 40 x 8200 x 544 runs the four-wave W4A4 variant (>= 256 workgroups, >= 16 tokens), 3 x 8200 x
+# 40 x 8200 x 544 runs the four-wave W4A4 and W4A16 variants (>= 256 workgroups), 3 x 8200 x
 # 1056 and 5 x 12288 x 3072 the two-wave W8A16 one (>= 256 workgroups, <= 16 tokens), 7 x 700 x
 # 544 the eight-wave W8A8 one (<= 8 tokens, small grid), all with ragged weight blocks.
 SKINNY_SHAPES = [(16, 3072, 3072), (33, 1000, 544), (64, 3072, 3072), (96, 520, 224), (160, 3072, 3072),

@@ -94,6 +94,7 @@ ROUTE_SHAPES = [
     (300, 520, 96, 24),     # decode GEMM for W4A4 (K % 256 != 0), ragged N, rank % 16 != 0
     (257, 300, 544, 128),   # largest rank, ragged everything
     (130, 200, 160, 48),    # decode GEMM W4A4, few-token fp8
+    (16, 8200, 512, 24),    # few-token kernels on a full grid (fewer waves per workgroup), ragged N
 ]
 
 

@@ -250,12 +250,13 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
 // wave, for K <= 6144, spill registers). With ENC the row maxima combine across the four
 // lanes of a row and then across the waves through LDS, and each wave encodes its values
 // with the quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))).
-// The nvfp4 encoding needs no row maximum: a lane's 16 values of a chunk are one block, encoded
-// by the quantizer's block function (and without the K slices' finishing pass this kernel
-// beats the sliced one at most shapes). Every wave multiplies the same registers into T on the matrix cores, with the adapter read
-// from L2 (A is the MFMA A operand, X the B operand). The waves' fp32 tiles are added in wave
-// order through LDS, one rank tile at a time, scaled and rounded to bf16. For an fp8r linear
-// one launch replaces the quantizer, the sliced down projection and its finishing pass.
+// The nvfp4 encoding needs no row maximum: a lane's 16 values of a chunk are one block,
+// encoded by the quantizer's block function (without the K slices' finishing pass this kernel
+// beats the sliced one at most shapes). Every wave multiplies the same registers into T on
+// the matrix cores, with the adapter read from L2 (A is the MFMA A operand, X the B operand).
+// The waves' fp32 tiles are added in wave order through LDS, one rank tile at a time, scaled
+// and rounded to bf16. For an fp8r linear one launch replaces the quantizer, the sliced down
+// projection and its finishing pass.
 // Measured at 4096 x 3072 (us, no profiler): the quantizer alone 6.5; this kernel 9.1 / 11.7 /
 // 15.2 / 20.8 at rank 16 / 32 / 64 / 128; without the encoding 6.5 / 8.8 / 11.6 / 17.7; without
 // the adapter part 9.3 (rank 32). The phases add up because each compute unit holds one

@@ -82,7 +82,7 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t ldx, const uint16_t* a, i
                             float scale, const float* ga, const float* gb, float* part, uint16_t* t, hipStream_t s,
                             const float* gq = nullptr, uint8_t* xq = nullptr, uint8_t* xs = nullptr);
 
-// The same down projection (same f) from whole rows of X, K <= 3072 (lora_down_rows_fits, else
+// The same down projection (same f) from whole rows of X, K <= 6144 (lora_down_rows_fits, else
 // hipErrorInvalidValue), optionally writing X's encoding for the GEMM in the same pass, bit
 // for bit what the activation quantizers write: fp8r (xq [M][K], sx [M]) or nvfp4 (xq
 // [M][K/2], xs [M][K/16], global scale *gq). lora_down_rows_pick: whether it beats the sliced

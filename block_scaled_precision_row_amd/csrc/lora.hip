@@ -244,10 +244,11 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
 // ---- whole rows: the down projection, optionally fused with X's encoding -----------------
 // The fp8r encoding of a row needs the row's maximum before any value is encoded, so it
 // cannot ride on the K-sliced kernel above. Here a workgroup owns 16 whole rows: each of its
-// (at most 8) waves holds 384 consecutive K values of all 16 rows in registers (six 64-deep
-// chunks; lane (lr, lg) holds the 16 values kc + 16 lg .. + 15 of row lr of chunk kc, the
-// layout of the kernel above), so X is read from HBM once and K <= 3072 (twelve chunks a
-// wave, for K <= 6144, spill registers). With ENC the row maxima combine across the four
+// (at most 8) waves holds 64 NC consecutive K values of all 16 rows in registers (NC = 6
+// 64-deep chunks for K <= 3072, 12 for K <= 6144; lane (lr, lg) holds the 16 values
+// kc + 16 lg .. + 15 of row lr of chunk kc, the layout of the kernel above), so X is read from
+// HBM once (with twelve chunks and the fp8r encoding, four registers a lane spill outside the
+// adapter loop, and fewer adapter pieces are requested ahead). With ENC the row maxima combine across the four
 // lanes of a row and then across the waves through LDS, and each wave encodes its values
 // with the quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))).
 // The nvfp4 encoding needs no row maximum: a lane's 16 values of a chunk are one block,
@@ -261,18 +262,18 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
 // 15.2 / 20.8 at rank 16 / 32 / 64 / 128; without the encoding 6.5 / 8.8 / 11.6 / 17.7; without
 // the adapter part 9.3 (rank 32). The phases add up because each compute unit holds one
 // workgroup (256 of them at 4096 rows): X's loads, then the encoded stores, then the adapter.
-constexpr int kFusedWaves = 8;   // at most; 256 registers a lane
-constexpr int kFusedChunks = 6;  // 64-deep chunks a wave
+constexpr int kFusedWaves = 8;      // at most; 256 registers a lane
+constexpr int kFusedMaxChunks = 12;  // 64-deep chunks a wave (6 up to K = 3072)
 constexpr int kRingSlots = 4;    // adapter pieces (16 rows x 64 values) staged at a time per wave
 
-template <int RT, DownEnc ENC>
+template <int RT, DownEnc ENC, int NC>
 __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                    const uint16_t* __restrict__ a, int M, int K,
                                                                    int rank, float scale, const float* ga,
                                                                    const float* gb, uint16_t* __restrict__ t,
                                                                    uint8_t* __restrict__ xq, float* __restrict__ sx,
                                                                    uint8_t* __restrict__ xs, const float* gq) {
-  constexpr int WMAX = kFusedWaves, NC = kFusedChunks, KW = 64 * NC;
+  constexpr int WMAX = kFusedWaves, KW = 64 * NC;
   __shared__ float red[WMAX][16];
   __shared__ __attribute__((aligned(16))) float part[WMAX][16 * 16];
   __shared__ __attribute__((aligned(16))) uint8_t aring[WMAX][kRingSlots][2048];
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   // kRingSlots pieces in this wave's LDS, XOR-swizzled by row, from which each lane reads its
   // MFMA operands. The first PRE pieces are requested with X, so that they arrive while the
   // row maxima are combined and X is encoded.
-  constexpr int NP = NC * RT, PRE = NP <= 12 ? NP : 8;
+  constexpr int NP = NC * RT, PRE = NC == 6 ? (NP <= 12 ? NP : 8) : (ENC == kDownFp8r ? 2 : 4);
   const int gr = lane >> 3, gp = lane & 7;  // this lane's row (and row + 8) and piece of a load
   uint4 xr[NC][2], aw[NP][2];
   auto load_a = [&](int i) {
@@ -397,22 +398,29 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   }
 }
 
+template <int RT, int NC>
+hipError_t run_down_rows_nc(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
+                            float scale, const float* ga, const float* gb, uint16_t* t, const RowsEncode& en,
+                            hipStream_t s) {
+  const int waves = (int)((K + 64 * NC - 1) / (64 * NC));
+  const dim3 grid((unsigned)((M + 15) / 16)), block((unsigned)(64 * waves));
+  if (en.enc == kDownFp8r)
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownFp8r, NC>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
+                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
+  else if (en.enc == kDownNvfp4)
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownNvfp4, NC>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
+                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
+  else
+    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownPlain, NC>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
+                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
+  return hipGetLastError();
+}
 template <int RT>
 hipError_t run_down_rows(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t M, int64_t K, int rank,
                          float scale, const float* ga, const float* gb, uint16_t* t, const RowsEncode& en,
                          hipStream_t s) {
-  const int waves = (int)((K + 64 * kFusedChunks - 1) / (64 * kFusedChunks));
-  const dim3 grid((unsigned)((M + 15) / 16)), block((unsigned)(64 * waves));
-  if (en.enc == kDownFp8r)
-    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownFp8r>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
-                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
-  else if (en.enc == kDownNvfp4)
-    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownNvfp4>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
-                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
-  else
-    hipLaunchKernelGGL((lora_down_rows_kernel<RT, kDownPlain>), grid, block, 0, s, x, ldx, a, (int)M, (int)K, rank,
-                       scale, ga, gb, t, en.xq, en.sx, en.xs, en.gq);
-  return hipGetLastError();
+  if (K <= 64 * 6 * kFusedWaves) return run_down_rows_nc<RT, 6>(x, ldx, a, M, K, rank, scale, ga, gb, t, en, s);
+  return run_down_rows_nc<RT, 12>(x, ldx, a, M, K, rank, scale, ga, gb, t, en, s);
 }
 
 template <int RT>
@@ -465,10 +473,14 @@ int lora_down_slices(int64_t M, int64_t K, int rank) {
 // 4096 rows 10.2 / 12.1 / 15.1 / 27.3 vs 6.5 / 8.8 / 11.6 / 17.7 at rank 16 / 32 / 64 / 128;
 // 16384 rows 20.8 / 23.0 / 28.6 / 36.8 vs 19.9 / 33.7 / 44.9 / 67.8; 256-1024 rows about 7 / 8 /
 // 12 / 25 vs 6.4 / 8.4 / 11.2 / 17.0; 16 rows 5.6 / 6.0 / 8.3 / 17.0 vs 6.2 / 8.1 / 10.8 / 16.4.
-bool lora_down_rows_fits(int64_t K) { return K <= 64 * kFusedChunks * kFusedWaves; }
+bool lora_down_rows_fits(int64_t K) { return K <= 64 * kFusedMaxChunks * kFusedWaves; }
 bool lora_down_rows_pick(int64_t M, int64_t K, int rank, DownEnc enc) {
   if (!lora_down_rows_fits(K)) return false;
   if (M > 4096) return rank <= 16;  // one rank tile keeps the adapter reads short
+  // rows over 3072 values (twelve chunks a wave): from 2048 rows at any rank and encoding --
+  // K = 4096 / 6144 at 4096 rows, rank 32, fp8r linear: quantizer + sliced 21.4 / 31.1 us
+  // against 17.1 / 21.2; below 2048 rows the sliced kernel wins from rank 32 on
+  if (K > 64 * 6 * kFusedWaves) return M >= 2048;
   // fp8r: the fused kernel also replaces the quantizer's launch
   if (enc == kDownFp8r) return true;
   // nvfp4 (the sliced kernel encodes too, with a finishing pass) and no encoding: below 256

@@ -141,10 +141,11 @@ def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K
 
 
 # The down projection alone takes the K-sliced kernel or, with K <= 3072, the whole-row kernel
-# without the encoding: for 256-4096 rows (rank 17-32 from 2048 rows), below 256 rows from rank 65.
+# without the encoding: for 256-4096 rows (rank 17-32 from 2048 rows), below 256 rows from rank 65;
+# with 3072 < K <= 6144 (twelve chunks a wave) from 2048 rows.
 DOWN_SHAPES = [(1, 32, 1), (17, 96, 4), (64, 256, 48), (40, 512, 64), (33, 128, 128), (300, 3072, 32),
                (4096, 3072, 32), (77, 12288, 16), (256, 1024, 64), (2048, 544, 24), (512, 96, 128),
-               (300, 2048, 100), (1000, 3072, 16)]
+               (300, 2048, 100), (1000, 3072, 16), (2048, 4096, 48), (2200, 6144, 16), (1000, 4096, 32)]
 
 
 @pytest.mark.parametrize("M,K,rank", DOWN_SHAPES)
@@ -188,7 +189,7 @@ def test_empty_batch_is_a_noop():
 # (the others) writes the encoding.
 @pytest.mark.parametrize("M,N,K,rank", [(300, 512, 512, 16), (4096, 3072, 3072, 32), (20, 1024, 512, 32),
                                         (130, 200, 160, 48), (257, 300, 544, 128), (16, 256, 96, 100),
-                                        (5000, 256, 1024, 16), (5000, 256, 1024, 32)])
+                                        (5000, 256, 1024, 16), (5000, 256, 1024, 32), (2048, 256, 4608, 64)])
 def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, rank):
     """The W4A4 path encodes X to nvfp4 inside its down projection: the workspace's first two
     parts (packed codes, then block scales, each padded to 256 bytes) must equal the activation
@@ -217,14 +218,16 @@ def test_quantized_activations_in_the_workspace_match_the_quantizer(M, N, K, ran
                       extra=t_rounding_bound(x[rows], a, b, SCALE))
 
 
-# fp8r linears with K <= 3072 encode X and compute T in one kernel (16 whole rows a workgroup,
-# up to 8 waves of 384 K values) up to 4096 rows, and beyond that at rank <= 16; otherwise the
-# quantizer and the K-sliced projection run. Shapes: one wave with a half chunk (K = 96), ragged
+# fp8r linears encode X and compute T in one kernel (16 whole rows a workgroup, up to 8 waves of
+# 384 K values) for K <= 3072 up to 4096 rows, and beyond that at rank <= 16; for 3072 < K <= 6144
+# (768 K values a wave) from 2048 rows; otherwise the quantizer and the K-sliced projection run. Shapes: one wave with a half chunk (K = 96), ragged
 # rows, 2 waves with a partial last chunk (K = 544), a full workgroup (K = 3072) at 4096 tokens,
-# 5000 tokens on both paths, and the unfused path for long rows (K = 4096).
+# 5000 tokens on both paths, the unfused path for long rows below 2048 tokens (40 x 4096), and
+# twelve chunks a wave from 2048 tokens (K = 3104, 4096, 6144).
 @pytest.mark.parametrize("M,N,K,rank", [(1, 64, 96, 5), (33, 128, 544, 16), (300, 256, 1056, 48),
                                         (4096, 3072, 3072, 32), (70, 256, 3072, 128), (40, 128, 4096, 24),
-                                        (5000, 256, 1024, 16), (5000, 256, 1024, 32)])
+                                        (5000, 256, 1024, 16), (5000, 256, 1024, 32), (2048, 256, 4096, 32),
+                                        (2100, 128, 6144, 128), (2048, 256, 3104, 16)])
 def test_fp8r_workspace_holds_the_quantizer_output_and_t(M, N, K, rank):
     """The fp8r W8A8 adapter path leaves in its workspace X's fp8r codes and row scales (bit for
     bit what the activation quantizer writes) and T = bf16(s X A^T) (within the down

@@ -75,6 +75,48 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
 }
 
+// Adapters of rank <= 32 with rank % 8 == 0: the tile's T rows and B rows are copied to LDS
+// by LDS DMA ahead of the first stage (64-byte LDS rows, values past the rank read as zeros,
+// chunks swizzled as in the stage regions), so the epilogue's adapter MFMAs read them from LDS
+// instead of waiting on global loads after the K loop (at 4096 x 3072 x 3072, rank 32: about
+// 2 us of exposed latency). Other ranks read T and B from global memory in the epilogue.
+constexpr int kLoraLdsRow = 64;  // bytes a row of the LDS copy (rank 32)
+constexpr bool lora_in_lds_host(int rank) { return rank <= 32 && (rank & 7) == 0; }
+template <int BM, int BN>
+__device__ __forceinline__ void lora_stage(const uint16_t* lt, const uint16_t* lb, int M, int N, int m0, int n0,
+                                           int rank, uint32_t lds, int wave, int lane) {
+  constexpr int R = kLoraLdsRow;
+  const int rows_t = M - m0 < BM ? M - m0 : BM, rows_b = N - n0 < BN ? N - n0 : BN;
+  const v4i rt = buffer_rsrc(lt + (int64_t)m0 * rank, (uint32_t)(rows_t * rank * 2));
+  const v4i rb = buffer_rsrc(lb + (int64_t)n0 * rank, (uint32_t)(rows_b * rank * 2));
+  dma_region<Region<R, BM, R / 2>>(rt, lds, wave, lane, 2 * rank, 0, 0, rank);
+  dma_region<Region<R, BN, R / 2>>(rb, lds + BM * R, wave, lane, 2 * rank, 0, 0, rank);
+}
+// acc += T B^T from the LDS copy (tile-local rows: n at nl0 + 32 i, m at ml0 + 32 j)
+template <int BM, int TN, int TM>
+__device__ __forceinline__ void lora_update_lds(v16f (&acc)[TN][TM], const uint8_t* lds, int rank, int nl0, int ml0,
+                                                int lane) {
+  constexpr int R = kLoraLdsRow;
+  const int lr = lane & 31, lh = lane >> 5;
+  LoraRegs<TN, TM, 2> r;
+  auto chunk = [&](const uint8_t* base, int row, int c) {
+    union {
+      uint4 u;
+      v8bf h;
+    } v;
+    v.u = *reinterpret_cast<const uint4*>(base + row * R + (swz_chunk<R>(row, c) << 4));
+    return v.h;
+  };
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) r.b[s][i] = chunk(lds + BM * R, nl0 + 32 * i + lr, 2 * s + lh);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) r.t[s][j] = chunk(lds, ml0 + 32 * j + lr, 2 * s + lh);
+  }
+  lora_mfma(acc, r, 0, rank);
+}
+
 // The K loop, two ways. The general loop (any K, any ring depth) leaves the order of its
 // LDS reads, DMAs and MFMAs to the compiler, within scheduling groups. The hand-ordered loop
 // (two stage buffers, K % 128 == 0, with or without an adapter) fixes the order per MFMA, which took the large tiles 8-13 %
@@ -94,8 +136,9 @@ template <int NS>
 constexpr bool hand_ordered() { return NS == 2; }
 
 // OQ: quantized output for the next linear -- 0 none, 1 nvfp4 blocks in the epilogue, 2 the
-// row maxima of the fp8r encoding (YQuant). HS: the hand-ordered K loop (K % 128 == 0).
-template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false>
+// row maxima of the fp8r encoding (YQuant). HS: the hand-ordered K loop (K % 128 == 0). LL:
+// the adapter's T and B rows staged in LDS (ranks lora_in_lds_host accepts).
+template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, bool LL = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                      const uint8_t* __restrict__ w, const float* __restrict__ sw,
@@ -106,6 +149,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   __shared__ __attribute__((aligned(16))) float s_sx[BM];
   __shared__ __attribute__((aligned(16))) float s_sw[BN];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lora[LL ? (BM + BN) * kLoraLdsRow : 16];
 
   int m0, n0;
   tile_of_block(M, N, BM, BN, m0, n0);
@@ -117,6 +161,9 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   const v4i rx = buffer_rsrc(xq + (int64_t)m0 * K, (uint32_t)(rows_x * K));
   const v4i rw = buffer_rsrc(w + (int64_t)n0 * K, (uint32_t)(rows_w * K));
   const uint32_t lds0 = lds_offset(smem);
+  // the adapter's T and B rows of this tile, ahead of the first stage (older than every stage
+  // load, so the prologue's wait covers them)
+  if constexpr (LL) lora_stage<BM, BN>(lt, lb, M, N, m0, n0, rank, lds_offset(s_lora), wave, lane);
 
   auto issue_stage = [&](int kt) {
     const int kb = kt * kStageK;
@@ -281,7 +328,10 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
           acc[i][j][4 * g + 3] = acc[i][j][4 * g + 3] * xs * s4.w;
         }
     }
-    lora_update<TN, TM>(acc, lt, lb, rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
+    if constexpr (LL)
+      lora_update_lds<BM>(acc, s_lora, rank, wn * C::WN, wm * C::WM, lane);
+    else
+      lora_update<TN, TM>(acc, lt, lb, rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
   }
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
@@ -335,9 +385,16 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
   const int st = (int)stream_output((M + N) * K, M, N);
   const YQuant qv = q ? *q : YQuant{};
   if (kAdapter && lt) {
-    if (hand_ordered<NS>() && K % kStageK == 0)
+    const bool hs = hand_ordered<NS>() && K % kStageK == 0, ll = lora_in_lds_host(rank);
+    if (hs && ll)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, hand_ordered<NS>(), kAdapter>), dim3(tiles),
+                         dim3(kThreads), 0, s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    else if (hs)
       hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, hand_ordered<NS>()>), dim3(tiles), dim3(kThreads),
                          0, s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    else if (ll)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, false, kAdapter>), dim3(tiles), dim3(kThreads), 0, s,
+                         xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
     else
       hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
                          y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);

@@ -87,6 +87,27 @@ void audit_region(const char* cfg, int region_base, int lds_size, int slot0, int
     }
 }
 
+// ---- fp8r W8A8 adapter rows (gemm_fp8.hip, ranks 8 / 16 / 24 / 32): the tile's T rows and B
+// rows copied once into a separate LDS array of (BM + BN) rows of 64 bytes
+template <int BM, int BN>
+void audit_lora_rows(int M, int N, int rank) {
+  constexpr int R = 64;
+  using RT = Region<R, BM, R / 2>;
+  using RBr = Region<R, BN, R / 2>;
+  char cfg[96];
+  std::snprintf(cfg, sizeof cfg, "fp8 adapter rows %dx%d, %dx%d rank %d", BM, BN, M, N, rank);
+  const int lds = (BM + BN) * R;
+  for (int tm : edge_tiles(M, BM))
+    for (int tn : edge_tiles(N, BN)) {
+      const int rows_t = std::min(BM, M - tm * BM), rows_b = std::min(BN, N - tn * BN);
+      audit_region<RT>(cfg, 0, lds, 0, BM * R, (uint32_t)(rows_t * rank * 2), rows_t, 2 * rank, 2 * rank, 2 * rank,
+                       0, 0, rank, 8, false);
+      audit_region<RBr>(cfg, BM * R, lds, BM * R, lds, (uint32_t)(rows_b * rank * 2), rows_b, 2 * rank, 2 * rank,
+                        2 * rank, 0, 0, rank, 8, false);
+    }
+  std::printf("ok %s\n", cfg);
+}
+
 // ---- fp8r W8A8 (gemm_fp8.hip): general loop (stages 0 .. nk + NS - 1) and, for two stage
 // buffers with K % 128 == 0, the hand-ordered loop (stages 0 .. nk - 1, lane offsets of stage 0)
 template <int BM, int BN, int NS>
@@ -241,6 +262,14 @@ int main() {
     audit_fp8<256, 192, 2>(s[0], s[1], s[2]);
     audit_fp8<256, 256, 2>(s[0], s[1], s[2]);
   }
+  const int lora_shapes[][2] = {{64, 64}, {300, 520}, {4096, 3072}, {77, 100}, {513, 257}};
+  for (auto& s : lora_shapes)
+    for (int rank : {8, 16, 24, 32}) {
+      audit_lora_rows<64, 64>(s[0], s[1], rank);
+      audit_lora_rows<64, 128>(s[0], s[1], rank);
+      audit_lora_rows<128, 128>(s[0], s[1], rank);
+      audit_lora_rows<256, 192>(s[0], s[1], rank);
+    }
   const int w4_shapes[][3] = {{64, 128, 256}, {300, 520, 512}, {4096, 12288, 3072}, {3100, 4000, 768},
                               {513, 257, 12288}};
   for (auto& s : w4_shapes) {

@@ -120,6 +120,21 @@ def test_lora_large_tiles_sampled(scheme, weight_only, M, N, K, rank):
              what="%s%s %dx%dx%d r%d" % (scheme, "-wo" if weight_only else "", M, N, K, rank))
 
 
+# The fp8r W8A8 GEMM copies the tile's rows of T and B into LDS when the rank is a multiple of 8
+# up to 32 (else it reads them from global memory in the epilogue): each of its adapter tiles at
+# both ranks of that copy and one past it -- 64 x 64 (300 x 520), 64 x 128 (1100 x 1000),
+# 128 x 128 (2100 x 1000), 256 x 192 (4096 x 3072); K = 320 is not a whole number of 128-deep
+# stages, 512 is.
+FP8_TILE_SHAPES = [(300, 520, 320), (1100, 1000, 512), (2100, 1000, 320), (2100, 1000, 512), (4096, 3072, 320)]
+
+
+@pytest.mark.parametrize("rank", [8, 24, 32, 40])
+@pytest.mark.parametrize("M,N,K", FP8_TILE_SHAPES)
+def test_fp8r_adapter_tiles(M, N, K, rank):
+    x, w, a, b = _inputs(M, N, K, rank, 8)
+    run_lora("fp8r", False, x, w, a, b, SCALE, sample=96, what="fp8r %dx%dx%d r%d" % (M, N, K, rank))
+
+
 @pytest.mark.parametrize("M,N,K,rank", ROUTE_SHAPES + [(4096, 3072, 3072, 32)])
 @pytest.mark.parametrize("scheme,weight_only", SCHEMES)
 def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K, rank):

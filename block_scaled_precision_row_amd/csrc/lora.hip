@@ -247,21 +247,23 @@ __global__ __launch_bounds__(256) void lora_down_finish_kernel(const float* __re
 // (at most 8) waves holds 64 NC consecutive K values of all 16 rows in registers (NC = 6
 // 64-deep chunks for K <= 3072, 12 for K <= 6144; lane (lr, lg) holds the 16 values
 // kc + 16 lg .. + 15 of row lr of chunk kc, the layout of the kernel above), so X is read from
-// HBM once (with twelve chunks and the fp8r encoding, four registers a lane spill outside the
-// adapter loop, and fewer adapter pieces are requested ahead). With ENC the row maxima combine across the four
+// HBM once (with twelve chunks fewer adapter pieces are requested ahead, which keeps the
+// kernel within 256 registers a lane). With ENC the row maxima combine across the four
 // lanes of a row and then across the waves through LDS, and each wave encodes its values
 // with the quantizer's own steps (d = fp32(amax / 448), r = fp32(1 / d), E4M3(fp32(x r))).
 // The nvfp4 encoding needs no row maximum: a lane's 16 values of a chunk are one block,
 // encoded by the quantizer's block function (without the K slices' finishing pass this kernel
 // beats the sliced one at most shapes). Every wave multiplies the same registers into T on
 // the matrix cores, with the adapter read from L2 (A is the MFMA A operand, X the B operand).
-// The waves' fp32 tiles are added in wave order through LDS, one rank tile at a time, scaled
-// and rounded to bf16. For an fp8r linear one launch replaces the quantizer, the sliced down
-// projection and its finishing pass.
-// Measured at 4096 x 3072 (us, no profiler): the quantizer alone 6.5; this kernel 9.1 / 11.7 /
-// 15.2 / 20.8 at rank 16 / 32 / 64 / 128; without the encoding 6.5 / 8.8 / 11.6 / 17.7; without
-// the adapter part 9.3 (rank 32). The phases add up because each compute unit holds one
-// workgroup (256 of them at 4096 rows): X's loads, then the encoded stores, then the adapter.
+// The waves' fp32 tiles (all rank tiles, behind one barrier) are added in wave order through
+// LDS, scaled and rounded to bf16. For an fp8r linear one launch replaces the quantizer, the
+// sliced down projection and its finishing pass.
+// Measured at 4096 x 3072 (us, no profiler): the quantizer alone 6.5; this kernel 9.1 / 10.6 /
+// 13.1 / 18.5 at rank 16 / 32 / 64 / 128 (with one reduction barrier per rank tile and the
+// adapter after the encoding it was 9.1 / 11.5 / 14.7 / 21.2); at 4096 x 6144 13.5 for the
+// quantizer, 17.1 / 19.6 / 24.0 / 33.3 here. The phases mostly add up because each compute
+// unit holds one workgroup (256 of them at 4096 rows): X's loads, the encoded stores and the
+// adapter's loads and MFMAs.
 constexpr int kFusedWaves = 8;      // at most; 256 registers a lane
 constexpr int kFusedMaxChunks = 12;  // 64-deep chunks a wave (6 up to K = 3072)
 constexpr int kRingSlots = 4;    // adapter pieces (16 rows x 64 values) staged at a time per wave
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
                                                                    uint8_t* __restrict__ xs, const float* gq) {
   constexpr int WMAX = kFusedWaves, KW = 64 * NC;
   __shared__ float red[WMAX][16];
-  __shared__ __attribute__((aligned(16))) float part[WMAX][16 * 16];
+  __shared__ __attribute__((aligned(16))) float part[WMAX][RT][16 * 16];
   __shared__ __attribute__((aligned(16))) uint8_t aring[WMAX][kRingSlots][2048];
   const int waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -293,8 +295,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   // eight lanes per 128-byte row segment (whole lines per load; in the MFMA layout the lanes
   // of a quarter wave would each address a different row) and staged through a ring of
   // kRingSlots pieces in this wave's LDS, XOR-swizzled by row, from which each lane reads its
-  // MFMA operands. The first PRE pieces are requested with X, so that they arrive while the
-  // row maxima are combined and X is encoded.
+  // MFMA operands. The first PRE pieces are requested with X, so that they arrive while X does
+  // (and, after the encoding, while the row maxima are combined and X is encoded).
   constexpr int NP = NC * RT, PRE = NC == 6 ? (NP <= 12 ? NP : 8) : (ENC == kDownFp8r ? 2 : 4);
   const int gr = lane >> 3, gp = lane & 7;  // this lane's row (and row + 8) and piece of a load
   uint4 xr[NC][2], aw[NP][2];
@@ -313,6 +315,37 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
   }
 #pragma unroll
   for (int i = 0; i < PRE; ++i) load_a(i);
+  // The adapter's MFMAs need X but not the row maxima. In the six-chunk fp8r kernel they run
+  // before the maxima are combined (what a wave computes while others' X is still arriving
+  // shortens the wait at the barrier; 4096 x 3072, rank 32: 11.5 -> 10.6 us, same bits); with
+  // twelve chunks (register-bound) and in the other modes they run after the encoding.
+  constexpr bool kAdapterFirst = ENC == kDownFp8r && NC == 6;
+  v4f acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto adapter = [&]() {
+    uint8_t* ring = aring[wave][0];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int c = i / RT, r = i % RT;
+      if (i + PRE < NP) load_a(i + PRE);  // PRE pieces in flight
+      uint8_t* slot = ring + (i % kRingSlots) * 2048;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + gr;
+        *reinterpret_cast<uint4*>(slot + row * 128 + ((gp ^ (row & 7)) << 4)) = aw[i][h];
+      }
+      // lane (lr, lg): row lr, values 16 lg + 8 q of the chunk, as in xr[c][q]
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 av = *reinterpret_cast<const uint4*>(slot + lr * 128 + (((2 * lg + q) ^ (lr & 7)) << 4));
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(av), as_v8bf(xr[c][q]), acc[r], 0, 0, 0);
+      }
+      if constexpr (NP > PRE) __builtin_amdgcn_sched_barrier(0);  // no loads hoisted past the window
+    }
+  };
+  if constexpr (kAdapterFirst) adapter();
+
   if constexpr (ENC == kDownFp8r) {
     float amax = 0.0f;
 #pragma unroll
@@ -358,43 +391,21 @@ __global__ __launch_bounds__(64 * kFusedWaves) void lora_down_rows_kernel(const 
     }
   }
 
-  v4f acc[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  uint8_t* ring = aring[wave][0];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int c = i / RT, r = i % RT;
-    if (i + PRE < NP) load_a(i + PRE);  // PRE pieces in flight
-    uint8_t* slot = ring + (i % kRingSlots) * 2048;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 8 * h + gr;
-      *reinterpret_cast<uint4*>(slot + row * 128 + ((gp ^ (row & 7)) << 4)) = aw[i][h];
-    }
-    // lane (lr, lg): row lr, values 16 lg + 8 q of the chunk, as in xr[c][q]
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint4 av = *reinterpret_cast<const uint4*>(slot + lr * 128 + (((2 * lg + q) ^ (lr & 7)) << 4));
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(av), as_v8bf(xr[c][q]), acc[r], 0, 0, 0);
-    }
-    if constexpr (NP > PRE) __builtin_amdgcn_sched_barrier(0);  // no loads hoisted past the window
-  }
+  if constexpr (!kAdapterFirst) adapter();
 
-  // T: lane (lr, lg) holds token lr, adapter rows 16 r + 4 lg + e; stage [wave][token][16]
-  // and add the waves in order
+  // T: lane (lr, lg) holds token lr, adapter rows 16 r + 4 lg + e; every wave stages its tiles
+  // in part[wave][r][token][16] and one barrier later the waves are added in wave order
   const float f = out_factor(scale, ga, gb);
-  for (int r = 0; r < RT; ++r) {
-    *reinterpret_cast<float4*>(&part[wave][lr * 16 + 4 * lg]) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-    __syncthreads();
-    for (int i = tid; i < 256; i += 64 * waves) {  // i = 16 token + adapter row within the tile
-      const int n = i >> 4, j = i & 15;
-      float s = part[0][i];
-      for (int w = 1; w < waves; ++w) s += part[w][i];
-      if (n < rows && 16 * r + j < rank)
-        t[(int64_t)(m0 + n) * rank + 16 * r + j] = (uint16_t)(pack_bf16x2(f * s, 0.0f) & 0xFFFFu);
-    }
-    __syncthreads();  // part is rewritten for the next tile
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+    *reinterpret_cast<float4*>(&part[wave][r][lr * 16 + 4 * lg]) = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+  __syncthreads();
+  for (int i = tid; i < 256 * RT; i += 64 * waves) {  // i = 256 r + 16 token + adapter row within tile r
+    const int r = i >> 8, n = (i >> 4) & 15, j = i & 15;
+    float s = part[0][r][i & 255];
+    for (int w = 1; w < waves; ++w) s += part[w][r][i & 255];
+    if (n < rows && 16 * r + j < rank)
+      t[(int64_t)(m0 + n) * rank + 16 * r + j] = (uint16_t)(pack_bf16x2(f * s, 0.0f) & 0xFFFFu);
   }
 }
 

@@ -347,7 +347,8 @@ def lora_overhead(L, syn, dev, x2, x3, w2q, w2s, w3q, w3s, g3, gx3, reps=10):
                    "its down projection), synthetic adapter with scale 1; the pages report about 5 % more "
                    "generation time with a LoRA attached (whole model, other hardware). down_us: the down "
                    "projection alone (bsq_lora_down); in the linears it is fused with the activation "
-                   "encoding (nvfp4: K-sliced kernel; fp8r: whole-row kernel, K <= 3072)")
+                   "encoding (whole-row kernel up to K = 6144 at these row counts, K-sliced kernel where the "
+                   "routing prefers it, e.g. the 16-token linear)")
     return out
 
 

@@ -75,30 +75,36 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
 }
 
-// Adapters of rank <= 32 with rank % 8 == 0: the tile's T rows and B rows are copied to LDS
-// by LDS DMA ahead of the first stage (64-byte LDS rows, values past the rank read as zeros,
-// chunks swizzled as in the stage regions), so the epilogue's adapter MFMAs read them from LDS
-// instead of waiting on global loads after the K loop (at 4096 x 3072 x 3072, rank 32: about
-// 2 us of exposed latency). Other ranks read T and B from global memory in the epilogue.
-constexpr int kLoraLdsRow = 64;  // bytes a row of the LDS copy (rank 32)
-constexpr bool lora_in_lds_host(int rank) { return rank <= 32 && (rank & 7) == 0; }
-template <int BM, int BN>
+// Where the epilogue's adapter MFMAs find the tile's T rows and B rows (rank % 8 == 0; other
+// ranks read them from global memory in the epilogue, where their load latency is exposed after
+// the K loop -- about 2 us at 4096 x 3072 x 3072, rank 32):
+//  * kLoraAhead (ranks 8..32): copied by LDS DMA ahead of the first stage into an LDS array of
+//    their own, 64-byte rows ((BM + BN) * 64 bytes; the prologue's wait covers them);
+//  * kLoraLate (ranks 40..64, hand-ordered loop): copied by LDS DMA into the stage buffer that
+//    the last two stages leave free, 128-byte rows ((BM + BN) * 128 bytes: one stage buffer),
+//    issued after the barrier of the second-to-last stage, so the last stage's MFMAs cover it.
+// Rows are swizzled as in the stage regions; values past the rank and rows past M or N read as
+// zeros.
+enum LoraLds { kLoraGlobal = 0, kLoraAhead = 1, kLoraLate = 2 };
+constexpr int kLoraLdsRow = 64;  // bytes a row of the kLoraAhead copy (rank 32)
+constexpr int lora_lds_host(int rank, bool hand) {
+  return (rank & 7) ? kLoraGlobal : rank <= 32 ? kLoraAhead : (hand && rank <= 64) ? kLoraLate : kLoraGlobal;
+}
+template <int BM, int BN, int R>
 __device__ __forceinline__ void lora_stage(const uint16_t* lt, const uint16_t* lb, int M, int N, int m0, int n0,
                                            int rank, uint32_t lds, int wave, int lane) {
-  constexpr int R = kLoraLdsRow;
   const int rows_t = M - m0 < BM ? M - m0 : BM, rows_b = N - n0 < BN ? N - n0 : BN;
   const v4i rt = buffer_rsrc(lt + (int64_t)m0 * rank, (uint32_t)(rows_t * rank * 2));
   const v4i rb = buffer_rsrc(lb + (int64_t)n0 * rank, (uint32_t)(rows_b * rank * 2));
   dma_region<Region<R, BM, R / 2>>(rt, lds, wave, lane, 2 * rank, 0, 0, rank);
   dma_region<Region<R, BN, R / 2>>(rb, lds + BM * R, wave, lane, 2 * rank, 0, 0, rank);
 }
-// acc += T B^T from the LDS copy (tile-local rows: n at nl0 + 32 i, m at ml0 + 32 j)
-template <int BM, int TN, int TM>
+// acc += T B^T from an LDS copy with R-byte rows (tile-local rows: n at nl0 + 32 i, m at
+// ml0 + 32 j), 32 rank values per batch
+template <int BM, int R, int TN, int TM>
 __device__ __forceinline__ void lora_update_lds(v16f (&acc)[TN][TM], const uint8_t* lds, int rank, int nl0, int ml0,
                                                 int lane) {
-  constexpr int R = kLoraLdsRow;
   const int lr = lane & 31, lh = lane >> 5;
-  LoraRegs<TN, TM, 2> r;
   auto chunk = [&](const uint8_t* base, int row, int c) {
     union {
       uint4 u;
@@ -107,14 +113,17 @@ __device__ __forceinline__ void lora_update_lds(v16f (&acc)[TN][TM], const uint8
     v.u = *reinterpret_cast<const uint4*>(base + row * R + (swz_chunk<R>(row, c) << 4));
     return v.h;
   };
+  for (int k0 = 0; k0 < rank; k0 += 32) {
+    LoraRegs<TN, TM, 2> r;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i) r.b[s][i] = chunk(lds + BM * R, nl0 + 32 * i + lr, 2 * s + lh);
+      for (int i = 0; i < TN; ++i) r.b[s][i] = chunk(lds + BM * R, nl0 + 32 * i + lr, k0 / 8 + 2 * s + lh);
 #pragma unroll
-    for (int j = 0; j < TM; ++j) r.t[s][j] = chunk(lds, ml0 + 32 * j + lr, 2 * s + lh);
+      for (int j = 0; j < TM; ++j) r.t[s][j] = chunk(lds, ml0 + 32 * j + lr, k0 / 8 + 2 * s + lh);
+    }
+    lora_mfma(acc, r, k0, rank);
   }
-  lora_mfma(acc, r, 0, rank);
 }
 
 // The K loop, two ways. The general loop (any K, any ring depth) leaves the order of its
@@ -137,8 +146,8 @@ constexpr bool hand_ordered() { return NS == 2; }
 
 // OQ: quantized output for the next linear -- 0 none, 1 nvfp4 blocks in the epilogue, 2 the
 // row maxima of the fp8r encoding (YQuant). HS: the hand-ordered K loop (K % 128 == 0). LL:
-// the adapter's T and B rows staged in LDS (ranks lora_in_lds_host accepts).
-template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, bool LL = false>
+// where the adapter's T and B rows are read (LoraLds).
+template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, int LL = kLoraGlobal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                      const uint8_t* __restrict__ w, const float* __restrict__ sw,
@@ -149,7 +158,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   __shared__ __attribute__((aligned(16))) float s_sx[BM];
   __shared__ __attribute__((aligned(16))) float s_sw[BN];
-  __shared__ __attribute__((aligned(16))) uint8_t s_lora[LL ? (BM + BN) * kLoraLdsRow : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lora[LL == kLoraAhead ? (BM + BN) * kLoraLdsRow : 16];
 
   int m0, n0;
   tile_of_block(M, N, BM, BN, m0, n0);
@@ -163,7 +172,8 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   const uint32_t lds0 = lds_offset(smem);
   // the adapter's T and B rows of this tile, ahead of the first stage (older than every stage
   // load, so the prologue's wait covers them)
-  if constexpr (LL) lora_stage<BM, BN>(lt, lb, M, N, m0, n0, rank, lds_offset(s_lora), wave, lane);
+  if constexpr (LL == kLoraAhead)
+    lora_stage<BM, BN, kLoraLdsRow>(lt, lb, M, N, m0, n0, rank, lds_offset(s_lora), wave, lane);
 
   auto issue_stage = [&](int kt) {
     const int kb = kt * kStageK;
@@ -213,11 +223,19 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     const int nk = K / kStageK;
 #pragma unroll
     for (int i = 0; i < LD; ++i) dma(i, 0);
+    // kLoraLate: the adapter rows go to the stage buffer of stage nk - 2 once it is read (stage
+    // buffer 1 for a single stage)
+    static_assert(LL != kLoraLate || C::STAGE == (BM + BN) * 128, "the adapter rows fill one stage buffer");
+    auto lora_late = [&](int buf) {
+      if constexpr (LL == kLoraLate)
+        lora_stage<BM, BN, 128>(lt, lb, M, N, m0, n0, rank, lds0 + (uint32_t)(buf * C::STAGE), wave, lane);
+    };
     if (nk > 1) {
 #pragma unroll
       for (int i = 0; i < LD; ++i) dma(i, 1);
       wait_vmcnt<LD>();
     } else {
+      lora_late(1);
       wait_vmcnt<0>();
     }
     __syncthreads();
@@ -242,8 +260,11 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vmcnt<0>();
+      if (LL != kLoraLate || s + 1 < nk) wait_vmcnt<0>();  // (the last stage leaves the adapter copy in flight)
       __syncthreads();  // stage s read by every wave; stage s + 1 landed
+      if constexpr (!F) {
+        if (s == nk - 2) lora_late(s % NS);
+      }
       const uint8_t* na = abuf(s + 1);
       const uint8_t* nb = na + C::A_BYTES;
 #pragma unroll
@@ -328,9 +349,14 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
           acc[i][j][4 * g + 3] = acc[i][j][4 * g + 3] * xs * s4.w;
         }
     }
-    if constexpr (LL)
-      lora_update_lds<BM>(acc, s_lora, rank, wn * C::WN, wm * C::WM, lane);
-    else
+    if constexpr (LL == kLoraAhead) {
+      lora_update_lds<BM, kLoraLdsRow>(acc, s_lora, rank, wn * C::WN, wm * C::WM, lane);
+    } else if constexpr (LL == kLoraLate) {
+      wait_vmcnt<0>();
+      __syncthreads();  // every wave's part of the copy has landed
+      lora_update_lds<BM, 128>(acc, smem + (nk >= 2 ? (nk - 2) % NS : 1) * C::STAGE, rank, wn * C::WN, wm * C::WM,
+                               lane);
+    } else
       lora_update<TN, TM>(acc, lt, lb, rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
   }
   wait_vmcnt<0>();
@@ -385,15 +411,21 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
   const int st = (int)stream_output((M + N) * K, M, N);
   const YQuant qv = q ? *q : YQuant{};
   if (kAdapter && lt) {
-    const bool hs = hand_ordered<NS>() && K % kStageK == 0, ll = lora_in_lds_host(rank);
-    if (hs && ll)
-      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, hand_ordered<NS>(), kAdapter>), dim3(tiles),
-                         dim3(kThreads), 0, s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    constexpr bool kHand = hand_ordered<NS>();
+    constexpr int kAhead = kAdapter ? kLoraAhead : kLoraGlobal, kLate = kAdapter && kHand ? kLoraLate : kLoraGlobal;
+    const bool hs = kHand && K % kStageK == 0;
+    const int ll = lora_lds_host(rank, hs);
+    if (hs && ll == kLoraAhead)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, kHand, kAhead>), dim3(tiles), dim3(kThreads), 0, s,
+                         xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    else if (hs && ll == kLoraLate)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, kHand, kLate>), dim3(tiles), dim3(kThreads), 0, s,
+                         xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
     else if (hs)
-      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, hand_ordered<NS>()>), dim3(tiles), dim3(kThreads),
-                         0, s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
-    else if (ll)
-      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, false, kAdapter>), dim3(tiles), dim3(kThreads), 0, s,
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, kHand>), dim3(tiles), dim3(kThreads), 0, s, xq, sx,
+                         w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    else if (ll == kLoraAhead)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, false, kAhead>), dim3(tiles), dim3(kThreads), 0, s,
                          xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
     else
       hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,

@@ -82,28 +82,41 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[TN][TM], const v8i (&a)[TN]
 //    their own, 64-byte rows ((BM + BN) * 64 bytes; the prologue's wait covers them);
 //  * kLoraLate (ranks 40..64, hand-ordered loop): copied by LDS DMA into the stage buffer that
 //    the last two stages leave free, 128-byte rows ((BM + BN) * 128 bytes: one stage buffer),
-//    issued after the barrier of the second-to-last stage, so the last stage's MFMAs cover it.
+//    issued after the barrier of the second-to-last stage, so the last stage's MFMAs cover it;
+//  * kLoraLate2 (ranks 72..128, hand-ordered loop): rank values 0..63 as kLoraLate, values
+//    64..127 into the other stage buffer after the last stage's barrier (its K step 1 and the
+//    first half's adapter MFMAs cover that copy).
 // Rows are swizzled as in the stage regions; values past the rank and rows past M or N read as
 // zeros.
-enum LoraLds { kLoraGlobal = 0, kLoraAhead = 1, kLoraLate = 2 };
+enum LoraLds { kLoraGlobal = 0, kLoraAhead = 1, kLoraLate = 2, kLoraLate2 = 3 };
 constexpr int kLoraLdsRow = 64;  // bytes a row of the kLoraAhead copy (rank 32)
 constexpr int lora_lds_host(int rank, bool hand) {
-  return (rank & 7) ? kLoraGlobal : rank <= 32 ? kLoraAhead : (hand && rank <= 64) ? kLoraLate : kLoraGlobal;
+  return (rank & 7) || rank > 128 ? kLoraGlobal
+         : rank <= 32             ? kLoraAhead
+         : !hand                  ? kLoraGlobal
+         : rank <= 64             ? kLoraLate
+                                  : kLoraLate2;
 }
+// rank values k_lo .. k_lo + R / 2 - 1 of the tile's T rows and B rows into R-byte LDS rows
 template <int BM, int BN, int R>
 __device__ __forceinline__ void lora_stage(const uint16_t* lt, const uint16_t* lb, int M, int N, int m0, int n0,
-                                           int rank, uint32_t lds, int wave, int lane) {
+                                           int rank, int k_lo, uint32_t lds, int wave, int lane) {
   const int rows_t = M - m0 < BM ? M - m0 : BM, rows_b = N - n0 < BN ? N - n0 : BN;
   const v4i rt = buffer_rsrc(lt + (int64_t)m0 * rank, (uint32_t)(rows_t * rank * 2));
   const v4i rb = buffer_rsrc(lb + (int64_t)n0 * rank, (uint32_t)(rows_b * rank * 2));
-  dma_region<Region<R, BM, R / 2>>(rt, lds, wave, lane, 2 * rank, 0, 0, rank);
-  dma_region<Region<R, BN, R / 2>>(rb, lds + BM * R, wave, lane, 2 * rank, 0, 0, rank);
+  dma_region<Region<R, BM, R / 2>>(rt, lds, wave, lane, 2 * rank, 2 * k_lo, k_lo, rank);
+  dma_region<Region<R, BN, R / 2>>(rb, lds + BM * R, wave, lane, 2 * rank, 2 * k_lo, k_lo, rank);
 }
-// acc += T B^T from an LDS copy with R-byte rows (tile-local rows: n at nl0 + 32 i, m at
-// ml0 + 32 j), 32 rank values per batch
+// this wave's LDS DMAs of one lora_stage call
+template <int BM, int BN, int R>
+constexpr int lora_stage_loads() {
+  return Region<R, BM, R / 2>::MIN_PER_WAVE + Region<R, BN, R / 2>::MIN_PER_WAVE;
+}
+// acc += T B^T over rank values k_lo .. k_lo + R / 2 - 1 from an LDS copy of them with R-byte rows
+// (tile-local rows: n at nl0 + 32 i, m at ml0 + 32 j), 32 rank values per batch
 template <int BM, int R, int TN, int TM>
-__device__ __forceinline__ void lora_update_lds(v16f (&acc)[TN][TM], const uint8_t* lds, int rank, int nl0, int ml0,
-                                                int lane) {
+__device__ __forceinline__ void lora_update_lds(v16f (&acc)[TN][TM], const uint8_t* lds, int rank, int k_lo, int nl0,
+                                                int ml0, int lane) {
   const int lr = lane & 31, lh = lane >> 5;
   auto chunk = [&](const uint8_t* base, int row, int c) {
     union {
@@ -113,14 +126,15 @@ __device__ __forceinline__ void lora_update_lds(v16f (&acc)[TN][TM], const uint8
     v.u = *reinterpret_cast<const uint4*>(base + row * R + (swz_chunk<R>(row, c) << 4));
     return v.h;
   };
-  for (int k0 = 0; k0 < rank; k0 += 32) {
+  for (int k0 = k_lo; k0 < k_lo + R / 2 && k0 < rank; k0 += 32) {
     LoraRegs<TN, TM, 2> r;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      const int c = (k0 - k_lo) / 8 + 2 * s + lh;
 #pragma unroll
-      for (int i = 0; i < TN; ++i) r.b[s][i] = chunk(lds + BM * R, nl0 + 32 * i + lr, k0 / 8 + 2 * s + lh);
+      for (int i = 0; i < TN; ++i) r.b[s][i] = chunk(lds + BM * R, nl0 + 32 * i + lr, c);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) r.t[s][j] = chunk(lds, ml0 + 32 * j + lr, k0 / 8 + 2 * s + lh);
+      for (int j = 0; j < TM; ++j) r.t[s][j] = chunk(lds, ml0 + 32 * j + lr, c);
     }
     lora_mfma(acc, r, k0, rank);
   }
@@ -173,7 +187,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   // the adapter's T and B rows of this tile, ahead of the first stage (older than every stage
   // load, so the prologue's wait covers them)
   if constexpr (LL == kLoraAhead)
-    lora_stage<BM, BN, kLoraLdsRow>(lt, lb, M, N, m0, n0, rank, lds_offset(s_lora), wave, lane);
+    lora_stage<BM, BN, kLoraLdsRow>(lt, lb, M, N, m0, n0, rank, 0, lds_offset(s_lora), wave, lane);
 
   auto issue_stage = [&](int kt) {
     const int kb = kt * kStageK;
@@ -223,19 +237,19 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     const int nk = K / kStageK;
 #pragma unroll
     for (int i = 0; i < LD; ++i) dma(i, 0);
-    // kLoraLate: the adapter rows go to the stage buffer of stage nk - 2 once it is read (stage
-    // buffer 1 for a single stage)
-    static_assert(LL != kLoraLate || C::STAGE == (BM + BN) * 128, "the adapter rows fill one stage buffer");
-    auto lora_late = [&](int buf) {
-      if constexpr (LL == kLoraLate)
-        lora_stage<BM, BN, 128>(lt, lb, M, N, m0, n0, rank, lds0 + (uint32_t)(buf * C::STAGE), wave, lane);
+    // kLoraLate(2): rank values 0..63 go to the stage buffer of stage nk - 2 once it is read
+    // (stage buffer 1 for a single stage), values 64..127 to that of stage nk - 1
+    static_assert(LL < kLoraLate || C::STAGE == (BM + BN) * 128, "64 rank values of the rows fill one stage buffer");
+    auto lora_late = [&](int buf, int k_lo) {
+      if constexpr (LL >= kLoraLate)
+        lora_stage<BM, BN, 128>(lt, lb, M, N, m0, n0, rank, k_lo, lds0 + (uint32_t)(buf * C::STAGE), wave, lane);
     };
     if (nk > 1) {
 #pragma unroll
       for (int i = 0; i < LD; ++i) dma(i, 1);
       wait_vmcnt<LD>();
     } else {
-      lora_late(1);
+      lora_late(1, 0);
       wait_vmcnt<0>();
     }
     __syncthreads();
@@ -260,10 +274,11 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (LL != kLoraLate || s + 1 < nk) wait_vmcnt<0>();  // (the last stage leaves the adapter copy in flight)
+      if (LL < kLoraLate || s + 1 < nk) wait_vmcnt<0>();  // (the last stage leaves the adapter copy in flight)
       __syncthreads();  // stage s read by every wave; stage s + 1 landed
       if constexpr (!F) {
-        if (s == nk - 2) lora_late(s % NS);
+        if (s == nk - 2) lora_late(s % NS, 0);
+        if (LL == kLoraLate2 && s == nk - 1) lora_late(s % NS, 64);
       }
       const uint8_t* na = abuf(s + 1);
       const uint8_t* nb = na + C::A_BYTES;
@@ -350,12 +365,18 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
         }
     }
     if constexpr (LL == kLoraAhead) {
-      lora_update_lds<BM, kLoraLdsRow>(acc, s_lora, rank, wn * C::WN, wm * C::WM, lane);
-    } else if constexpr (LL == kLoraLate) {
-      wait_vmcnt<0>();
+      lora_update_lds<BM, kLoraLdsRow>(acc, s_lora, rank, 0, wn * C::WN, wm * C::WM, lane);
+    } else if constexpr (LL >= kLoraLate) {
+      // rank values 0..63 (with kLoraLate2 the copy of 64..127, issued later, may still be in flight)
+      wait_vmcnt<LL == kLoraLate2 ? lora_stage_loads<BM, BN, 128>() : 0>();
       __syncthreads();  // every wave's part of the copy has landed
-      lora_update_lds<BM, 128>(acc, smem + (nk >= 2 ? (nk - 2) % NS : 1) * C::STAGE, rank, wn * C::WN, wm * C::WM,
+      lora_update_lds<BM, 128>(acc, smem + (nk >= 2 ? (nk - 2) % NS : 1) * C::STAGE, rank, 0, wn * C::WN, wm * C::WM,
                                lane);
+      if constexpr (LL == kLoraLate2) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        lora_update_lds<BM, 128>(acc, smem + ((nk - 1) % NS) * C::STAGE, rank, 64, wn * C::WN, wm * C::WM, lane);
+      }
     } else
       lora_update<TN, TM>(acc, lt, lb, rank, M, N, n0 + wn * C::WN, m0 + wm * C::WM, lane);
   }
@@ -412,7 +433,8 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
   const YQuant qv = q ? *q : YQuant{};
   if (kAdapter && lt) {
     constexpr bool kHand = hand_ordered<NS>();
-    constexpr int kAhead = kAdapter ? kLoraAhead : kLoraGlobal, kLate = kAdapter && kHand ? kLoraLate : kLoraGlobal;
+    constexpr int kAhead = kAdapter ? kLoraAhead : kLoraGlobal, kLate = kAdapter && kHand ? kLoraLate : kLoraGlobal,
+                  kLate2 = kAdapter && kHand ? kLoraLate2 : kLoraGlobal;
     const bool hs = kHand && K % kStageK == 0;
     const int ll = lora_lds_host(rank, hs);
     if (hs && ll == kLoraAhead)
@@ -420,6 +442,9 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
                          xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
     else if (hs && ll == kLoraLate)
       hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, kHand, kLate>), dim3(tiles), dim3(kThreads), 0, s,
+                         xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
+    else if (hs && ll == kLoraLate2)
+      hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, kHand, kLate2>), dim3(tiles), dim3(kThreads), 0, s,
                          xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, lt, lb, rank, st, qv);
     else if (hs)
       hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, kAdapter, 0, kHand>), dim3(tiles), dim3(kThreads), 0, s, xq, sx,

@@ -111,22 +111,23 @@ void audit_lora_rows(int M, int N, int rank) {
 // ---- fp8r W8A8 adapter rows late (gemm_fp8.hip, hand-ordered 256 x 192 loop, ranks 40..64): the
 // tile's T rows and B rows copied into one stage buffer (128-byte rows) of the two
 template <int BM, int BN>
-void audit_lora_late(int M, int N, int rank, int buf) {
+void audit_lora_late(int M, int N, int rank, int buf, int k_lo = 0) {
   using C = Fp8Cfg<BM, BN, 2>;
   constexpr int R = 128;
   using RT = Region<R, BM, R / 2>;
   using RBr = Region<R, BN, R / 2>;
   static_assert(C::STAGE == (BM + BN) * R, "one stage buffer");
   char cfg[112];
-  std::snprintf(cfg, sizeof cfg, "fp8 adapter rows late %dx%d, %dx%d rank %d buffer %d", BM, BN, M, N, rank, buf);
+  std::snprintf(cfg, sizeof cfg, "fp8 adapter rows late %dx%d, %dx%d rank %d from %d buffer %d", BM, BN, M, N, rank,
+                k_lo, buf);
   const int s0 = buf * C::STAGE, s1 = s0 + C::STAGE;
   for (int tm : edge_tiles(M, BM))
     for (int tn : edge_tiles(N, BN)) {
       const int rows_t = std::min(BM, M - tm * BM), rows_b = std::min(BN, N - tn * BN);
       audit_region<RT>(cfg, s0, C::LDS, s0, s1, (uint32_t)(rows_t * rank * 2), rows_t, 2 * rank, 2 * rank, 2 * rank,
-                       0, 0, rank, 8, false);
+                       2 * k_lo, k_lo, rank, 8, false);
       audit_region<RBr>(cfg, s0 + BM * R, C::LDS, s0, s1, (uint32_t)(rows_b * rank * 2), rows_b, 2 * rank, 2 * rank,
-                        2 * rank, 0, 0, rank, 8, false);
+                        2 * rank, 2 * k_lo, k_lo, rank, 8, false);
     }
   std::printf("ok %s\n", cfg);
 }
@@ -296,6 +297,10 @@ int main() {
   for (auto& s : lora_shapes)
     for (int rank : {40, 48, 56, 64})
       for (int buf : {0, 1}) audit_lora_late<256, 192>(s[0], s[1], rank, buf);
+  for (auto& s : lora_shapes)
+    for (int rank : {72, 96, 120, 128})
+      for (int buf : {0, 1})
+        for (int k_lo : {0, 64}) audit_lora_late<256, 192>(s[0], s[1], rank, buf, k_lo);
   const int w4_shapes[][3] = {{64, 128, 256}, {300, 520, 512}, {4096, 12288, 3072}, {3100, 4000, 768},
                               {513, 257, 12288}};
   for (auto& s : w4_shapes) {

@@ -135,12 +135,14 @@ def test_fp8r_adapter_tiles(M, N, K, rank):
     run_lora("fp8r", False, x, w, a, b, SCALE, sample=96, what="fp8r %dx%dx%d r%d" % (M, N, K, rank))
 
 
-# On the hand-ordered 256 x 192 loop (K % 128 == 0), ranks 40..64 that are multiples of 8 get T and
-# B copied into the stage buffer that the last two stages leave free (the copy is issued in the
-# second-to-last stage; with a single stage, in the prologue); 72 and 60 read them from global
-# memory. K = 128 and 256 are the one- and two-stage cases, 4000 x 3000 has ragged last tiles.
+# On the hand-ordered 256 x 192 loop (K % 128 == 0), ranks that are multiples of 8 from 40 get T and
+# B copied into the stage buffers the last stages leave free: rank values 0..63 into that of the
+# second-to-last stage (in the prologue for a single stage), 64..127 into that of the last one;
+# 60 and 100 read them from global memory. K = 128 and 256 are the one- and two-stage cases,
+# 4000 x 3000 has ragged last tiles.
 LATE_SHAPES = [(4096, 3072, 128, 64), (4096, 3072, 256, 40), (4096, 3072, 640, 48), (4000, 3000, 384, 56),
-               (4000, 3000, 384, 64), (4096, 3072, 640, 72), (4096, 3072, 640, 60)]
+               (4000, 3000, 384, 64), (4096, 3072, 640, 72), (4096, 3072, 640, 60), (4096, 3072, 128, 128),
+               (4096, 3072, 256, 96), (4000, 3000, 384, 120), (4096, 3072, 640, 128), (4096, 3072, 640, 100)]
 
 
 @pytest.mark.parametrize("M,N,K,rank", LATE_SHAPES)
@@ -149,7 +151,8 @@ def test_fp8r_adapter_late_copy(M, N, K, rank):
     run_lora("fp8r", False, x, w, a, b, SCALE, sample=96, what="fp8r %dx%dx%d r%d" % (M, N, K, rank))
 
 
-@pytest.mark.parametrize("M,N,K,rank", ROUTE_SHAPES + [(4096, 3072, 3072, 32), (4096, 3072, 640, 64)])
+@pytest.mark.parametrize("M,N,K,rank", ROUTE_SHAPES + [(4096, 3072, 3072, 32), (4096, 3072, 640, 64),
+                                            (4096, 3072, 640, 128)])
 @pytest.mark.parametrize("scheme,weight_only", SCHEMES)
 def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K, rank):
     x, w, a, b = _inputs(M, N, K, rank, 2)

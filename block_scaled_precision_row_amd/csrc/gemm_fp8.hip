@@ -196,9 +196,15 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     dma_region<typename C::RB>(rx, base + C::A_BYTES, wave, lane, K, kb, kb, K);
   };
 
-  // row / column scales of the tile, for the epilogue
-  for (int i = tid; i < BM; i += kThreads) s_sx[i] = m0 + i < M ? sx[m0 + i] : 0.0f;
-  for (int i = tid; i < BN; i += kThreads) s_sw[i] = n0 + i < N ? sw[n0 + i] : 0.0f;
+  // row / column scales of the tile, for the epilogue: dword LDS DMA of 64 rows a load (rows past
+  // M or N read as zeros), issued ahead of the first stage -- older than every stage load, so the
+  // prologue's wait covers them, and no wave waits for them before its first stage is in flight
+  {
+    const v4i rsx = buffer_rsrc(sx + m0, (uint32_t)(rows_x * 4));
+    const v4i rsw = buffer_rsrc(sw + n0, (uint32_t)(rows_w * 4));
+    for (int i = wave; i < BM / 64; i += 4) dma4(rsx, lds_offset(s_sx) + 256 * i, (64 * i + lane) * 4, 0);
+    for (int i = wave; i < BN / 64; i += 4) dma4(rsw, lds_offset(s_sw) + 256 * i, (64 * i + lane) * 4, 0);
+  }
 
   v16f acc[TN][TM];
 #pragma unroll

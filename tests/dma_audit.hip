@@ -16,6 +16,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <vector>
+#include <utility>
 
 #include "gemm_tiles.hpp"
 
@@ -104,6 +105,26 @@ void audit_lora_rows(int M, int N, int rank) {
                        0, 0, rank, 8, false);
       audit_region<RBr>(cfg, BM * R, lds, BM * R, lds, (uint32_t)(rows_b * rank * 2), rows_b, 2 * rank, 2 * rank,
                         2 * rank, 0, 0, rank, 8, false);
+    }
+  std::printf("ok %s\n", cfg);
+}
+
+// ---- fp8r W8A8 row / column scales (gemm_fp8.hip): dword LDS DMA of 64 rows a load into the
+// tile's scale arrays (BM and BN floats), rows past M or N past the records
+void audit_fp8_scales(int BM, int BN, int M, int N) {
+  char cfg[96];
+  std::snprintf(cfg, sizeof cfg, "fp8 scales %dx%d, %dx%d", BM, BN, M, N);
+  for (int tm : edge_tiles(M, BM))
+    for (int tn : edge_tiles(N, BN)) {
+      const int rows[2] = {std::min(BM, M - tm * BM), std::min(BN, N - tn * BN)}, len[2] = {BM, BN};
+      for (int v = 0; v < 2; ++v)
+        for (int wave = 0; wave < 4; ++wave)
+          for (int i = wave; i < len[v] / 64; i += 4)
+            for (int lane = 0; lane < 64; ++lane) {
+              const DmaAddr d{256 * i + 4 * lane, (64 * i + lane) * 4, 0};
+              // one float per row: pitch 4, row data 4; the scale array is its own LDS array
+              check_lane(cfg, d, 0, 4, 4 * len[v], 0, 4 * len[v], (uint32_t)(rows[v] * 4), rows[v], 4, 4, true);
+            }
     }
   std::printf("ok %s\n", cfg);
 }
@@ -285,6 +306,13 @@ int main() {
     audit_fp8<128, 128, 4>(s[0], s[1], s[2]);
     audit_fp8<256, 192, 2>(s[0], s[1], s[2]);
     audit_fp8<256, 256, 2>(s[0], s[1], s[2]);
+  }
+  for (auto& s : {std::pair<int, int>{4096, 3072}, {300, 520}, {77, 100}, {513, 257}}) {
+    audit_fp8_scales(64, 64, s.first, s.second);
+    audit_fp8_scales(64, 128, s.first, s.second);
+    audit_fp8_scales(128, 128, s.first, s.second);
+    audit_fp8_scales(256, 192, s.first, s.second);
+    audit_fp8_scales(256, 256, s.first, s.second);
   }
   const int lora_shapes[][2] = {{64, 64}, {300, 520}, {4096, 3072}, {77, 100}, {513, 257}};
   for (auto& s : lora_shapes)

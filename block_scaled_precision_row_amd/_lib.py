@@ -51,6 +51,8 @@ SIGNATURES = {
                                           _p]),
     "bsq_gemm_nvfp4_q_quantize_y_fp8r": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
                                                 _p]),
+    "bsq_gemm_weight_only_quantize_y": (_int, [_int, _p, _i64, _p, _p, _p, _int, _p, _p, _p, _p, _i64, _i64, _i64,
+                                                _i64, _p, _sz, _p]),
     "bsq_lora_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _u32]),
     "bsq_gemm_fp8r_lora": (_int, [_p, _i64, _p, _p, _p, _p, _i64, _f32, _p, _i64, _i64, _i64, _i64, _u32, _p, _sz,
                                   _p]),
@@ -423,6 +425,29 @@ def bsq_gemm_nvfp4_q_quantize_y_fp8r(xq, x_bscale, input_scale, w, w_bscale, w_s
         _ptr(xq), _ptr(x_bscale), _ptr(input_scale), _ptr(w), _ptr(w_bscale), _ptr(w_scale2), _ptr(yq),
         _ptr(y_rowscale), _ptr(y), ldy, M, N, K, _ptr(ws), _nbytes(ws), _stream()))
     return yq, y_rowscale, y
+
+
+def bsq_gemm_weight_only_quantize_y(w_format, x, w, w_scale, w_scale2, out_format, y_global=None, with_y=False,
+                                    yq=None, yq_scale=None, y=None, workspace=None):
+    """Weight-only linear (bf16 x [M, K]; nvfp4 w [N, K/2] with uint8 block scales [N, K/16] and
+    w_scale2 [1], or E4M3 w [N, K] with fp32 row scales [N] and w_scale2 None) whose output is
+    also returned encoded for the next linear: (yq, yq_scale, bf16 y or None), as
+    bsq_gemm_fp8r_q_quantize_y."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N = w.shape[0]
+    if w_format == BSQ_FMT_NVFP4:
+        _dense(w, torch.uint8, (N, K // 2), "w")
+        _dense(w_scale, torch.uint8, (N, K // 16), "w_scale")
+        _scalar(w_scale2, "w_scale2")
+    else:
+        _dense(w, torch.uint8, (N, K), "w")
+        _dense(w_scale, torch.float32, (N,), "w_scale")
+    yq, yq_scale, y, ldy = _quantized_output(out_format, M, N, y_global, with_y, yq, yq_scale, y, x.device)
+    ws = _quantize_y_workspace(out_format, M, N, y, workspace, x.device)
+    _check("bsq_gemm_weight_only_quantize_y", lib.bsq_gemm_weight_only_quantize_y(
+        w_format, _ptr(x), ldx, _ptr(w), _ptr(w_scale), _ptr(w_scale2), out_format, _ptr(y_global), _ptr(yq),
+        _ptr(yq_scale), _ptr(y), ldy, M, N, K, _ptr(ws), _nbytes(ws), _stream()))
+    return yq, yq_scale, y
 
 
 def bsq_dequant_to_bf16(fmt, w, w_scale, w_scale2=None, out=None):

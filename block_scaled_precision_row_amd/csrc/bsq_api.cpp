@@ -503,6 +503,54 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y_fp8r(const uint8_t* xq, const uint8_t* x_
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
+bsq_status bsq_gemm_weight_only_quantize_y(bsq_format w_format, const uint16_t* x, int64_t ldx, const uint8_t* w,
+                                           const void* w_scale, const float* w_scale2, bsq_format out_format,
+                                           const float* y_global, uint8_t* yq, void* yq_scale, uint16_t* y,
+                                           int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (w_format != BSQ_FMT_FP8R && w_format != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;
+  if (w_format == BSQ_FMT_FP8R && w_scale2) return BSQ_ERR_ARG;
+  // without a bf16 output the shape is checked as for a dense [M][N] one, with yq standing in
+  bsq_status st = check_gemm_common(x, ldx, w, y ? y : reinterpret_cast<uint16_t*>(yq), y ? ldy : N, M, N, K, 0);
+  if (st != BSQ_OK) return st;
+  uint16_t* ybuf = nullptr;
+  int64_t ldb = 0;
+  float* pmax = nullptr;
+  st = check_quantize_y(out_format, y_global, yq, yq_scale, y, ldy, M, N, workspace, workspace_bytes, &ybuf, &ldb,
+                        &pmax);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!w_scale || (w_format == BSQ_FMT_NVFP4 && !w_scale2)) return BSQ_ERR_NULL;
+  if (!aligned(w_scale, 4) || (w_scale2 && !aligned(w_scale2, 4))) return BSQ_ERR_ALIGN;
+  if ((st = check_device()) != BSQ_OK) return st;
+  const bsq::DecMode mode = w_format == BSQ_FMT_NVFP4 ? bsq::kW4A16 : bsq::kW8A16;
+  bsq::DecArgs a{};
+  a.x = x; a.ldx = ldx; a.w = w; a.M = M; a.N = N; a.K = K;
+  if (mode == bsq::kW4A16) {
+    a.ws = static_cast<const uint8_t*>(w_scale);
+    a.gw = w_scale2;
+  } else {
+    a.sw = static_cast<const float*>(w_scale);
+  }
+  hipError_t e;
+  if (!route_skinny(mode, a) && bsq::gemm_a16_supported(mode, a)) {
+    if (out_format == BSQ_FMT_NVFP4) {  // encoded in the tiled epilogue; bf16 Y only if asked for
+      a.y = y; a.ldy = ldy;
+      a.yq = yq; a.ys = static_cast<uint8_t*>(yq_scale); a.gy = y_global;
+      e = bsq::launch_gemm_a16(mode, a, stream);
+    } else {  // row maxima in the epilogue, then the encoding pass over Y
+      a.y = ybuf; a.ldy = ldb; a.ypmax = pmax;
+      e = bsq::launch_gemm_a16(mode, a, stream);
+      if (e == hipSuccess)
+        e = bsq::launch_encode_fp8r_rows(ybuf, M, N, ldb, pmax, yq, static_cast<float*>(yq_scale), stream);
+    }
+  } else {  // few tokens or the decode GEMM: bf16 Y, then the quantizer over it
+    a.y = ybuf; a.ldy = ldb;
+    e = launch_dec_or_skinny(mode, a, stream);
+    if (e == hipSuccess) e = quantize_y_after(out_format, ybuf, ldb, M, N, y_global, yq, yq_scale, stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
 size_t bsq_lora_workspace_bytes(bsq_format f, int64_t M, int64_t N, int64_t K, int64_t rank, uint32_t flags) {
   if ((f != BSQ_FMT_FP8R && f != BSQ_FMT_NVFP4) || M <= 0 || K <= 0 || rank <= 0) return 0;
   return bsq_gemm_workspace_bytes(f, M, N, K, flags) + ws_lora_down(M, K, rank);

@@ -274,7 +274,13 @@ void gemm_a16_kernel(DecArgs a) {
     }
   }
   __syncthreads();
-  store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid, a.stream_y != 0);
+  if (a.y) store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid, a.stream_y != 0);
+  // optionally Y encoded for the next quantized linear ("BFL (fp8r / nvfp4)": every quantized
+  // linear quantizes its input at run time), from the same bf16 values: nvfp4 16-blocks along
+  // this N (inside the tile), or the row maxima of an fp8r encoding (its row scale spans every
+  // tile of the row; one pass after the GEMM encodes)
+  if (a.yq) quant_tile_rows<BM, BN, C::TROW>(smem, a.yq, a.ys, 1.0f / a.gy[0], M, N, m0, n0, tid);
+  if (a.ypmax) rowmax_tile<BM, BN, C::TROW>(smem, a.ypmax, M, N, m0, n0, tid);
 }
 
 template <int BM, int BN, int MODE>

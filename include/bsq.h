@@ -256,6 +256,34 @@ bsq_status bsq_gemm_nvfp4_q_quantize_y_fp8r(const uint8_t* xq, const uint8_t* x_
                                             hipStream_t stream);
 
 /*
+ * Weight-only linears (the BSQ_WEIGHT_ONLY semantics of bsq_gemm_nvfp4 and
+ * bsq_gemm_fp8r: bf16 activations, W4A16 or W8A16) whose output is also
+ * handed to the next quantized linear, encoded exactly as the activation
+ * quantizers encode that bf16 Y ("BFL (fp8r / nvfp4)": every quantized linear
+ * quantizes its input at run time; a weight-only producer can feed one):
+ *   w_format BSQ_FMT_NVFP4: w [N][K/2] packed E2M1, w_scale = E4M3 block
+ *     scales uint8 [N][K/16], w_scale2 [1] fp32 (K % 64 == 0 for the fused
+ *     tiled route; other K run the GEMM, then the quantizer);
+ *   w_format BSQ_FMT_FP8R: w [N][K] E4M3, w_scale = fp32 row scales [N],
+ *     w_scale2 must be NULL;
+ *   x [M][ldx] bf16 (ldx % 8 == 0);
+ *   out_format, y_global, yq, yq_scale, y, ldy, workspace: as
+ *     bsq_gemm_fp8r_q_quantize_y (same workspace query,
+ *     bsq_gemm_quantize_y_workspace_bytes).
+ * Y is, bit for bit, what bsq_gemm_nvfp4 / bsq_gemm_fp8r with
+ * BSQ_WEIGHT_ONLY return. On the tiled route the nvfp4 blocks are encoded in
+ * the GEMM's epilogue and an fp8r encoding takes the epilogue's row maxima and
+ * one pass; few-token and decode-GEMM shapes run the GEMM and then the
+ * quantizer. Errors: BSQ_ERR_ARG for an unknown format or a w_scale2 with fp8r
+ * weights, otherwise as bsq_gemm_fp8r_q_quantize_y.
+ */
+bsq_status bsq_gemm_weight_only_quantize_y(bsq_format w_format, const uint16_t* x, int64_t ldx, const uint8_t* w,
+                                           const void* w_scale, const float* w_scale2, bsq_format out_format,
+                                           const float* y_global, uint8_t* yq, void* yq_scale, uint16_t* y,
+                                           int64_t ldy, int64_t M, int64_t N, int64_t K, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Low-rank adapter (LoRA) side path on the quantized linear. "FLUX 3 Image
  * Klein vs Qwen-Image-2.1" (model overview) and the FLUX 3 Image Klein
  * open-source release page (section three, speed figures): the quantized

@@ -33,13 +33,31 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 24
+    assert len(syms) == 25
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
         assert s in _lib.SIGNATURES, s
     assert L.bsq_abi_version() == 3
     assert L.bsq_status_string(SHAPE).decode().startswith("invalid shape")
+
+
+def test_weight_only_quantized_output_validation():
+    fp8, nv = _lib.BSQ_FMT_FP8R, _lib.BSQ_FMT_NVFP4
+    g = L.bsq_gemm_weight_only_quantize_y
+    ws = L.bsq_gemm_quantize_y_workspace_bytes(fp8, 64, 64, 0)
+    # w_fmt, x, ldx, w, w_scale, w_scale2, out_fmt, y_global, yq, yq_scale, y, ldy, M, N, K, ws, ws_bytes, stream
+    assert g(3, A, 64, B, C, None, fp8, None, A, B, None, 0, 64, 64, 64, A, ws, None) == ARG     # weight format
+    assert g(fp8, A, 64, B, C, D, fp8, None, A, B, None, 0, 64, 64, 64, A, ws, None) == ARG      # fp8r: no scale2
+    assert g(nv, A, 64, B, C, None, fp8, None, A, B, None, 0, 64, 64, 64, A, ws, None) == NULL   # nvfp4: scale2
+    assert g(fp8, A, 64, B, None, None, fp8, None, A, B, None, 0, 64, 64, 64, A, ws, None) == NULL  # w_scale
+    assert g(fp8, A, 64, B, C, None, 3, None, A, B, None, 0, 64, 64, 64, A, ws, None) == ARG     # output format
+    assert g(fp8, A, 64, B, C, None, nv, None, A, B, None, 0, 64, 64, 64, A, ws, None) == NULL   # nvfp4 out: global
+    assert g(fp8, A, 64, B, C, None, fp8, None, A, B, None, 0, 64, 48, 64, A, ws, None) == SHAPE  # N % 32
+    assert g(fp8, A, 60, B, C, None, fp8, None, A, B, None, 0, 64, 64, 64, A, ws, None) == SHAPE  # ldx < K
+    assert g(fp8, A, 64, B, C, None, fp8, None, ODD, B, None, 0, 64, 64, 64, A, ws, None) == ALIGN  # yq
+    assert g(fp8, A, 64, B, C, None, fp8, None, A, B, None, 0, 64, 64, 64, A, ws - 1, None) == WS
+    assert g(fp8, None, 64, None, None, None, fp8, None, None, None, None, 0, 0, 64, 64, None, 0, None) == OK  # empty
 
 
 def test_workspace_sizes():

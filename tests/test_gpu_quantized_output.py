@@ -117,3 +117,59 @@ def test_fp8r_output_of_rows_with_zeros_and_one_large_value():
     torch.cuda.synchronize()
     _check_encoding(yq, yd, y_plain, "fp8r")
     assert np.all(_bits(yd)[::7] == 0)
+
+
+# Weight-only producers (bf16 activations): the tiled weight-only kernels (256 x 192 and 128 x 128
+# nvfp4 tiles, 128 x 256 E4M3 tiles at these sizes), the few-token kernels, and for nvfp4 weights
+# with K % 64 != 0 the decode GEMM (the last three run the GEMM, then the quantizer).
+WO_SHAPES = [(4096, 3072, 3072), (1000, 4960, 512), (300, 544, 512), (20, 1024, 512), (300, 512, 96), (1, 32, 32)]
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+@pytest.mark.parametrize("wfmt", ["fp8r", "nvfp4"])
+@pytest.mark.parametrize("M,N,K", WO_SHAPES)
+def test_weight_only_linear_with_quantized_output(M, N, K, wfmt, fmt):
+    print("weight-only %s producer -> %s M=%d N=%d K=%d" % (wfmt, fmt, M, N, K), flush=True)
+    x = syn.normal_bf16((M, K), 59, M, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 59, 4000 + N, sigma=0.02)
+    dx = dev_bf16(x)
+    rows = np.arange(M) if M <= 1024 else np.arange(0, M, 8)
+    if wfmt == "fp8r":
+        wq, sw = quant.quantize_fp8r(w)
+        wargs = (L.BSQ_FMT_FP8R, dx, dev(wq), dev(sw), None)
+        y_plain = _bits(L.bsq_gemm_fp8r(dx, dev(wq), dev(sw), flags=L.BSQ_WEIGHT_ONLY))
+        ref = gemm.gemm_fp8r_weight_only(x[rows], wq, sw)
+    else:
+        gw = quant.calibrate_global_scale(w)
+        wq, ws = quant.quantize_nvfp4(w, gw)
+        wargs = (L.BSQ_FMT_NVFP4, dx, dev(wq), dev(ws), dev_scalar(gw))
+        y_plain = _bits(L.bsq_gemm_nvfp4(dx, dev(wq), dev(ws), dev_scalar(gw), None, flags=L.BSQ_WEIGHT_ONLY))
+        ref = gemm.gemm_nvfp4_weight_only(x[rows], wq, ws, gw)
+    torch.cuda.synchronize()
+    assert_gemm_close(y_plain[rows], ref, "weight-only %s %dx%dx%d" % (wfmt, M, N, K))
+    out = L.BSQ_FMT_FP8R if fmt == "fp8r" else L.BSQ_FMT_NVFP4
+    gy = None if fmt == "fp8r" else quant.calibrate_global_scale(y_plain)
+    gyd = None if gy is None else dev_scalar(gy)
+    for with_y in (True, False):
+        yq, ys, y = L.bsq_gemm_weight_only_quantize_y(*wargs, out, gyd, with_y=with_y)
+        torch.cuda.synchronize()
+        if with_y:
+            assert np.array_equal(_bits(y), y_plain), "bf16 output differs from the weight-only linear"
+        else:
+            assert y is None
+        _check_encoding(yq, ys, y_plain, fmt, gy)
+
+
+def test_weight_only_quantized_output_strided_input():
+    """x with a row pitch wider than K (a view of a wider matrix), on the tiled route."""
+    M, N, K = 1024, 3072, 512
+    full = syn.normal_bf16((M, K + 64), 60, M)
+    w = syn.normal_bf16((N, K), 60, 4000 + N, sigma=0.02)
+    wq, sw = quant.quantize_fp8r(w)
+    dx = dev_bf16(full)[:, :K]
+    y_plain = _bits(L.bsq_gemm_fp8r(dx, dev(wq), dev(sw), flags=L.BSQ_WEIGHT_ONLY))
+    yq, yd, y = L.bsq_gemm_weight_only_quantize_y(L.BSQ_FMT_FP8R, dx, dev(wq), dev(sw), None, L.BSQ_FMT_FP8R, None,
+                                                  with_y=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y), y_plain)
+    _check_encoding(yq, yd, y_plain, "fp8r")

@@ -160,7 +160,7 @@ def cpu_model():
     return None
 
 
-def quantized_output_comparison(L, dev, y3, y2, gemm3_args, gemm2_args, operands3, operands2):
+def quantized_output_comparison(L, dev, y3, y2, gemm3_args, gemm2_args, operands3, operands2, x3):
     """Linears feeding another quantized linear, in both producers and both output formats: the
     GEMM followed by the activation quantizer over its bf16 Y, against the GEMM that encodes Y
     itself (nvfp4 in its epilogue; fp8r from per-segment row maxima written by the epilogue and
@@ -247,9 +247,33 @@ def quantized_output_comparison(L, dev, y3, y2, gemm3_args, gemm2_args, operands
                 fmt, gy, P(qq), P(qs), P(y2), N_FP8, M, N_FP8, K, P(wy), nwy, stream))]),
         }
     out["fp8r_4096x3072x3072"] = entry
-    out["note"] = ("us per linear (GEMM on pre-quantized activations + the next linear's input encoding); "
-                   "fused = the producer encodes its own output (nvfp4 in the epilogue, fp8r from the "
-                   "epilogue's per-segment row maxima and one encoding pass)")
+    # weight-only W4A16 linear 4096 x 12288 x 3072 (bf16 X) as the producer
+    q4 = torch.empty((M, N_FP4 // 2), dtype=torch.uint8, device=dev)
+    s4 = torch.empty((M, N_FP4 // 16), dtype=torch.uint8, device=dev)
+    q8 = torch.empty((M, N_FP4), dtype=torch.uint8, device=dev)
+    d8 = torch.empty((M,), dtype=torch.float32, device=dev)
+    wo_gemm = (lib.bsq_gemm_nvfp4, (P(x3), K, P(w3q), P(w3s), P(g3), None, P(y3), N_FP4, M, N_FP4, K,
+                                    L.BSQ_WEIGHT_ONLY, None, 0, stream))
+    entry = {}
+    for name, fmt in (("to_nvfp4", nv), ("to_fp8r", fp8)):
+        qq, qs = (q4, s4) if fmt == nv else (q8, d8)
+        gy = P(gy3) if fmt == nv else None
+        quantizer = ((lib.bsq_quantize_act_nvfp4, (P(y3), M, N_FP4, N_FP4, P(gy3), P(q4), P(s4), stream)) if fmt == nv
+                     else (lib.bsq_quantize_act_fp8r, (P(y3), M, N_FP4, N_FP4, P(q8), P(d8), stream)))
+        wy, nwy = ws(fmt, M, N_FP4, True)
+        wn, nwn = ws(fmt, M, N_FP4, False)
+        fused = lambda y, ldy, wsp, nws: (lib.bsq_gemm_weight_only_quantize_y, (
+            nv, P(x3), K, P(w3q), P(w3s), P(g3), fmt, gy, P(qq), P(qs), y, ldy, M, N_FP4, K, wsp, nws, stream))
+        entry[name] = {
+            "gemm_then_quantizer": time_calls([wo_gemm, quantizer]),
+            "fused_no_bf16_y": time_calls([fused(None, 0, P(wn), nwn)]),
+            "fused_with_bf16_y": time_calls([fused(P(y3), N_FP4, P(wy), nwy)]),
+        }
+    out["w4a16_4096x12288x3072"] = entry
+    out["note"] = ("us per linear (GEMM on pre-quantized activations, or for the W4A16 producer on bf16 "
+                   "activations, + the next linear's input encoding); fused = the producer encodes its own "
+                   "output (nvfp4 in the epilogue, fp8r from the epilogue's per-segment row maxima and one "
+                   "encoding pass)")
     return out
 
 
@@ -761,7 +785,7 @@ def main():
     if not args.no_quant_out:
         log("quantized-output comparison")
         result["quantized_output_us"] = quantized_output_comparison(
-            L, dev, y3, y2, seq[DOM][1], seq[FP8][1], (x3q, x3s, gx3, w3q, w3s, g3), (x2q, x2s, w2q, w2s))
+            L, dev, y3, y2, seq[DOM][1], seq[FP8][1], (x3q, x3s, gx3, w3q, w3s, g3), (x2q, x2s, w2q, w2s), x3)
     if not args.no_vendor:
         log("vendor-library GEMM context")
         result["vendor_gemm_context"] = vendor_gemm_context(dev)

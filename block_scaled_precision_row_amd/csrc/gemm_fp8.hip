@@ -160,9 +160,10 @@ constexpr bool hand_ordered() { return NS == 2; }
 
 // OQ: quantized output for the next linear -- 0 none, 1 nvfp4 blocks in the epilogue, 2 the
 // row maxima of the fp8r encoding (YQuant). HS: the hand-ordered K loop (K % 128 == 0). LL:
-// where the adapter's T and B rows are read (LoraLds).
-template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, int LL = kLoraGlobal>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// where the adapter's T and B rows are read (LoraLds). WPE: waves per SIMD the registers are
+// budgeted for (2: two workgroups share a compute unit).
+template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, int LL = kLoraGlobal, int WPE = 1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                      const uint8_t* __restrict__ w, const float* __restrict__ sw,
                      uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, const uint16_t* lt,
@@ -413,20 +414,32 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   if constexpr (OQ == 2) rowmax_tile<BM, BN, C::TROW>(smem, q.pmax, M, N, m0, n0, tid);
 }
 
-template <int BM, int BN, int NS, bool HS>
+template <int BM, int BN, int NS, bool HS, int WPE = 1>
 hipError_t launch_oq(int oq, int tiles, const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                      uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int st, const YQuant& qv,
                      hipStream_t s) {
   if (oq == 1)
-    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 1, HS>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
-                       y, ldy, (int)M, (int)N, (int)K, nullptr, nullptr, 0, st, qv);
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 1, HS, kLoraGlobal, WPE>), dim3(tiles), dim3(kThreads), 0,
+                       s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, nullptr, nullptr, 0, st, qv);
   else if (oq == 2)
-    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 2, HS>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
-                       y, ldy, (int)M, (int)N, (int)K, nullptr, nullptr, 0, st, qv);
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 2, HS, kLoraGlobal, WPE>), dim3(tiles), dim3(kThreads), 0,
+                       s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, nullptr, nullptr, 0, st, qv);
   else
-    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 0, HS>), dim3(tiles), dim3(kThreads), 0, s, xq, sx, w, sw,
-                       y, ldy, (int)M, (int)N, (int)K, nullptr, nullptr, 0, st, qv);
+    hipLaunchKernelGGL((gemm_fp8_kernel<BM, BN, NS, false, 0, HS, kLoraGlobal, WPE>), dim3(tiles), dim3(kThreads), 0,
+                       s, xq, sx, w, sw, y, ldy, (int)M, (int)N, (int)K, nullptr, nullptr, 0, st, qv);
   return hipGetLastError();
+}
+
+// 128 x 128 tiles with two stage buffers and the hand-ordered loop, two workgroups per compute
+// unit (65 KB of LDS and at most 256 registers a lane each), so one workgroup's barrier waits,
+// prologue and output write overlap the other's K loop: 512 tiles a round
+hipError_t run_pair(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw, uint16_t* y, int64_t ldy,
+                    int64_t M, int64_t N, int64_t K, hipStream_t s, const YQuant* q) {
+  const int tiles = (int)(((M + 127) / 128) * ((N + 127) / 128));
+  const int st = (int)stream_output((M + N) * K, M, N);
+  const YQuant qv = q ? *q : YQuant{};
+  const int oq = qv.yq ? 1 : qv.pmax ? 2 : 0;
+  return launch_oq<128, 128, 2, true, 2>(oq, tiles, xq, sx, w, sw, y, ldy, M, N, K, st, qv, s);
 }
 
 template <int BM, int BN, int NS>
@@ -494,6 +507,12 @@ hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w,
   if (t64x128 <= 256) return run<64, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
   const int64_t c256 = lt ? INT64_MAX : rounds_cost(M, N, 256, 256, 92);
   const int64_t c192 = rounds_cost(M, N, 256, 192, 72), c128 = rounds_cost(M, N, 128, 128, 31);
+  // 128 x 128 tiles two to a compute unit (no adapter, K % 128 == 0): 512 tiles a round at
+  // about 26 us (K = 3072), which wins between 256 and 512 of them -- 2048 x 3072 28.3 -> 22.7 us,
+  // 1536 x 3072 28.0 -> 21.7 us, 2048 x 4096 31.3 -> 26.6 us, 2500 x 3072 30.5 -> 25.7 us
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t c2 = lt || K % kStageK != 0 || t128 <= 256 ? INT64_MAX : (t128 + 511) / 512 * 52;
+  if (c2 < c256 && c2 < c192 && c2 < c128) return run_pair(xq, sx, w, sw, y, ldy, M, N, K, s, q);
   if (c256 <= c192 && c256 <= c128) return run<256, 256, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
   if (c192 <= c128) return run<256, 192, 2>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);
   return run<128, 128, 4>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, s, q);

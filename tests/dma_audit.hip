@@ -304,6 +304,7 @@ int main() {
     audit_fp8<64, 64, 4>(s[0], s[1], s[2]);
     audit_fp8<64, 128, 4>(s[0], s[1], s[2]);
     audit_fp8<128, 128, 4>(s[0], s[1], s[2]);
+    audit_fp8<128, 128, 2>(s[0], s[1], s[2]);  // two workgroups a compute unit, hand-ordered loop
     audit_fp8<256, 192, 2>(s[0], s[1], s[2]);
     audit_fp8<256, 256, 2>(s[0], s[1], s[2]);
   }

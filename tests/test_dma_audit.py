@@ -33,7 +33,8 @@ def test_every_lds_dma_load_is_in_bounds(tmp_path):
     assert r.returncode == 0, r.stdout[-2000:]
     assert "all LDS-DMA loads in bounds" in r.stdout
     # every kernel family was enumerated
-    for family in ("fp8 256x192", "fp8 256x256", "fp8 scales 256x192", "fp8 scales 64x64", "fp8 adapter rows 256x192", "fp8 adapter rows late 256x192", "w4a4 256x256", "a16 nvfp4",
+    for family in ("fp8 256x192", "fp8 128x128 ring 2", "fp8 256x256", "fp8 scales 256x192", "fp8 scales 64x64",
+                   "fp8 adapter rows 256x192", "fp8 adapter rows late 256x192", "w4a4 256x256", "a16 nvfp4",
                    "a16 e4m3", "skinny w8a8", "skinny w8a16"):
         assert re.search(r"^ok %s" % family, r.stdout, re.M), family
 

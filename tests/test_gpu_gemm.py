@@ -234,7 +234,8 @@ def test_fp8r_square_tiles(M, N, K):
 # The large-grid tile choice counts whole rounds of tiles on the 256 compute units: 3100 x
 # 4000 takes 256 x 256 tiles in one round (256 x 192 would need two), 4100 x 4100 takes 256 x
 # 192 tiles in two rounds (256 x 256 and 128 x 128 would need two and five), 1000 x 5000 takes
-# 128 x 128 tiles, on both the fp8r and the W4A4 GEMM; all with ragged M and N tails.
+# 128 x 128 tiles (on the fp8r GEMM two workgroups a compute unit), on both the fp8r and the W4A4
+# GEMM; all with ragged M and N tails.
 ROUND_SHAPES = [(3100, 4000, 768), (4100, 4100, 768), (1000, 5000, 512)]
 
 
@@ -244,6 +245,19 @@ def test_large_grid_tile_choice(M, N, K):
     w = syn.normal_bf16((N, K), 57, 7000 + N, sigma=0.02)
     run_fp8r(x, w, sample=96, what="fp8r rounds %dx%dx%d" % (M, N, K))
     run_nvfp4(x, w, sample=96, what="nvfp4 rounds %dx%dx%d" % (M, N, K))
+
+
+# Between 256 and 512 tiles of 128 x 128 (K % 128 == 0) the fp8r GEMM runs them two workgroups
+# a compute unit on the hand-ordered loop: 2048 x 3072 (384 tiles), ragged 2500 x 3000 (480) and
+# 1500 x 3000 (288, K = 384: three stages); the same bits as any other tile.
+PAIR_SHAPES = [(2048, 3072, 3072), (2500, 3000, 512), (1500, 3000, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", PAIR_SHAPES)
+def test_fp8r_paired_tiles(M, N, K):
+    x = syn.normal_bf16((M, K), 58, M + N, outlier_frac=0.01)
+    w = syn.normal_bf16((N, K), 58, 7500 + N, sigma=0.02)
+    run_fp8r(x, w, sample=96, what="fp8r paired 128x128 %dx%dx%d" % (M, N, K))
 
 
 # Small grids (a few hundred tokens) run 64 x 64 or 64 x 128 tiles: ragged M and N tails, two

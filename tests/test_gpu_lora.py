@@ -152,7 +152,7 @@ def test_fp8r_adapter_late_copy(M, N, K, rank):
 
 
 @pytest.mark.parametrize("M,N,K,rank", ROUTE_SHAPES + [(4096, 3072, 3072, 32), (4096, 3072, 640, 64),
-                                            (4096, 3072, 640, 128)])
+                                            (4096, 3072, 640, 128), (2048, 3072, 512, 16)])
 @pytest.mark.parametrize("scheme,weight_only", SCHEMES)
 def test_zero_scale_is_the_plain_linear_bit_for_bit(scheme, weight_only, M, N, K, rank):
     x, w, a, b = _inputs(M, N, K, rank, 2)

@@ -27,6 +27,7 @@ SHAPES = [
     (3100, 4000, 768),   # 256 x 256 tiles, ragged M, N % 64 == 32
     (1000, 4960, 512),   # 128 x 128 tiles, ragged M and N
     (300, 512, 512),     # 64 x 64 tiles, ragged M
+    (2048, 3040, 512),   # fp8r: 128 x 128 tiles two to a compute unit, N % 64 == 32
     (20, 1024, 512),     # few tokens
     (64, 16416, 256),    # rows longer than 16384 values (the encode pass reads Y for the maximum)
     (1, 32, 32),         # smallest

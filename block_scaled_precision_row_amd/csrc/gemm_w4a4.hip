@@ -92,8 +92,8 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q) {
   return T == 0 ? q.x : T == 1 ? q.y : T == 2 ? q.z : q.w;
 }
 
-template <int BM, int BN, bool LORA>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, bool LORA, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_w4a4_kernel(DecArgs a) {
   using C = W4Cfg<BM, BN>;
   constexpr int TN = C::TN, TM = C::TM;
@@ -290,13 +290,17 @@ void gemm_w4a4_kernel(DecArgs a) {
   if (a.ypmax) rowmax_tile<BM, BN, C::TROW>(smem, a.ypmax, M, N, m0, n0, tid);
 }
 
+// WPE: waves per SIMD the registers are budgeted for. The 128 x 128 tile takes 72 KB of LDS, so
+// two of its workgroups share a compute unit when each wave keeps to 256 registers; the decode
+// VALU of one then overlaps the other's MFMAs.
 template <int BM, int BN>
 hipError_t run(const DecArgs& a, hipStream_t s) {
+  constexpr int WPE = BM == 128 && BN == 128 ? 2 : 1;
   const int tiles = (int)(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN));
   if (a.lt)
-    hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, true>), dim3(tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, true, WPE>), dim3(tiles), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, false>), dim3(tiles), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, false, WPE>), dim3(tiles), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -313,17 +317,18 @@ hipError_t launch_gemm_w4a4(const DecArgs& args, hipStream_t s) {
   // one waits on its own loads. Measured at K = 3072: 512 x 3072 26.6 -> 19.2 us, 256 x 3072
   // 27 -> 13.3 us, 64 x 12288 29 -> 14 us, 512 x 3072 x 12288 88 -> 64 us.
   //
-  // Larger grids take the tile of least expected time over whole rounds, with per-tile times
-  // measured at K = 3072 with every unit busy: 256 x 256 76 us, 256 x 192 60 us, 128 x 128
-  // 26 us (the square tile does the most work per operand byte and per decode, so it wins when
-  // the rounds come out even, as at 4096 x 12288: 230 vs 240 us). Where they do not:
-  // 3072 x 3072 75 -> 53 us and 4096 x 6144 136 -> 122 us on 256 x 192, 2048 x 3072 54 -> 50
-  // us on 128 x 128. Every tile shape gives the same bits.
+  // Larger grids take the tile of least expected time over whole rounds, with round times
+  // measured at K = 3072 with every unit busy: 256 x 256 76 us and 256 x 192 60 us for 256
+  // tiles, 128 x 128 49 us for 512 (two workgroups a compute unit). The square tile does the
+  // most work per operand byte and per decode, so it wins when the rounds come out even, as at
+  // 4096 x 12288: 230 vs 240 us. Where they do not: 3072 x 3072 75 -> 53 us and 4096 x 6144
+  // 136 -> 122 us on 256 x 192; 2048 x 3072 54 -> 43 us and 1536 x 3072 48 -> 41 us on
+  // 128 x 128. Every tile shape gives the same bits.
   const int64_t t64 = ((a.M + 63) / 64) * ((a.N + 63) / 64), t64x128 = ((a.M + 63) / 64) * ((a.N + 127) / 128);
   if (t64 <= 256) return run<64, 64>(a, s);
   if (t64x128 <= 256) return run<64, 128>(a, s);
   const int64_t c256 = rounds_cost(a.M, a.N, 256, 256, 76), c192 = rounds_cost(a.M, a.N, 256, 192, 60);
-  const int64_t c128 = rounds_cost(a.M, a.N, 128, 128, 26);
+  const int64_t c128 = ((a.M + 127) / 128 * ((a.N + 127) / 128) + 511) / 512 * 49;
   if (c256 <= c192 && c256 <= c128) return run<256, 256>(a, s);
   if (c192 <= c128) return run<256, 192>(a, s);
   return run<128, 128>(a, s);

@@ -265,8 +265,24 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
 #pragma unroll
     for (int j = 0; j < TM; ++j) b0[j] = frag(abuf(0) + C::A_BYTES, rowb + 32 * j, lh, 0);
 
-    auto iter = [&](int s, auto fetch) {
-      constexpr bool F = decltype(fetch)::value;
+    // the epilogue's scaling and bf16 conversion of accumulator tile t into the LDS copy of the
+    // output tile (see the epilogue below; without an adapter)
+    auto tile_out = [&](int t) {
+      const int i = t / TM, j = t % TM;
+      const int ml = wm * C::WM + j * 32 + lr;
+      const float xs = s_sx[ml];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
+        const v16f& A = acc[i][j];
+        const float4 s4 = *reinterpret_cast<const float4*>(&s_sw[nl]);
+        *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
+            make_uint2(pack_bf16x2(A[4 * g + 0] * xs * s4.x, A[4 * g + 1] * xs * s4.y),
+                       pack_bf16x2(A[4 * g + 2] * xs * s4.z, A[4 * g + 3] * xs * s4.w));
+      }
+    };
+    auto iter = [&](int s, auto fetch, auto last) {
+      constexpr bool F = decltype(fetch)::value, LAST = decltype(last)::value;
       const uint8_t* ca = abuf(s);
       const uint8_t* cb = ca + C::A_BYTES;
 #pragma unroll
@@ -286,6 +302,19 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
       if constexpr (!F) {
         if (s == nk - 2) lora_late(s % NS, 0);
         if (LL == kLoraLate2 && s == nk - 1) lora_late(s % NS, 64);
+      }
+      if constexpr (LAST) {
+        // the last stage without an adapter: once every wave has passed the barrier above no
+        // stage buffer is read any more, so each tile is scaled and written to the output copy
+        // while the next tile's last MFMA runs
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+          const int i = k / TM, j = k % TM;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[i], b1[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+          if (k > 0) tile_out(k - 1);
+        }
+        tile_out(NM - 1);
+        return;
       }
       const uint8_t* na = abuf(s + 1);
       const uint8_t* nb = na + C::A_BYTES;
@@ -318,8 +347,9 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
       }
     };
     int s = 0;
-    for (; s + 2 < nk; ++s) iter(s, std::true_type{});
-    for (; s < nk; ++s) iter(s, std::false_type{});
+    for (; s + 2 < nk; ++s) iter(s, std::true_type{}, std::false_type{});
+    for (; s + 1 < nk; ++s) iter(s, std::false_type{}, std::false_type{});
+    iter(s, std::false_type{}, std::integral_constant<bool, !LORA>{});
   } else {
   // prologue: NS stages in flight, wait for the first
 #pragma unroll
@@ -389,8 +419,10 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   }
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
+  // (the hand-ordered loop without an adapter has written the output copy in its last stage)
+  constexpr bool kWritten = HS && !LORA;
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
+  for (int j = 0; j < (kWritten ? 0 : TM); ++j) {
     const int ml = wm * C::WM + j * 32 + lr;
     const float xs = LORA ? 1.0f : s_sx[ml];
 #pragma unroll

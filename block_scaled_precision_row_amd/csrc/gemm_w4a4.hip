@@ -98,6 +98,7 @@ void gemm_w4a4_kernel(DecArgs a) {
   using C = W4Cfg<BM, BN>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+  __shared__ __attribute__((aligned(16))) float s_g[2][64];  // gx, gw (lane 0 of two dword DMAs)
 
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   int m0, n0;
@@ -113,6 +114,12 @@ void gemm_w4a4_kernel(DecArgs a) {
   const v4i rxs = buffer_rsrc(a.xs + (int64_t)m0 * ks, (uint32_t)(rows_x * ks));
   const v4i rws = buffer_rsrc(a.ws + (int64_t)n0 * ks, (uint32_t)(rows_w * ks));
   const uint32_t lds0 = lds_offset(smem);
+  // the two global scales, by dword LDS DMA ahead of the first stage (older than every stage
+  // load, so the prologue's wait covers them): the last stage scales the accumulators in the loop
+  if (wave == 0) {
+    dma4(buffer_rsrc(a.gx, 4u), lds_offset(s_g[0]), lane == 0 ? 0 : kOutOfRange, 0);
+    dma4(buffer_rsrc(a.gw, 4u), lds_offset(s_g[1]), lane == 0 ? 0 : kOutOfRange, 0);
+  }
 
   // fetch stage kt into buffer kt % 2 (stages past K read as zeros)
   auto issue_stage = [&](int kt) {
@@ -187,25 +194,55 @@ void gemm_w4a4_kernel(DecArgs a) {
   using NV = std::integral_constant<int, 8 * (TN + TM) / (TN * TM) + 1>;  // decode VALU per MFMA
   using NV2 = std::integral_constant<int, 8 * (TN + TM) / (TN * TM) + 3>;
 
+  // the epilogue's scaling by gx gw and bf16 conversion of accumulator tile t into the LDS copy
+  // of the output tile [BM][BN]
+  auto tile_out = [&](int t, float alpha) {
+    const int i = t / TM, j = t % TM;
+    const int ml = wm * C::WM + j * 32 + lr;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
+      const v16f& A = acc[i][j];
+      *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
+          make_uint2(pack_bf16x2(A[4 * g + 0] * alpha, A[4 * g + 1] * alpha),
+                     pack_bf16x2(A[4 * g + 2] * alpha, A[4 * g + 3] * alpha));
+    }
+  };
+
   // K group q of a stage: operands in ca/cb (K step 0 decoded in d0, scale pairs of the group
   // in spa/spb); the next group's packed bytes are read into na/nb from `nst` (group nq, whose
-  // scales are in nsa/nsb) and its K step 0 decoded into d0
+  // scales are in nsa/nsb) and its K step 0 decoded into d0. The last group of the last stage
+  // (LG) reads nothing ahead; once every wave has passed the last stage's barrier no stage
+  // buffer is read any more, so each accumulator tile is scaled and written to the output copy
+  // while the next tile's last MFMA runs.
   auto group = [&](const Raw (&ca)[TN], const Raw (&cb)[TM], Raw (&na)[TN], Raw (&nb)[TM], const uint8_t* nst,
-                   int nq, const uint2 (&nsa)[TN], const uint2 (&nsb)[TM]) {
-    read_raw<TN, TM>(nst, C::A_OFF, C::B_OFF, rowa, rowb, lh, nq, na, nb);
+                   int nq, const uint2 (&nsa)[TN], const uint2 (&nsb)[TM], auto lg) {
+    constexpr bool LG = decltype(lg)::value;
+    if constexpr (!LG) read_raw<TN, TM>(nst, C::A_OFF, C::B_OFF, rowa, rowb, lh, nq, na, nb);
     decode_step(I1{}, ca, cb, d1a, d1b);
     mfmas(d0a, d0b);
-    pipeline(NV{}, std::integral_constant<int, 1>{});
+    pipeline(NV{}, std::integral_constant<int, LG ? 0 : 1>{});
     decode_step(I2{}, ca, cb, d0a, d0b);
     mfmas(d1a, d1b);
     pipeline(NV{}, I0{});
     decode_step(I3{}, ca, cb, d1a, d1b);
-    scales_of(nsa, nsb, nq);
+    if constexpr (!LG) scales_of(nsa, nsb, nq);
     mfmas(d0a, d0b);
     pipeline(NV2{}, I0{});
-    decode_step(I0{}, na, nb, d0a, d0b);
-    mfmas(d1a, d1b);
-    pipeline(NV{}, I0{});
+    if constexpr (LG) {
+      const float alpha = s_g[0][0] * s_g[1][0];
+#pragma unroll
+      for (int k = 0; k < TN * TM; ++k) {
+        const int i = k / TM, j = k % TM;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d1a[i], d1b[j], acc[i][j], 0, 0, 0);
+        if (k > 0) tile_out(k - 1, alpha);
+      }
+      tile_out(TN * TM - 1, alpha);
+    } else {
+      decode_step(I0{}, na, nb, d0a, d0b);
+      mfmas(d1a, d1b);
+      pipeline(NV{}, I0{});
+    }
   };
 
   if constexpr (LORA) {
@@ -240,46 +277,42 @@ void gemm_w4a4_kernel(DecArgs a) {
 
   // Stage s sits in buffer s % 2 and stage s + 1 is in flight into the other one. Before the
   // last K group reads ahead into stage s + 1, every wave waits for its share of stage s + 1,
-  // the barrier publishes it (and ends all reads of stage s), and stage s + 2 is fetched into
-  // buffer s % 2. Past the last stage the read-ahead sees a buffer of zeros and goes unused.
-  auto stage = [&](int s, const uint2 (&csa)[TN], const uint2 (&csb)[TM], uint2 (&nsa)[TN], uint2 (&nsb)[TM]) {
+  // the barrier publishes it (and ends all reads of stage s), and stage s + 2 (if there is one)
+  // is fetched into buffer s % 2. Past the second-to-last stage the read-ahead sees a stale
+  // buffer and goes unused; the last stage reads nothing ahead.
+  using F = std::false_type;
+  auto stage = [&](int s, const uint2 (&csa)[TN], const uint2 (&csb)[TM], uint2 (&nsa)[TN], uint2 (&nsb)[TM],
+                   auto last) {
+    constexpr bool LAST = decltype(last)::value;
     const uint8_t* cur = smem + (s & 1) * C::STAGE;
     const uint8_t* nxt = smem + ((s + 1) & 1) * C::STAGE;
-    group(r0a, r0b, r1a, r1b, cur, 1, csa, csb);
-    group(r1a, r1b, r0a, r0b, cur, 2, csa, csb);
-    group(r0a, r0b, r1a, r1b, cur, 3, csa, csb);
+    group(r0a, r0b, r1a, r1b, cur, 1, csa, csb, F{});
+    group(r1a, r1b, r0a, r0b, cur, 2, csa, csb, F{});
+    group(r0a, r0b, r1a, r1b, cur, 3, csa, csb, F{});
     wait_vmcnt<0>();
     __syncthreads();
-    issue_stage(s + 2);
-    read_scales<TN, TM>(nxt, C::SA_OFF, C::SB_OFF, rowa, rowb, lh, nsa, nsb);
-    group(r1a, r1b, r0a, r0b, nxt, 0, nsa, nsb);
+    if (s + 2 < nk) issue_stage(s + 2);
+    if constexpr (!LAST) read_scales<TN, TM>(nxt, C::SA_OFF, C::SB_OFF, rowa, rowb, lh, nsa, nsb);
+    group(r1a, r1b, r0a, r0b, nxt, 0, nsa, nsb, last);
   };
+  using T = std::true_type;
   int s = 0;
-  for (; s + 1 < nk; s += 2) {
-    stage(s, s0a, s0b, s1a, s1b);
-    stage(s + 1, s1a, s1b, s0a, s0b);
+  for (; s + 2 < nk; s += 2) {
+    stage(s, s0a, s0b, s1a, s1b, F{});
+    stage(s + 1, s1a, s1b, s0a, s0b, F{});
   }
-  if (s < nk) stage(s, s0a, s0b, s1a, s1b);
+  if (s + 2 == nk) {
+    stage(s, s0a, s0b, s1a, s1b, F{});
+#pragma unroll
+    for (int i = 0; i < TN; ++i) s0a[i] = s1a[i];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) s0b[j] = s1b[j];
+    ++s;
+  }
+  stage(s, s0a, s0b, s1a, s1b, T{});
 
-  // ---- epilogue: y = bf16(acc * gx * gw) via an LDS copy of the tile [BM][BN]
-  const float alpha = a.gx[0] * a.gw[0];
-  wait_vmcnt<0>();
-  __syncthreads();  // all stage buffers are free now
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int ml = wm * C::WM + j * 32 + lr;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
-        const v16f& A = acc[i][j];
-        *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
-            make_uint2(pack_bf16x2(A[4 * g + 0] * alpha, A[4 * g + 1] * alpha),
-                       pack_bf16x2(A[4 * g + 2] * alpha, A[4 * g + 3] * alpha));
-      }
-    }
-  }
+  // ---- epilogue: y = bf16(acc * gx * gw), written to the LDS copy of the tile [BM][BN] by the
+  // last stage above, then stored
   __syncthreads();
   if (a.y) store_tile_rows<BM, BN, C::TROW>(smem, a.y, a.ldy, M, N, m0, n0, tid, a.stream_y != 0);
   // optionally the nvfp4 encoding of Y for the next linear ("BFL (fp8r / nvfp4)": every

@@ -217,6 +217,24 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   const int rowa = wn * C::WN + lr, rowb = wm * C::WM + lr;  // region-local rows
   const int nk = (K + kStageK - 1) / kStageK;
 
+  // the epilogue's scaling and bf16 conversion of accumulator tile t into the LDS copy of the
+  // output tile (see the epilogue below). The last K stage does it without an adapter; in the
+  // general loop only for the tiles whose registers hold it (the 256-row ones would spill).
+  constexpr bool kLoopOut = !LORA && (HS || BM * BN <= 128 * 128);
+  auto tile_out = [&](int t) {
+    const int i = t / TM, j = t % TM;
+    const int ml = wm * C::WM + j * 32 + lr;
+    const float xs = s_sx[ml];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
+      const v16f& A = acc[i][j];
+      const float4 s4 = *reinterpret_cast<const float4*>(&s_sw[nl]);
+      *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
+          make_uint2(pack_bf16x2(A[4 * g + 0] * xs * s4.x, A[4 * g + 1] * xs * s4.y),
+                     pack_bf16x2(A[4 * g + 2] * xs * s4.z, A[4 * g + 3] * xs * s4.w));
+    }
+  };
   v8i a0[TN], b0[TM], a1[TN], b1[TM];
   if constexpr (HS) {
     static_assert(NS == 2, "two stage buffers");
@@ -265,22 +283,6 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
 #pragma unroll
     for (int j = 0; j < TM; ++j) b0[j] = frag(abuf(0) + C::A_BYTES, rowb + 32 * j, lh, 0);
 
-    // the epilogue's scaling and bf16 conversion of accumulator tile t into the LDS copy of the
-    // output tile (see the epilogue below; without an adapter)
-    auto tile_out = [&](int t) {
-      const int i = t / TM, j = t % TM;
-      const int ml = wm * C::WM + j * 32 + lr;
-      const float xs = s_sx[ml];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
-        const v16f& A = acc[i][j];
-        const float4 s4 = *reinterpret_cast<const float4*>(&s_sw[nl]);
-        *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
-            make_uint2(pack_bf16x2(A[4 * g + 0] * xs * s4.x, A[4 * g + 1] * xs * s4.y),
-                       pack_bf16x2(A[4 * g + 2] * xs * s4.z, A[4 * g + 3] * xs * s4.w));
-      }
-    };
     auto iter = [&](int s, auto fetch, auto last) {
       constexpr bool F = decltype(fetch)::value, LAST = decltype(last)::value;
       const uint8_t* ca = abuf(s);
@@ -368,7 +370,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     __builtin_amdgcn_sched_barrier(0);
   };
   // stage s, its step 0 already in a0/b0. Stages past K read as zeros and go unused.
-  for (int s = 0; s < nk; ++s) {
+  for (int s = 0; s < nk - (kLoopOut ? 1 : 0); ++s) {
     const uint8_t* cur = smem + (s % NS) * C::STAGE;
     const uint8_t* nxt = smem + ((s + 1) % NS) * C::STAGE;
     read_ops<TN, TM>(cur, cur + C::A_BYTES, rowa, rowb, lh, 1, a1, b1);
@@ -380,6 +382,24 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
     read_ops<TN, TM>(nxt, nxt + C::A_BYTES, rowa, rowb, lh, 0, a0, b0);
     mfma_all<TN, TM>(acc, a1, b1);
     sched();
+  }
+  if constexpr (kLoopOut) {
+    // the last stage without an adapter: once the loads of the stages past K (zeros, into the
+    // stage buffers) have landed and every wave has passed the barrier, no stage buffer is used
+    // any more, and each tile is written to the output copy under the next one's MFMA
+    const uint8_t* cur = smem + ((nk - 1) % NS) * C::STAGE;
+    read_ops<TN, TM>(cur, cur + C::A_BYTES, rowa, rowb, lh, 1, a1, b1);
+    mfma_all<TN, TM>(acc, a0, b0);
+    sched();
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TN * TM; ++k) {
+      const int i = k / TM, j = k % TM;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1[i], b1[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+      if (k > 0) tile_out(k - 1);
+    }
+    tile_out(TN * TM - 1);
   }
   }
 
@@ -419,8 +439,8 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   }
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
-  // (the hand-ordered loop without an adapter has written the output copy in its last stage)
-  constexpr bool kWritten = HS && !LORA;
+  // (the K loop has written the output copy in its last stage)
+  constexpr bool kWritten = kLoopOut;
 #pragma unroll
   for (int j = 0; j < (kWritten ? 0 : TM); ++j) {
     const int ml = wm * C::WM + j * 32 + lr;

@@ -215,6 +215,10 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // land at LDS [lds + 16 l, lds + 16 l + 16). Written as inline asm so that the
 // compiler does not serialize unrelated LDS reads behind it; the caller
 // waits for completion (wait_vmem) before the barrier that publishes the data.
+// The compiler inserts no wait states in front of inline asm: an SGPR operand
+// written by a VALU instruction (e.g. a spill reload by v_readlane) less than
+// five wait states before would be read stale. tests/test_asm_hazards.py checks
+// the kernels' assembly for that pattern.
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, int voff, int soff) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
 }

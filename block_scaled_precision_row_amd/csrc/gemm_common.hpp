@@ -47,7 +47,8 @@ __device__ __forceinline__ void dma_region(const v4i& rsrc, uint32_t lds_base, i
   }
 }
 
-// dword LDS DMA: lane l's 4 bytes land at M0 + 4 l
+// dword LDS DMA: lane l's 4 bytes land at M0 + 4 l (inline asm like dma16, with the same
+// caveat on VALU-written SGPR operands)
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, int voff, int soff) {
   asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
 }

@@ -187,11 +187,38 @@ void gemm_a16_kernel(DecArgs a) {
   read_x(smem, 0, x0);
   decode(r0, 0, 0, d0);
 
+  // the epilogue's scaling and bf16 conversion of accumulator tile t into the LDS copy of the
+  // output tile (see the epilogue below); without an adapter the last K stage does it
+  const float gw = FP4 ? a.gw[0] : 1.0f;
+  constexpr bool kLoopOut = !LORA;
+  auto tile_out = [&](int t) {
+    const int i = t / TM, j = t % TM;
+    const int ml = wm * C::WM + j * 32 + lr;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * C::WN + i * 32 + 8 * g + 4 * lh;
+      const v16f& A = acc[i][j];
+      float sv[4] = {gw, gw, gw, gw};
+      if (LORA) {
+        sv[0] = sv[1] = sv[2] = sv[3] = 1.0f;
+      } else if (!FP4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[e] = s_sw[nl + e];
+      }
+      *reinterpret_cast<uint2*>(smem + ml * C::TROW + nl * 2) =
+          make_uint2(pack_bf16x2(A[4 * g + 0] * sv[0], A[4 * g + 1] * sv[1]),
+                     pack_bf16x2(A[4 * g + 2] * sv[2], A[4 * g + 3] * sv[3]));
+    }
+  };
+
   // Stage s sits in buffer s % 2 and stage s + 1 in the other. Each K step's MFMAs run while
   // the next step's X chunks are read and its W fragments decoded. Once the last step's chunks
   // are read, every wave waits for stage s + 1, the barrier publishes it (and ends all reads
-  // of stage s), and stage s + 2 is fetched into buffer s % 2.
-  for (int s = 0; s < nk; ++s) {
+  // of stage s), and stage s + 2 is fetched into buffer s % 2. Without an adapter the last
+  // stage is peeled: after its barrier no stage buffer is read any more (and no load is in
+  // flight), so each tile is written to the output copy under the next tile's last MFMA.
+  auto stage = [&](int s, auto last) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last)::value;
     const uint8_t* cur = smem + (s & 1) * C::STAGE;
     const uint8_t* nxt = smem + ((s + 1) & 1) * C::STAGE;
     read_x(cur, 1, x1);
@@ -222,18 +249,33 @@ void gemm_a16_kernel(DecArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     __syncthreads();
-    issue_stage(s + 2);
-    read_sc(nxt);
-    read_w(nxt, 0, r0);
-    read_x(nxt, 0, x0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(d1, x1);
-    decode(r0, 0, 0, d0);
-  }
+    if constexpr (LAST) {
+#pragma unroll
+      for (int k = 0; k < TN * TM; ++k) {
+        const int i = k / TM, j = k % TM;
+        union { uint4 u; v8bf h; } p, q;
+        p.u = d1[i];
+        q.u = x1[j];
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p.h, q.h, acc[i][j], 0, 0, 0);
+        if (k > 0) tile_out(k - 1);
+      }
+      tile_out(TN * TM - 1);
+    } else {
+      issue_stage(s + 2);
+      read_sc(nxt);
+      read_w(nxt, 0, r0);
+      read_x(nxt, 0, x0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(d1, x1);
+      decode(r0, 0, 0, d0);
+    }
+  };
+  int s = 0;
+  for (; s + 1 < nk; ++s) stage(s, std::false_type{});
+  stage(s, std::integral_constant<bool, kLoopOut>{});
 
   // ---- epilogue: y = bf16(acc * gw) (W4A16) or bf16(acc * sw[n]) (W8A16), via an LDS copy of
   // the tile [BM][BN]
-  const float gw = FP4 ? a.gw[0] : 1.0f;
   if constexpr (LORA) {
     // with an adapter: y = bf16(acc * scale + T B^T), the adapter's MFMAs accumulating onto the
     // scaled accumulators
@@ -252,7 +294,7 @@ void gemm_a16_kernel(DecArgs a) {
   wait_vmcnt<0>();
   __syncthreads();  // all stage buffers are free now
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
+  for (int j = 0; j < (kLoopOut ? 0 : TM); ++j) {
     const int ml = wm * C::WM + j * 32 + lr;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {

@@ -539,6 +539,7 @@ def joint_block_sweep(L, syn, dev, reps=5):
 
     out = {"tokens": Mj, "gemms": []}
     block_us = {"nvfp4": 0.0, "fp8r": 0.0}
+    seq_us, grouped_us = {}, {}
     quant_us = {"nvfp4": 0.0, "fp8r": 0.0}
     for scheme, block in (("nvfp4", 0), ("fp8r", 1)):
         xq = {}
@@ -553,6 +554,8 @@ def joint_block_sweep(L, syn, dev, reps=5):
                 q, sq = L.bsq_quantize_act_fp8r(x)
                 xq[k] = (q, sq, None)
                 quant_us[scheme] += timed(lambda: check(lib.bsq_quantize_act_fp8r(P(x), Mj, k, k, P(q), P(sq), stream)))
+        calls, keep = [], []
+        probs = (L.GemmProblem * len(syn.JOINT_GEMMS))()
         for gi, (name, N, Kj) in enumerate(syn.JOINT_GEMMS):
             w = torch.from_numpy(syn.weights(syn.JOINT_4MP, N, Kj, block=block * 4 + gi).view("int16")) \
                 .to(dev).view(torch.bfloat16)
@@ -561,24 +564,48 @@ def joint_block_sweep(L, syn, dev, reps=5):
             if scheme == "nvfp4":
                 gw = L.bsq_calibrate_global_scale(w)
                 wq, ws = L.bsq_quantize_act_nvfp4(w, gw)
-                us = timed(lambda: check(lib.bsq_gemm_nvfp4_q(P(q), P(sq), P(gx), P(wq), P(ws), P(gw), P(y), N, Mj, N,
-                                                              Kj, stream)))
+                call = (lambda q=q, sq=sq, gx=gx, wq=wq, ws=ws, gw=gw, y=y, N=N, Kj=Kj:
+                        check(lib.bsq_gemm_nvfp4_q(P(q), P(sq), P(gx), P(wq), P(ws), P(gw), P(y), N, Mj, N, Kj,
+                                                   stream)))
+                probs[gi] = L.GemmProblem(P(q), P(sq), P(gx), P(wq), P(ws), P(gw), P(y), N, Mj, N, Kj)
+                keep += [wq, ws, gw, y]
                 peak = PEAK_F16_TFLOPS
             else:
                 wq, ws = L.bsq_quantize_act_fp8r(w)
-                us = timed(lambda: check(lib.bsq_gemm_fp8r_q(P(q), P(sq), P(wq), P(ws), P(y), N, Mj, N, Kj, stream)))
+                call = (lambda q=q, sq=sq, wq=wq, ws=ws, y=y, N=N, Kj=Kj:
+                        check(lib.bsq_gemm_fp8r_q(P(q), P(sq), P(wq), P(ws), P(y), N, Mj, N, Kj, stream)))
+                probs[gi] = L.GemmProblem(P(q), P(sq), None, P(wq), P(ws), None, P(y), N, Mj, N, Kj)
+                keep += [wq, ws, y]
                 peak = PEAK_FP8_TFLOPS
+            us = timed(call)
+            calls.append(call)
             tf = 2.0 * Mj * N * Kj / (us * 1e-6) / 1e12
             out["gemms"].append({"scheme": scheme, "gemm": name, "N": N, "K": Kj, "us": round(us, 1),
                                  "tflops": round(tf, 1), "frac_peak": round(tf / peak, 4)})
             block_us[scheme] += us
             log("joint block %s %s %dx%dx%d: %.1f us, %.0f TFLOP/s" % (scheme, name, Mj, N, Kj, us, tf))
-            del w, y
+            del w
+        # the whole block: its four launches back to back, against one grouped launch of all four
+        fmt = L.BSQ_FMT_NVFP4 if scheme == "nvfp4" else L.BSQ_FMT_FP8R
+        seq_us[scheme] = timed(lambda: [c() for c in calls])
+        grouped_us[scheme] = timed(lambda: check(lib.bsq_gemm_grouped_q(fmt, probs, len(calls), stream)))
+        log("joint block %s: four launches %.1f us, one grouped launch %.1f us"
+            % (scheme, seq_us[scheme], grouped_us[scheme]))
+        del calls, keep, probs
     out["block_us"] = {k: round(v, 1) for k, v in block_us.items()}
     out["activation_quant_us_per_block"] = {k: round(v, 1) for k, v in quant_us.items()}
     out["gemm_ms_28_blocks"] = round(14 * (block_us["nvfp4"] + block_us["fp8r"]) / 1e3, 2)
+    out["block_us_four_launches"] = {k: round(v, 1) for k, v in seq_us.items()}
+    out["block_us_grouped"] = {k: round(v, 1) for k, v in grouped_us.items()}
+    out["gemm_ms_28_blocks_grouped"] = round(14 * (grouped_us["nvfp4"] + grouped_us["fp8r"]) / 1e3, 2)
+    out["frac_of_ideal_28_blocks_grouped"] = round(
+        28 * 2.0 * Mj * sum(N * K for _, N, K in syn.JOINT_GEMMS) / 2 * (1 / PEAK_F16_TFLOPS + 1 / PEAK_FP8_TFLOPS)
+        / 1e9 / out["gemm_ms_28_blocks_grouped"], 4)
     out["note"] = ("peaks: f16 MFMA for nvfp4 (decoded operands), fp8 MFMA for fp8r; activations pre-quantized "
-                   "(their quantization time per block listed separately)")
+                   "(their quantization time per block listed separately); gemm_ms_28_blocks sums the GEMMs timed "
+                   "one by one, gemm_ms_28_blocks_grouped times each block's four GEMMs as one grouped launch "
+                   "(bsq_gemm_grouped_q); frac_of_ideal = the 28 blocks' flops at the f16 (nvfp4) and fp8 (fp8r) "
+                   "MFMA peaks over the grouped time")
     del xs
     torch.cuda.empty_cache()
     return out

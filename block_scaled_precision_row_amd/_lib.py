@@ -27,6 +27,15 @@ STATUS = {0: "BSQ_OK", 1: "BSQ_ERR_NULL", 2: "BSQ_ERR_SHAPE", 3: "BSQ_ERR_ALIGN"
 _p, _i64, _u32, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_int
 _f32 = ctypes.c_float
 
+BSQ_MAX_GROUP = 8
+
+
+class GemmProblem(ctypes.Structure):
+    """bsq_gemm_problem: one linear of a grouped launch (device pointers as integers)."""
+    _fields_ = [("xq", _p), ("x_scale", _p), ("input_scale", _p), ("w", _p), ("w_scale", _p), ("w_scale2", _p),
+                ("y", _p), ("ldy", _i64), ("M", _i64), ("N", _i64), ("K", _i64)]
+
+
 # symbol -> (restype, argtypes); mirrors include/bsq.h
 SIGNATURES = {
     "bsq_abi_version": (_int, []),
@@ -43,6 +52,7 @@ SIGNATURES = {
     "bsq_dequant_to_bf16": (_int, [_int, _p, _p, _p, _i64, _i64, _p, _p]),
     "bsq_gemm_fp8r_q": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "bsq_gemm_nvfp4_q": (_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
+    "bsq_gemm_grouped_q": (_int, [_int, ctypes.POINTER(GemmProblem), _int, _p]),
     "bsq_gemm_nvfp4_quantize_y_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "bsq_gemm_nvfp4_q_quantize_y": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
                                            _p]),
@@ -323,6 +333,47 @@ def bsq_gemm_nvfp4_q(xq, x_bscale, input_scale, w, w_bscale, w_scale2, y=None):
                                                     _ptr(w_bscale), _ptr(w_scale2), _ptr(y), ldy, M, N, K,
                                                     _stream()))
     return y
+
+
+def bsq_gemm_grouped_q(fmt, problems, ys=None):
+    """Several pre-quantized linears of one scheme in one launch (bsq_gemm_grouped_q).
+    fmt BSQ_FMT_FP8R: each problem is (xq [M, K], x_scale [M], w [N, K], w_scale [N]);
+    fmt BSQ_FMT_NVFP4: (xq [M, K/2], x_bscale [M, K/16], input_scale [1], w [N, K/2], w_bscale [N, K/16],
+    w_scale2 [1]). Returns the bf16 outputs [M, N], each bit for bit what bsq_gemm_fp8r_q /
+    bsq_gemm_nvfp4_q returns for that problem."""
+    if fmt not in (BSQ_FMT_FP8R, BSQ_FMT_NVFP4):
+        raise ValueError("fmt must be BSQ_FMT_FP8R or BSQ_FMT_NVFP4")
+    if len(problems) > BSQ_MAX_GROUP:
+        raise ValueError("at most %d problems per group" % BSQ_MAX_GROUP)
+    arr = (GemmProblem * max(len(problems), 1))()
+    out = []
+    for i, p in enumerate(problems):
+        if fmt == BSQ_FMT_FP8R:
+            xq, xs, w, ws = p
+            M, K = xq.shape
+            N = w.shape[0]
+            _dense(xq, torch.uint8, (M, K), "xq")
+            _dense(xs, torch.float32, (M,), "x_scale")
+            _dense(w, torch.uint8, (N, K), "w")
+            _dense(ws, torch.float32, (N,), "w_scale")
+            gx = gw = None
+        else:
+            xq, xs, gx, w, ws, gw = p
+            M, K = xq.shape[0], xq.shape[1] * 2
+            N = w.shape[0]
+            _dense(xq, torch.uint8, (M, K // 2), "xq")
+            _dense(xs, torch.uint8, (M, K // 16), "x_bscale")
+            _scalar(gx, "input_scale")
+            _dense(w, torch.uint8, (N, K // 2), "w")
+            _dense(ws, torch.uint8, (N, K // 16), "w_bscale")
+            _scalar(gw, "w_scale2")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if ys is None else ys[i]
+        _, _, ldy = _rows(y, torch.bfloat16, "y")
+        arr[i] = GemmProblem(xq.data_ptr(), xs.data_ptr(), None if gx is None else gx.data_ptr(), w.data_ptr(),
+                             ws.data_ptr(), None if gw is None else gw.data_ptr(), y.data_ptr(), ldy, M, N, K)
+        out.append(y)
+    _check("bsq_gemm_grouped_q", lib.bsq_gemm_grouped_q(fmt, arr, len(problems), _stream()))
+    return out
 
 
 def bsq_gemm_nvfp4_q_quantize_y(xq, x_bscale, input_scale, w, w_bscale, w_scale2, y_scale, with_y=False,

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <utility>
 
 #include "bsq_launch.hpp"
 
@@ -307,13 +308,34 @@ bsq_status bsq_gemm_nvfp4(const uint16_t* x, int64_t ldx, const uint8_t* w, cons
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 
-bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
-                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+namespace {
+// argument checks of the pre-quantized W8A8 and W4A4 linears (also per problem of a grouped
+// launch); empty shapes pass without looking at any pointer
+bsq_status check_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
+                        uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K) {
   // xq rows are dense (ld = K); reuse the common checks with ldx = K
   bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w, y, ldy, M, N, K, 0);
   if (st != BSQ_OK || M == 0 || N == 0) return st;
   if (!x_scale || !w_scale) return BSQ_ERR_NULL;
   if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return BSQ_ERR_ALIGN;
+  return BSQ_OK;
+}
+bsq_status check_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale, const uint8_t* w,
+                         const uint8_t* w_bscale, const float* w_scale2, uint16_t* y, int64_t ldy, int64_t M,
+                         int64_t N, int64_t K) {
+  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w, y, ldy, M, N, K, 0);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
+  if (!x_bscale || !input_scale || !w_bscale || !w_scale2) return BSQ_ERR_NULL;
+  if (!aligned(x_bscale, 4) || !aligned(input_scale, 4) || !aligned(w_bscale, 4) || !aligned(w_scale2, 4))
+    return BSQ_ERR_ALIGN;
+  return BSQ_OK;
+}
+}  // namespace
+
+bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_t* w, const float* w_scale,
+                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  bsq_status st = check_fp8r_q(xq, x_scale, w, w_scale, y, ldy, M, N, K);
+  if (st != BSQ_OK || M == 0 || N == 0) return st;
   if ((st = check_device()) != BSQ_OK) return st;
   hipError_t e = launch_w8a8(xq, x_scale, w, w_scale, y, ldy, M, N, K, stream);
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
@@ -322,16 +344,81 @@ bsq_status bsq_gemm_fp8r_q(const uint8_t* xq, const float* x_scale, const uint8_
 bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const float* input_scale,
                             const uint8_t* w, const uint8_t* w_bscale, const float* w_scale2, uint16_t* y,
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  bsq_status st = check_gemm_common(reinterpret_cast<const uint16_t*>(xq), K, w, y, ldy, M, N, K, 0);
+  bsq_status st = check_nvfp4_q(xq, x_bscale, input_scale, w, w_bscale, w_scale2, y, ldy, M, N, K);
   if (st != BSQ_OK || M == 0 || N == 0) return st;
-  if (!x_bscale || !input_scale || !w_bscale || !w_scale2) return BSQ_ERR_NULL;
-  if (!aligned(x_bscale, 4) || !aligned(input_scale, 4) || !aligned(w_bscale, 4) || !aligned(w_scale2, 4))
-    return BSQ_ERR_ALIGN;
   if ((st = check_device()) != BSQ_OK) return st;
   bsq::DecArgs a{};
   a.xq = xq; a.xs = x_bscale; a.gx = input_scale; a.w = w; a.ws = w_bscale; a.gw = w_scale2;
   a.y = y; a.ldy = ldy; a.M = M; a.N = N; a.K = K;
   hipError_t e = launch_dec_or_skinny(bsq::kW4A4, a, stream);
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
+static_assert(BSQ_MAX_GROUP == bsq::kMaxGroup, "the header states the group limit");
+
+bsq_status bsq_gemm_grouped_q(bsq_format format, const bsq_gemm_problem* problems, int count, hipStream_t stream) {
+  if (format != BSQ_FMT_FP8R && format != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;
+  if (count < 0 || count > BSQ_MAX_GROUP) return BSQ_ERR_ARG;
+  if (count == 0) return BSQ_OK;
+  if (!problems) return BSQ_ERR_NULL;
+  const bool fp8 = format == BSQ_FMT_FP8R;
+  // every problem is checked before anything is enqueued; empty ones are dropped
+  int order[BSQ_MAX_GROUP], n = 0;
+  for (int i = 0; i < count; ++i) {
+    const bsq_gemm_problem& p = problems[i];
+    bsq_status st;
+    if (fp8) {
+      if (p.input_scale || p.w_scale2) return BSQ_ERR_ARG;
+      st = check_fp8r_q(p.xq, static_cast<const float*>(p.x_scale), p.w, static_cast<const float*>(p.w_scale), p.y,
+                        p.ldy, p.M, p.N, p.K);
+    } else {
+      st = check_nvfp4_q(p.xq, static_cast<const uint8_t*>(p.x_scale), p.input_scale, p.w,
+                         static_cast<const uint8_t*>(p.w_scale), p.w_scale2, p.y, p.ldy, p.M, p.N, p.K);
+    }
+    if (st != BSQ_OK) return st;
+    if (p.M > 0 && p.N > 0) order[n++] = i;
+  }
+  if (n == 0) return BSQ_OK;
+  bsq_status st = check_device();
+  if (st != BSQ_OK) return st;
+  // longest K first (stable), so the grid's last round holds the shortest tiles
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && problems[order[j]].K > problems[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
+  hipError_t e = hipSuccess;
+  if (fp8) {
+    bsq::Fp8Problem q[BSQ_MAX_GROUP];
+    for (int i = 0; i < n; ++i) {
+      const bsq_gemm_problem& p = problems[order[i]];
+      q[i] = bsq::Fp8Problem{p.xq, static_cast<const float*>(p.x_scale), p.w, static_cast<const float*>(p.w_scale),
+                             p.y, p.ldy, (int)p.M, (int)p.N, (int)p.K, 0};
+    }
+    if (bsq::gemm_fp8_grouped_supported(q, n)) {
+      e = bsq::launch_gemm_fp8_grouped(q, n, stream);
+    } else {
+      for (int i = 0; i < count && e == hipSuccess; ++i) {
+        const bsq_gemm_problem& p = problems[i];
+        if (p.M > 0 && p.N > 0)
+          e = launch_w8a8(p.xq, static_cast<const float*>(p.x_scale), p.w, static_cast<const float*>(p.w_scale), p.y,
+                          p.ldy, p.M, p.N, p.K, stream);
+      }
+    }
+  } else {
+    bsq::DecArgs q[BSQ_MAX_GROUP];
+    auto args = [](const bsq_gemm_problem& p) {
+      bsq::DecArgs a{};
+      a.xq = p.xq; a.xs = static_cast<const uint8_t*>(p.x_scale); a.gx = p.input_scale; a.w = p.w;
+      a.ws = static_cast<const uint8_t*>(p.w_scale); a.gw = p.w_scale2; a.y = p.y; a.ldy = p.ldy;
+      a.M = p.M; a.N = p.N; a.K = p.K;
+      return a;
+    };
+    for (int i = 0; i < n; ++i) q[i] = args(problems[order[i]]);
+    if (bsq::gemm_w4a4_grouped_supported(q, n)) {
+      e = bsq::launch_gemm_w4a4_grouped(q, n, stream);
+    } else {
+      for (int i = 0; i < count && e == hipSuccess; ++i)
+        if (problems[i].M > 0 && problems[i].N > 0) e = launch_dec_or_skinny(bsq::kW4A4, args(problems[i]), stream);
+    }
+  }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }
 

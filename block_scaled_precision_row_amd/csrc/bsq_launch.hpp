@@ -144,6 +144,25 @@ hipError_t launch_gemm_a16(DecMode mode, const DecArgs& a, hipStream_t s);
 // W4A4 on the LDS-DMA pipeline with in-register decode; needs K % 256 == 0
 bool gemm_w4a4_supported(const DecArgs& a);
 hipError_t launch_gemm_w4a4(const DecArgs& a, hipStream_t s);
+// Grouped launches: the tiles of up to kMaxGroup independent GEMMs of one scheme in one grid
+// (every problem with K % 256 == 0 for W4A4, K % 128 == 0 for fp8r). Problems are taken in the
+// order given; callers put the longest K first so that the last round holds the short tiles.
+constexpr int kMaxGroup = 8;
+struct Fp8Problem {
+  const uint8_t* xq;  // E4M3 activations [M][K]
+  const float* sx;    // per-row activation scales [M]
+  const uint8_t* w;   // E4M3 weights [N][K]
+  const float* sw;    // per-row weight scales [N]
+  uint16_t* y;        // bf16 output [M][ldy]
+  int64_t ldy;
+  int M, N, K;
+  int stream_y;       // set by the launcher
+};
+bool gemm_fp8_grouped_supported(const Fp8Problem* p, int count);
+hipError_t launch_gemm_fp8_grouped(const Fp8Problem* p, int count, hipStream_t s);
+bool gemm_w4a4_grouped_supported(const DecArgs* p, int count);
+hipError_t launch_gemm_w4a4_grouped(const DecArgs* p, int count, hipStream_t s);
+
 // Few-token GEMMs: 32 weight rows per workgroup, K split over its 8 waves
 bool gemm_skinny_supported(DecMode mode, const DecArgs& a);
 hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s);

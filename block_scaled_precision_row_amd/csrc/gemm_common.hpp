@@ -270,12 +270,26 @@ __device__ __forceinline__ void lora_update(v16f (&acc)[TN][TM], const uint16_t*
 }
 
 // tile index of this workgroup (XCD-contiguous, grouped along M)
-__device__ __forceinline__ void tile_of_block(int M, int N, int BM, int BN, int& m0, int& n0) {
+// tile of workgroup `bid` of a grid of BM x BN tiles over M x N (bid < the tile count)
+__device__ __forceinline__ void tile_of_id(int bid, int M, int N, int BM, int BN, int& m0, int& n0) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  grouped_tile(xcd_contiguous_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
+  grouped_tile(xcd_contiguous_id(bid, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
   m0 = tm * BM;
   n0 = tn * BN;
+}
+__device__ __forceinline__ void tile_of_block(int M, int N, int BM, int BN, int& m0, int& n0) {
+  tile_of_id(blockIdx.x, M, N, BM, BN, m0, n0);
+}
+
+// A grouped launch runs the tiles of several independent GEMMs in one grid: problem p owns
+// workgroups [start[p], start[p + 1]). Returns the problem of workgroup `bid` (uniform).
+template <int S>
+__device__ __forceinline__ int group_problem(const int (&start)[S], int count, int bid) {
+  int p = 0;
+#pragma unroll
+  for (int i = 1; i < S - 1; ++i) p += (i < count && bid >= start[i]) ? 1 : 0;
+  return p;
 }
 
 }  // namespace gemm

@@ -23,6 +23,8 @@
 // and Xq, so every product pairs equal K indices.
 // The epilogue scales the accumulators, converts them to bf16 into an LDS
 // copy of the output tile, and writes the tile back in 16-byte row chunks.
+#include <cmath>
+
 #include "gemm_common.hpp"
 #include "bsq_launch.hpp"
 
@@ -162,12 +164,13 @@ constexpr bool hand_ordered() { return NS == 2; }
 // row maxima of the fp8r encoding (YQuant). HS: the hand-ordered K loop (K % 128 == 0). LL:
 // where the adapter's T and B rows are read (LoraLds). WPE: waves per SIMD the registers are
 // budgeted for (2: two workgroups share a compute unit).
-template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, int LL = kLoraGlobal, int WPE = 1>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
-                     const uint8_t* __restrict__ w, const float* __restrict__ sw,
-                     uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, const uint16_t* lt,
-                     const uint16_t* lb, int rank, int stream_y, YQuant q) {
+// One output tile: workgroup `bid` of the grid of BM x BN tiles over M x N.
+template <int BM, int BN, int NS, bool LORA, int OQ, bool HS, int LL>
+__device__ __forceinline__ void fp8_tile(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
+                                         const uint8_t* __restrict__ w, const float* __restrict__ sw,
+                                         uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K,
+                                         const uint16_t* lt, const uint16_t* lb, int rank, int stream_y,
+                                         const YQuant& q, int bid) {
   using C = Cfg<BM, BN, NS>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -176,7 +179,7 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   __shared__ __attribute__((aligned(16))) uint8_t s_lora[LL == kLoraAhead ? (BM + BN) * kLoraLdsRow : 16];
 
   int m0, n0;
-  tile_of_block(M, N, BM, BN, m0, n0);
+  tile_of_id(bid, M, N, BM, BN, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -466,6 +469,33 @@ void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ s
   if constexpr (OQ == 2) rowmax_tile<BM, BN, C::TROW>(smem, q.pmax, M, N, m0, n0, tid);
 }
 
+template <int BM, int BN, int NS, bool LORA, int OQ = 0, bool HS = false, int LL = kLoraGlobal, int WPE = 1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void gemm_fp8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
+                     const uint8_t* __restrict__ w, const float* __restrict__ sw,
+                     uint16_t* __restrict__ y, int64_t ldy, int M, int N, int K, const uint16_t* lt,
+                     const uint16_t* lb, int rank, int stream_y, YQuant q) {
+  fp8_tile<BM, BN, NS, LORA, OQ, HS, LL>(xq, sx, w, sw, y, ldy, M, N, K, lt, lb, rank, stream_y, q, blockIdx.x);
+}
+
+// The tiles of several W8A8 GEMMs in one grid (hand-ordered loop, two stage buffers): the
+// problem of each workgroup, then that problem's tile, exactly as its own launch would compute
+// it (same tile shape, same bits).
+struct Fp8Group {
+  Fp8Problem p[kMaxGroup];
+  int start[kMaxGroup + 1];
+  int count;
+};
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_fp8_grouped_kernel(Fp8Group g) {
+  const int bid = blockIdx.x;
+  const int p = group_problem(g.start, g.count, bid);
+  const Fp8Problem& q = g.p[p];
+  fp8_tile<BM, BN, 2, false, 0, true, kLoraGlobal>(q.xq, q.sx, q.w, q.sw, q.y, q.ldy, q.M, q.N, q.K, nullptr,
+                                                   nullptr, 0, q.stream_y, YQuant{}, bid - g.start[p]);
+}
+
 template <int BM, int BN, int NS, bool HS, int WPE = 1>
 hipError_t launch_oq(int oq, int tiles, const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                      uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int st, const YQuant& qv,
@@ -535,6 +565,47 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
 }
 
 }  // namespace
+
+// Grouped W8A8: every problem on the hand-ordered loop (K % 128 == 0) and at least one full
+// round of 256 x 192 tiles in all; smaller groups gain nothing over one launch per problem,
+// whose small-grid tiles reach the idle compute units.
+bool gemm_fp8_grouped_supported(const Fp8Problem* p, int count) {
+  if (count < 2 || count > kMaxGroup) return false;
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    if (p[i].K % kStageK != 0) return false;
+    tiles += ((int64_t)(p[i].M + 255) / 256) * ((p[i].N + 191) / 192);
+  }
+  return tiles >= 256;
+}
+
+// One grid over every problem's tiles, the tile shape chosen for the whole group as for one
+// GEMM (whole rounds of 256 x 256 or 256 x 192 tiles, each tile's time in proportion to its K).
+hipError_t launch_gemm_fp8_grouped(const Fp8Problem* p, int count, hipStream_t s) {
+  auto cost = [&](int BM, int BN, int per_tile) {
+    double work = 0;  // tiles times K / 3072
+    for (int i = 0; i < count; ++i)
+      work += (double)(((int64_t)(p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN)) * p[i].K / 3072.0;
+    return std::ceil(work / 256.0 - 1e-9) * per_tile;
+  };
+  const bool square = cost(256, 256, 92) <= cost(256, 192, 72);
+  const int BM = 256, BN = square ? 256 : 192;
+  Fp8Group g{};
+  g.count = count;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    g.p[i] = p[i];
+    g.p[i].stream_y = (int)stream_output((int64_t)(p[i].M + p[i].N) * p[i].K, p[i].M, p[i].N);
+    g.start[i] = (int)total;
+    total += ((int64_t)(p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN);
+  }
+  for (int i = count; i <= kMaxGroup; ++i) g.start[i] = (int)total;
+  if (square)
+    hipLaunchKernelGGL((gemm_fp8_grouped_kernel<256, 256>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_fp8_grouped_kernel<256, 192>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,
                            uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, const uint16_t* lt,

@@ -29,6 +29,8 @@
 // [128 h + 32 q, 128 h + 32 q + 32), one 8-value group per K step -- for both
 // operands alike, so every product pairs equal K indices. A lane's 8 block
 // scales of a stage are then 8 consecutive bytes, read once per stage.
+#include <cmath>
+
 #include "gemm_common.hpp"
 #include "bsq_launch.hpp"
 
@@ -92,9 +94,9 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q) {
   return T == 0 ? q.x : T == 1 ? q.y : T == 2 ? q.z : q.w;
 }
 
-template <int BM, int BN, bool LORA, int WPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void gemm_w4a4_kernel(DecArgs a) {
+// One output tile: workgroup `bid` of the grid of BM x BN tiles over M x N.
+template <int BM, int BN, bool LORA>
+__device__ __forceinline__ void w4a4_tile(const DecArgs& a, int bid) {
   using C = W4Cfg<BM, BN>;
   constexpr int TN = C::TN, TM = C::TM;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -102,7 +104,7 @@ void gemm_w4a4_kernel(DecArgs a) {
 
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   int m0, n0;
-  tile_of_block(M, N, BM, BN, m0, n0);
+  tile_of_id(bid, M, N, BM, BN, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -323,6 +325,27 @@ void gemm_w4a4_kernel(DecArgs a) {
   if (a.ypmax) rowmax_tile<BM, BN, C::TROW>(smem, a.ypmax, M, N, m0, n0, tid);
 }
 
+template <int BM, int BN, bool LORA, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void gemm_w4a4_kernel(DecArgs a) {
+  w4a4_tile<BM, BN, LORA>(a, blockIdx.x);
+}
+
+// The tiles of several W4A4 GEMMs in one grid: the problem of each workgroup, then that
+// problem's tile, exactly as its own launch would compute it (same tile shape, same bits).
+struct W4Group {
+  DecArgs p[kMaxGroup];
+  int start[kMaxGroup + 1];
+  int count;
+};
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_w4a4_grouped_kernel(W4Group g) {
+  const int bid = blockIdx.x;
+  const int p = group_problem(g.start, g.count, bid);
+  w4a4_tile<BM, BN, false>(g.p[p], bid - g.start[p]);
+}
+
 // WPE: waves per SIMD the registers are budgeted for. The 128 x 128 tile takes 72 KB of LDS, so
 // two of its workgroups share a compute unit when each wave keeps to 256 registers; the decode
 // VALU of one then overlaps the other's MFMAs.
@@ -340,6 +363,47 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
 }  // namespace
 
 bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kStageK == 0; }
+
+// Grouped W4A4: every problem with K % 256 == 0, plain bf16 output (no adapter, no quantized
+// output), and at least one full round of 256 x 192 tiles in all; smaller groups gain nothing
+// over one launch per problem, whose small-grid tiles reach the idle compute units.
+bool gemm_w4a4_grouped_supported(const DecArgs* p, int count) {
+  if (count < 2 || count > kMaxGroup) return false;
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    if (p[i].K % kStageK != 0 || p[i].lt || p[i].yq || p[i].ypmax || !p[i].y) return false;
+    tiles += ((p[i].M + 255) / 256) * ((p[i].N + 191) / 192);
+  }
+  return tiles >= 256;
+}
+
+// One grid over every problem's tiles, the tile shape chosen for the whole group as for one
+// GEMM (whole rounds of 256 x 256 or 256 x 192 tiles, each tile's time in proportion to its K).
+hipError_t launch_gemm_w4a4_grouped(const DecArgs* p, int count, hipStream_t s) {
+  auto cost = [&](int BM, int BN, int per_tile) {
+    double work = 0;  // tiles times K / 3072
+    for (int i = 0; i < count; ++i)
+      work += (double)(((p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN)) * (double)p[i].K / 3072.0;
+    return std::ceil(work / 256.0 - 1e-9) * per_tile;
+  };
+  const bool square = cost(256, 256, 76) <= cost(256, 192, 60);
+  const int BM = 256, BN = square ? 256 : 192;
+  W4Group g{};
+  g.count = count;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    g.p[i] = p[i];
+    g.p[i].stream_y = stream_output((p[i].M + p[i].N) * (p[i].K / 2 + p[i].K / 16), p[i].M, p[i].N);
+    g.start[i] = (int)total;
+    total += ((p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN);
+  }
+  for (int i = count; i <= kMaxGroup; ++i) g.start[i] = (int)total;
+  if (square)
+    hipLaunchKernelGGL((gemm_w4a4_grouped_kernel<256, 256>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_w4a4_grouped_kernel<256, 192>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
 bool lora_pre_scaled_w4a4(const DecArgs& a) { return gemm_w4a4_supported(a); }
 
 hipError_t launch_gemm_w4a4(const DecArgs& args, hipStream_t s) {

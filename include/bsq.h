@@ -193,6 +193,49 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * Grouped launch: several independent pre-quantized linears of one scheme in
+ * one kernel launch (the four linears of a joint transformer block -- qkv,
+ * proj, MLP up and down -- whose 28 blocks the FLUX 3 Image Klein release
+ * page, section one, describes; each linear's arithmetic is that of the
+ * "BFL (fp8r / nvfp4)" scheme list and "Kernels" table, as above). Problem i's
+ * y is, bit for bit, what bsq_gemm_fp8r_q (format BSQ_FMT_FP8R) or
+ * bsq_gemm_nvfp4_q (BSQ_FMT_NVFP4) returns for its operands: one grid holds
+ * every problem's output tiles, longest K first, so one problem's last round
+ * of tiles overlaps the next problem's first instead of leaving compute
+ * units idle between launches. Groups the grouped kernels do not cover (fp8r
+ * with K % 128 != 0, nvfp4 with K % 256 != 0, or fewer output tiles in all
+ * than one round of 256 x 192 tiles on the 256 compute units) run as one
+ * launch per problem, in the order given, with the same results.
+ *   problems : host array of `count` descriptors (read during the call only);
+ *              count 0 is a no-op, 1 <= count <= BSQ_MAX_GROUP otherwise
+ *   per problem, with the layouts and alignment of the two entry points:
+ *     xq       fp8r [M][K] E4M3 | nvfp4 [M][K/2] packed E2M1
+ *     x_scale  fp8r fp32 [M] row scales | nvfp4 E4M3 [M][K/16] block scales
+ *     input_scale  nvfp4 [1] fp32 | fp8r NULL
+ *     w        fp8r [N][K] E4M3 | nvfp4 [N][K/2]
+ *     w_scale  fp8r fp32 [N] | nvfp4 E4M3 [N][K/16]
+ *     w_scale2 nvfp4 [1] fp32 | fp8r NULL
+ *     y [M][ldy] bf16; problems with M == 0 or N == 0 are skipped.
+ * No output may alias another problem's output or any input. Errors:
+ * BSQ_ERR_ARG for an unknown format, count < 0 or count > BSQ_MAX_GROUP, or a
+ * non-NULL input_scale / w_scale2 with fp8r; otherwise the statuses of the
+ * two entry points. Every problem is validated before anything is enqueued.
+ */
+#define BSQ_MAX_GROUP 8
+typedef struct {
+  const uint8_t* xq;
+  const void* x_scale;
+  const float* input_scale;
+  const uint8_t* w;
+  const void* w_scale;
+  const float* w_scale2;
+  uint16_t* y;
+  int64_t ldy;
+  int64_t M, N, K;
+} bsq_gemm_problem;
+bsq_status bsq_gemm_grouped_q(bsq_format format, const bsq_gemm_problem* problems, int count, hipStream_t stream);
+
+/*
  * W4A4 linear whose output is also handed to the next quantized linear in
  * nvfp4 ("BFL (fp8r / nvfp4)": every quantized linear quantizes its input at
  * run time; here the producing GEMM does it in its epilogue, where the

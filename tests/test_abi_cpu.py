@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 25
+    assert len(syms) == 26
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
@@ -58,6 +58,48 @@ def test_weight_only_quantized_output_validation():
     assert g(fp8, A, 64, B, C, None, fp8, None, ODD, B, None, 0, 64, 64, 64, A, ws, None) == ALIGN  # yq
     assert g(fp8, A, 64, B, C, None, fp8, None, A, B, None, 0, 64, 64, 64, A, ws - 1, None) == WS
     assert g(fp8, None, 64, None, None, None, fp8, None, None, None, None, 0, 0, 64, 64, None, 0, None) == OK  # empty
+
+
+def test_grouped_validation():
+    fp8, nv = _lib.BSQ_FMT_FP8R, _lib.BSQ_FMT_NVFP4
+    g = L.bsq_gemm_grouped_q
+    GP = _lib.GemmProblem
+
+    def probs(*ps):
+        arr = (GP * len(ps))()
+        for i, p in enumerate(ps):
+            arr[i] = p
+        return arr
+
+    f8 = GP(A.value, B.value, None, C.value, D.value, None, A.value, 64, 64, 64, 128)  # xq, sx, w, sw, y
+    n4 = GP(A.value, B.value, C.value, C.value, D.value, D.value, A.value, 64, 64, 64, 256)
+    assert g(3, probs(f8), 1, None) == ARG                       # format
+    assert g(fp8, probs(f8), -1, None) == ARG                    # count
+    assert g(fp8, probs(*[f8] * 9), 9, None) == ARG              # more than BSQ_MAX_GROUP
+    assert g(fp8, None, 0, None) == OK                           # nothing to do
+    assert g(fp8, None, 2, None) == NULL                         # no descriptors
+    bad = GP(A.value, B.value, C.value, C.value, D.value, None, A.value, 64, 64, 64, 128)
+    assert g(fp8, probs(f8, bad), 2, None) == ARG                # fp8r takes no input_scale
+    assert g(nv, probs(n4, GP(A.value, B.value, None, C.value, D.value, D.value, A.value, 64, 64, 64, 256)),
+             2, None) == NULL                                    # nvfp4 needs input_scale
+    assert g(fp8, probs(f8, GP(A.value, B.value, None, C.value, D.value, None, A.value, 64, 64, 64, 100)),
+             2, None) == SHAPE                                   # K % 32
+    assert g(fp8, probs(f8, GP(A.value, None, None, C.value, D.value, None, A.value, 64, 64, 64, 128)),
+             2, None) == NULL                                    # x_scale
+    assert g(nv, probs(n4, GP(ODD.value, B.value, C.value, C.value, D.value, D.value, A.value, 64, 64, 64, 256)),
+             2, None) == ALIGN                                   # xq
+    assert g(fp8, probs(f8, GP(A.value, B.value, None, C.value, D.value, None, A.value, 32, 64, 64, 128)),
+             2, None) == SHAPE                                   # ldy < N
+    # empty problems are skipped without looking at their pointers; all empty is a no-op
+    empty = GP(None, None, None, None, None, None, None, 64, 0, 64, 128)  # M = 0
+    assert g(fp8, probs(empty, empty), 2, None) == OK
+    # a bad problem after a valid one still fails before anything is enqueued (no device here)
+    assert g(fp8, probs(f8, GP(A.value, B.value, None, C.value, D.value, None, A.value, 64, 64, 64, 0)),
+             2, None) == SHAPE
+    if not torch.cuda.is_available():
+        assert g(fp8, probs(f8, f8), 2, None) == DEV
+    with pytest.raises(ValueError):
+        _lib.bsq_gemm_grouped_q(fp8, [None] * 9)
 
 
 def test_workspace_sizes():

@@ -1,0 +1,140 @@
+"""GPU parity of the grouped launch (bsq_gemm_grouped_q).
+
+Every problem of a group must come out bit for bit as the single pre-quantized
+entry point (bsq_gemm_fp8r_q / bsq_gemm_nvfp4_q) computes it -- the grouped
+kernels run the same tile code, only the workgroup -> (problem, tile) mapping
+differs -- and sampled rows must match the oracle's fp64 product within the
+GEMM tolerance. Groups cover the grouped kernels (ragged M and N, mixed K,
+longest K not first), the per-problem fallback (too few tiles, a K the grouped
+kernels do not take, empty problems) and the four joint-block linears at
+16384 tokens ("FLUX 3 Image Klein" release page, section one: 28 joint blocks
+of qkv, proj, MLP up and down).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_row_amd import synthetic as syn
+from oracle import gemm, quant
+from tests.gpu_util import assert_gemm_close, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from block_scaled_precision_row_amd import _lib as L
+
+
+def _acts(fmt, M, K, block):
+    """Seeded activations, quantized on the GPU (bit-exact with the oracle's quantizers)."""
+    xb = syn.activations(syn.JOINT_4MP, M, K, block=block)
+    x = dev_bf16(xb)
+    if fmt == "fp8r":
+        return xb, L.bsq_quantize_act_fp8r(x)
+    gx = L.bsq_calibrate_global_scale(x)
+    xq, xs = L.bsq_quantize_act_nvfp4(x, gx)
+    return xb, (xq, xs, gx)
+
+
+def _weights(fmt, N, K, block):
+    wb = syn.weights(syn.JOINT_4MP, N, K, block=block)
+    w = dev_bf16(wb)
+    if fmt == "fp8r":
+        return L.bsq_quantize_act_fp8r(w)
+    gw = L.bsq_calibrate_global_scale(w)
+    wq, ws = L.bsq_quantize_act_nvfp4(w, gw)
+    return wq, ws, gw
+
+
+def _problem(fmt, xs, ws):
+    if fmt == "fp8r":
+        return (xs[0], xs[1], ws[0], ws[1])
+    return (xs[0], xs[1], xs[2], ws[0], ws[1], ws[2])
+
+
+def _single(fmt, p):
+    return L.bsq_gemm_fp8r_q(*p) if fmt == "fp8r" else L.bsq_gemm_nvfp4_q(*p)
+
+
+def _fmt(fmt):
+    return L.BSQ_FMT_FP8R if fmt == "fp8r" else L.BSQ_FMT_NVFP4
+
+
+def _oracle_rows(fmt, p, xb, rows):
+    """The oracle's product on `rows`, from the weights' codes and scales as the GPU holds them;
+    the GPU's encoding of these activation rows must equal the oracle quantizer's."""
+    r = torch.as_tensor(rows, device="cuda")
+    if fmt == "fp8r":
+        xq, sx = host(p[0][r]), host(p[1][r])
+        wq, sw = host(p[2]), host(p[3])
+        oq, osx = quant.quantize_fp8r(xb[rows])
+        assert np.array_equal(oq, xq) and np.array_equal(osx, sx)
+        return gemm.gemm_fp8r(xq, sx, wq, sw)
+    xq, xs, gx = host(p[0][r]), host(p[1][r]), host(p[2])
+    wq, ws, gw = host(p[3]), host(p[4]), host(p[5])
+    oq, os_ = quant.quantize_nvfp4(xb[rows], np.float32(gx[0]))
+    assert np.array_equal(oq, xq) and np.array_equal(os_, xs)
+    return gemm.gemm_nvfp4(xq, xs, np.float32(gx[0]), wq, ws, np.float32(gw[0]))
+
+
+def _check_group(fmt, probs, xbs, sample=12, seed=0):
+    ys = L.bsq_gemm_grouped_q(_fmt(fmt), probs)
+    singles = [_single(fmt, p) for p in probs]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    for i, (y, s) in enumerate(zip(ys, singles)):
+        yb, sb = host(y), host(s)
+        assert np.array_equal(yb, sb), "problem %d differs from its single launch" % i
+        if sample:
+            M = yb.shape[0]
+            rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, sample, replace=False)]))
+            assert_gemm_close(yb[rows], _oracle_rows(fmt, probs[i], xbs[i], rows), "%s grouped problem %d" % (fmt, i))
+    return ys
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+def test_grouped_kernel_mixed_shapes(fmt):
+    """296 tiles of 256 x 192 in all (the grouped kernel), ragged M and N, the longest K last."""
+    M = 2000
+    xb1, x1 = _acts(fmt, M, 1024, 0)
+    xb2, x2 = _acts(fmt, M, 2048, 1)
+    shapes = [(2304, 1024), (776, 1024), (3072, 1024), (760, 2048)]
+    probs, xbs = [], []
+    for b, (N, K) in enumerate(shapes):
+        probs.append(_problem(fmt, x1 if K == 1024 else x2, _weights(fmt, N, K, 10 + b)))
+        xbs.append(xb1 if K == 1024 else xb2)
+    _check_group(fmt, probs, xbs)
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+def test_grouped_fallback_paths(fmt):
+    """Groups the grouped kernels do not take run one launch per problem, with the same bits:
+    too few tiles, a K that is not a whole number of the grouped kernels' stages, empty problems."""
+    xb, x = _acts(fmt, 300, 512, 2)
+    small = [_problem(fmt, x, _weights(fmt, N, 512, 20 + i)) for i, N in enumerate((520, 264))]
+    _check_group(fmt, small, [xb, xb])
+    xb2, x2 = _acts(fmt, 2000, 1088, 3)  # K % 128 == 64: neither grouped kernel's stage
+    odd = [_problem(fmt, x2, _weights(fmt, N, 1088, 30 + i)) for i, N in enumerate((3072, 3000))]
+    _check_group(fmt, odd, [xb2, xb2], sample=6)
+    # an empty problem (M = 0) among full ones is skipped
+    xb3, x3 = _acts(fmt, 2000, 1024, 5)
+    e = tuple(t[:0] if t.dim() == 2 or t.numel() > 1 else t for t in x3)  # no rows (global scale kept)
+    mixed = [_problem(fmt, x3, _weights(fmt, 3072, 1024, 40)), _problem(fmt, e, _weights(fmt, 256, 1024, 41)),
+             _problem(fmt, x3, _weights(fmt, 3072, 1024, 42))]
+    ys = L.bsq_gemm_grouped_q(_fmt(fmt), mixed)
+    singles = [_single(fmt, mixed[0]), _single(fmt, mixed[2])]
+    torch.cuda.synchronize()
+    assert ys[1].shape == (0, 256)
+    assert np.array_equal(host(ys[0]), host(singles[0])) and np.array_equal(host(ys[2]), host(singles[1]))
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+def test_grouped_joint_block_16384(fmt):
+    """The joint block's four linears at 16384 tokens in one launch, as the benchmark times them."""
+    block = 0 if fmt == "nvfp4" else 1
+    xb_a, xa = _acts(fmt, syn.JOINT_TOKENS, 3072, 0)
+    xb_b, xb = _acts(fmt, syn.JOINT_TOKENS, 12288, 1)
+    probs, xbs = [], []
+    for gi, (name, N, K) in enumerate(syn.JOINT_GEMMS):
+        probs.append(_problem(fmt, xa if K == 3072 else xb, _weights(fmt, N, K, block * 4 + gi)))
+        xbs.append(xb_a if K == 3072 else xb_b)
+    _check_group(fmt, probs, xbs, sample=4)

@@ -502,6 +502,104 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
                     "hbm_frac = (weights + activations + Y bytes) / time / 8 TB/s"}
 
 
+def few_token_block(L, syn, dev, Ms=(1, 16)):
+    """A joint block's four linears (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288) for
+    a few tokens, with cold weights: four launches back to back against one grouped launch
+    (bsq_gemm_grouped_q, one grid of the few-token kernels), per scheme and token count.
+
+    The block's weights are copied until the copies exceed 600 MB and the timed calls rotate over
+    them, so that no call finds its weights in the 256 MB Infinity Cache; activations are
+    pre-quantized. Bytes per block are the algorithmic ones: weights + activations + Y.
+    """
+    import torch
+
+    lib = L.lib
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def up_bf16(bits):
+        return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
+
+    def check(st):
+        if st != 0:
+            raise L.BsqError("few-token block", st)
+
+    def timed(calls, iters=24):
+        it = iter(range(1 << 30))
+        warm_gpu(lambda: calls[next(it) % len(calls)](), ms=30.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead()
+        e0.record()
+        for i in range(iters):
+            calls[i % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e3  # us per block
+
+    gemms = syn.JOINT_GEMMS
+    out = {"gemms": [{"gemm": n, "N": N, "K": K} for n, N, K in gemms], "rows": []}
+    for scheme in ("nvfp4", "fp8r"):
+        block = []
+        for gi, (name, N, K) in enumerate(gemms):
+            w = up_bf16(syn.weights(syn.JOINT_4MP, N, K, block=gi))
+            if scheme == "nvfp4":
+                gw = L.bsq_calibrate_global_scale(w)
+                block.append((*L.bsq_quantize_act_nvfp4(w, gw), gw))
+            else:
+                block.append(L.bsq_quantize_act_fp8r(w))
+            del w
+        wbytes = sum(sum(t.numel() * t.element_size() for t in b) for b in block)
+        copies = [block] + [[tuple(t.clone() for t in b) for b in block] for _ in range(int(600e6 // wbytes))]
+        for Mi in Ms:
+            xs = {}
+            for K in sorted({K for _, _, K in gemms}):
+                x = up_bf16(syn.activations(syn.JOINT_4MP, Mi, K, block=0 if K == 3072 else 1))
+                if scheme == "nvfp4":
+                    gx = L.bsq_calibrate_global_scale(x)
+                    xs[K] = (*L.bsq_quantize_act_nvfp4(x, gx), gx)
+                else:
+                    xs[K] = L.bsq_quantize_act_fp8r(x)
+            ys = [torch.empty((Mi, N), dtype=torch.bfloat16, device=dev) for _, N, _ in gemms]
+            singles, groups = [], []
+            for cp in copies:
+                probs = (L.GemmProblem * len(gemms))()
+                one = []
+                for gi, (name, N, K) in enumerate(gemms):
+                    xa, w, y = xs[K], cp[gi], ys[gi]
+                    if scheme == "nvfp4":
+                        probs[gi] = L.GemmProblem(P(xa[0]), P(xa[1]), P(xa[2]), P(w[0]), P(w[1]), P(w[2]), P(y), N, Mi,
+                                                  N, K)
+                        one.append(lambda xa=xa, w=w, y=y, N=N, K=K: check(lib.bsq_gemm_nvfp4_q(
+                            P(xa[0]), P(xa[1]), P(xa[2]), P(w[0]), P(w[1]), P(w[2]), P(y), N, Mi, N, K, stream)))
+                    else:
+                        probs[gi] = L.GemmProblem(P(xa[0]), P(xa[1]), None, P(w[0]), P(w[1]), None, P(y), N, Mi, N,
+                                                  K)
+                        one.append(lambda xa=xa, w=w, y=y, N=N, K=K: check(lib.bsq_gemm_fp8r_q(
+                            P(xa[0]), P(xa[1]), P(w[0]), P(w[1]), P(y), N, Mi, N, K, stream)))
+                singles.append(lambda one=one: [c() for c in one])
+                fmt = L.BSQ_FMT_NVFP4 if scheme == "nvfp4" else L.BSQ_FMT_FP8R
+                groups.append(lambda probs=probs, fmt=fmt: check(lib.bsq_gemm_grouped_q(fmt, probs, len(gemms),
+                                                                                         stream)))
+            us_four, us_grouped = timed(singles), timed(groups)
+            nbytes = wbytes + sum(xs[K][0].numel() + xs[K][1].numel() * xs[K][1].element_size() for K in xs) \
+                + sum(2 * Mi * N for _, N, _ in gemms)
+            row = {"scheme": scheme, "M": Mi, "four_launches_us": round(us_four, 2),
+                   "grouped_us": round(us_grouped, 2),
+                   "hbm_frac_four_launches": round(nbytes / (us_four * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                   "hbm_frac_grouped": round(nbytes / (us_grouped * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                   "block_mb": round(nbytes / 1e6, 2)}
+            out["rows"].append(row)
+            log("few-token block %s M=%d: four launches %.1f us, one grouped launch %.1f us" %
+                (scheme, Mi, us_four, us_grouped))
+            del ys, singles, groups
+        del copies, block
+        torch.cuda.empty_cache()
+    out["note"] = ("us per block (the four GEMMs) from events around 24 back-to-back blocks rotated over > 600 MB of "
+                   "weight copies (cold weights), queued behind other GPU work; hbm_frac = (weights + activations + "
+                   "Y bytes) / time / 8 TB/s")
+    return out
+
+
 def joint_block_sweep(L, syn, dev, reps=5):
     """The 4-megapixel joint-block workload: 16384 tokens through the four linears of a block
     (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288), once as an nvfp4 W4A4 block
@@ -822,6 +920,9 @@ def main():
     if not args.no_small_m:
         log("few-token sweep")
         result["small_m"] = small_m_sweep(L, syn, dev)
+    if not args.no_small_m:
+        log("few-token joint block")
+        result["few_token_block"] = few_token_block(L, syn, dev)
     if not args.no_joint:
         log("joint-block shapes")
         result["joint_block_4mp"] = joint_block_sweep(L, syn, dev)

@@ -384,40 +384,53 @@ bsq_status bsq_gemm_grouped_q(bsq_format format, const bsq_gemm_problem* problem
   // longest K first (stable), so the grid's last round holds the shortest tiles
   for (int i = 1; i < n; ++i)
     for (int j = i; j > 0 && problems[order[j]].K > problems[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
+  // the problems as the single entry points see them
+  const bsq::DecMode mode = fp8 ? bsq::kW8A8 : bsq::kW4A4;
+  auto args = [&](const bsq_gemm_problem& p) {
+    bsq::DecArgs a{};
+    a.xq = p.xq; a.w = p.w; a.y = p.y; a.ldy = p.ldy; a.M = p.M; a.N = p.N; a.K = p.K;
+    if (fp8) {
+      a.sx = static_cast<const float*>(p.x_scale); a.sw = static_cast<const float*>(p.w_scale);
+    } else {
+      a.xs = static_cast<const uint8_t*>(p.x_scale); a.gx = p.input_scale;
+      a.ws = static_cast<const uint8_t*>(p.w_scale); a.gw = p.w_scale2;
+    }
+    return a;
+  };
+  bsq::DecArgs q[BSQ_MAX_GROUP];
+  int few = 0;  // problems on the few-token route
+  for (int i = 0; i < n; ++i) {
+    q[i] = args(problems[order[i]]);
+    few += route_skinny(mode, q[i]) ? 1 : 0;
+  }
+  // one grid when every problem takes the same route and the grouped kernels cover the group
   hipError_t e = hipSuccess;
-  if (fp8) {
-    bsq::Fp8Problem q[BSQ_MAX_GROUP];
-    for (int i = 0; i < n; ++i) {
-      const bsq_gemm_problem& p = problems[order[i]];
-      q[i] = bsq::Fp8Problem{p.xq, static_cast<const float*>(p.x_scale), p.w, static_cast<const float*>(p.w_scale),
-                             p.y, p.ldy, (int)p.M, (int)p.N, (int)p.K, 0};
+  bool done = false;
+  if (few == n && bsq::gemm_skinny_grouped_supported(mode, q, n)) {
+    e = bsq::launch_gemm_skinny_grouped(mode, q, n, stream);
+    done = true;
+  } else if (few == 0 && fp8) {
+    bsq::Fp8Problem f[BSQ_MAX_GROUP];
+    for (int i = 0; i < n; ++i)
+      f[i] = bsq::Fp8Problem{q[i].xq, q[i].sx, q[i].w, q[i].sw, q[i].y, q[i].ldy, (int)q[i].M, (int)q[i].N,
+                             (int)q[i].K, 0};
+    if (bsq::gemm_fp8_grouped_supported(f, n)) {
+      e = bsq::launch_gemm_fp8_grouped(f, n, stream);
+      done = true;
     }
-    if (bsq::gemm_fp8_grouped_supported(q, n)) {
-      e = bsq::launch_gemm_fp8_grouped(q, n, stream);
-    } else {
-      for (int i = 0; i < count && e == hipSuccess; ++i) {
-        const bsq_gemm_problem& p = problems[i];
-        if (p.M > 0 && p.N > 0)
-          e = launch_w8a8(p.xq, static_cast<const float*>(p.x_scale), p.w, static_cast<const float*>(p.w_scale), p.y,
-                          p.ldy, p.M, p.N, p.K, stream);
-      }
-    }
-  } else {
-    bsq::DecArgs q[BSQ_MAX_GROUP];
-    auto args = [](const bsq_gemm_problem& p) {
-      bsq::DecArgs a{};
-      a.xq = p.xq; a.xs = static_cast<const uint8_t*>(p.x_scale); a.gx = p.input_scale; a.w = p.w;
-      a.ws = static_cast<const uint8_t*>(p.w_scale); a.gw = p.w_scale2; a.y = p.y; a.ldy = p.ldy;
-      a.M = p.M; a.N = p.N; a.K = p.K;
-      return a;
-    };
-    for (int i = 0; i < n; ++i) q[i] = args(problems[order[i]]);
-    if (bsq::gemm_w4a4_grouped_supported(q, n)) {
-      e = bsq::launch_gemm_w4a4_grouped(q, n, stream);
-    } else {
-      for (int i = 0; i < count && e == hipSuccess; ++i)
-        if (problems[i].M > 0 && problems[i].N > 0) e = launch_dec_or_skinny(bsq::kW4A4, args(problems[i]), stream);
-    }
+  } else if (few == 0 && bsq::gemm_w4a4_grouped_supported(q, n)) {
+    e = bsq::launch_gemm_w4a4_grouped(q, n, stream);
+    done = true;
+  }
+  // otherwise one launch per problem, in the order given
+  for (int i = 0; i < count && !done && e == hipSuccess; ++i) {
+    const bsq_gemm_problem& p = problems[i];
+    if (p.M == 0 || p.N == 0) continue;
+    if (fp8)
+      e = launch_w8a8(p.xq, static_cast<const float*>(p.x_scale), p.w, static_cast<const float*>(p.w_scale), p.y,
+                      p.ldy, p.M, p.N, p.K, stream);
+    else
+      e = launch_dec_or_skinny(bsq::kW4A4, args(p), stream);
   }
   return e == hipSuccess ? BSQ_OK : hip_fail(e);
 }

@@ -166,6 +166,9 @@ hipError_t launch_gemm_w4a4_grouped(const DecArgs* p, int count, hipStream_t s);
 // Few-token GEMMs: 32 weight rows per workgroup, K split over its 8 waves
 bool gemm_skinny_supported(DecMode mode, const DecArgs& a);
 hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s);
+// Several few-token W4A4 or W8A8 GEMMs (no adapter, bf16 output) in one grid
+bool gemm_skinny_grouped_supported(DecMode mode, const DecArgs* p, int count);
+hipError_t launch_gemm_skinny_grouped(DecMode mode, const DecArgs* p, int count, hipStream_t s);
 
 }  // namespace bsq
 

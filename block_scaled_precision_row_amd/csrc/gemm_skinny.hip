@@ -369,8 +369,9 @@ __device__ __forceinline__ void read_bf16(OpBf& o, const uint8_t* codes, int lr,
   for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
 }
 
-template <int MODE, int MB, bool LORA, int NWV = kSkStagedWaves>
-__global__ __launch_bounds__(64 * NWV) void gemm_skinny_staged_kernel(DecArgs a) {
+// One workgroup's 32 weight rows and MB activation blocks: workgroup `bid` of the grid.
+template <int MODE, int MB, bool LORA, int NWV>
+__device__ __forceinline__ void skinny_staged_tile(const DecArgs& a, int bid) {
   static_assert(MODE == kW4A4 || MODE == kW4A16, "nvfp4 weights only");
   using S = Scheme<MODE>;
   constexpr int NW = NWV;
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_staged_kernel(DecArgs a)
 
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   const int nblk = (N + 31) / 32;
-  const int n0 = (blockIdx.x % nblk) * 32, m0 = (blockIdx.x / nblk) * (32 * MB);
+  const int n0 = (bid % nblk) * 32, m0 = (bid / nblk) * (32 * MB);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_staged_kernel(DecArgs a)
 
   const int nk = (K + kSkK - 1) / kSkK;
   const int mine = nk > wave ? (nk - wave + NW - 1) / NW : 0;  // uniform per wave
-  const int rot = (int)(blockIdx.x % (unsigned)nk);
+  const int rot = (int)((unsigned)bid % (unsigned)nk);
   RawNv w0, w1, w2;
   RawX x0[MB], x1[MB], x2[MB];
   auto fetch = [&](RawNv& w, RawX (&x)[MB], int i) {
@@ -484,6 +485,11 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_staged_kernel(DecArgs a)
   skinny_epilogue<MODE, MB, NW, LORA>(a, red, lred, m0, n0, tid);
 }
 
+template <int MODE, int MB, bool LORA, int NWV = kSkStagedWaves>
+__global__ __launch_bounds__(64 * NWV) void gemm_skinny_staged_kernel(DecArgs a) {
+  skinny_staged_tile<MODE, MB, LORA, NWV>(a, blockIdx.x);
+}
+
 // ---- LDS-DMA variant (E4M3 weights): stage layout of one wave -----------------------
 // A code region holds 32 rows of R bytes (R = 128 for E4M3, 256 for bf16 at a 128-deep
 // stage), 16-byte chunks XOR-swizzled as in gemm_common.hpp.
@@ -534,8 +540,9 @@ __device__ __forceinline__ void read_bf(OpBf& o, const uint8_t* codes, int lr, i
   for (int c = 0; c < 8; ++c) o.d[c] = *reinterpret_cast<const uint4*>(codes + swz_off<256>(lr, 8 * lh + c));
 }
 
+// One workgroup's 32 weight rows and MB activation blocks: workgroup `bid` of the grid.
 template <int MODE, int MB, int NW, bool LORA>
-__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
+__device__ __forceinline__ void skinny_tile(const DecArgs& a, int bid) {
   using S = Scheme<MODE>;
   using L = Layout<MODE>;
   using SC = SkCfg<MODE, MB, NW, LORA>;
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
 
   const int M = (int)a.M, N = (int)a.N, K = (int)a.K;
   const int nblk = (N + 31) / 32;
-  const int n0 = (blockIdx.x % nblk) * 32, m0 = (blockIdx.x / nblk) * (32 * MB);
+  const int n0 = (bid % nblk) * 32, m0 = (bid / nblk) * (32 * MB);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lh = lane >> 5;
@@ -569,7 +576,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   const uint32_t wave_lds = lds_offset(smem) + (uint32_t)(wave * WAVE);
   const uint8_t* wave_mem = smem + wave * WAVE;
   const int nk = (K + kSkK - 1) / kSkK;
-  const int rot = (int)(blockIdx.x % (unsigned)nk);
+  const int rot = (int)((unsigned)bid % (unsigned)nk);
   // fetch this wave's i-th stage into ring buffer i % 2 (stages past K read as zeros)
   auto issue = [&](int i) {
     const int kv = stage_k(wave, NW, i, nk, rot, K);
@@ -626,6 +633,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
   __syncthreads();
 
   skinny_epilogue<MODE, MB, NW, LORA>(a, red, lred, m0, n0, tid);
+}
+
+template <int MODE, int MB, int NW, bool LORA>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(DecArgs a) {
+  skinny_tile<MODE, MB, NW, LORA>(a, blockIdx.x);
+}
+
+// The workgroups of several few-token GEMMs of one scheme in one grid: each workgroup finds its
+// problem and computes what that problem's own launch computes in its workgroup (same bits).
+struct SkGroup {
+  DecArgs p[kMaxGroup];
+  int start[kMaxGroup + 1];
+  int count;
+};
+template <int MODE, int MB, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_staged_grouped_kernel(SkGroup g) {
+  const int bid = blockIdx.x;
+  const int p = group_problem(g.start, g.count, bid);
+  skinny_staged_tile<MODE, MB, false, NW>(g.p[p], bid - g.start[p]);
+}
+template <int MODE, int MB, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_grouped_kernel(SkGroup g) {
+  const int bid = blockIdx.x;
+  const int p = group_problem(g.start, g.count, bid);
+  skinny_tile<MODE, MB, NW, false>(g.p[p], bid - g.start[p]);
 }
 
 template <int MODE, int MB, int NW>
@@ -701,6 +733,57 @@ hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s) {
     case kW8A8: return pick<kW8A8>(a, s);
     default: return pick<kW8A16>(a, s);
   }
+}
+
+// Grouped few-token launch (W4A4, W8A8; no adapter): one grid over every problem's workgroups,
+// the variant (activation blocks and waves per workgroup) picked for the whole group from the
+// largest token count and the group's total grid. A group's grid holds several problems' worth
+// of workgroups, which favours more waves per workgroup than one launch of the same token count
+// would take: a joint block's four linears (qkv, proj, up, down; cold weights) at 16 tokens
+// took 34.5 us as one grid of four-wave W4A4 workgroups and 27.0 us with eight waves; W8A8 took
+// 27.9 us with four waves and 30.0 us with eight, but 25.8 -> 24.8 us with eight at one token.
+bool gemm_skinny_grouped_supported(DecMode mode, const DecArgs* p, int count) {
+  if ((mode != kW4A4 && mode != kW8A8) || count < 2 || count > kMaxGroup) return false;
+  for (int i = 0; i < count; ++i)
+    if (p[i].lt || p[i].yq || p[i].ypmax || !p[i].y || !gemm_skinny_supported(mode, p[i])) return false;
+  return true;
+}
+
+namespace {
+template <int MODE, int MB, int NW, bool STAGED>
+hipError_t run_grouped(const DecArgs* p, int count, hipStream_t s) {
+  SkGroup g{};
+  g.count = count;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    g.p[i] = p[i];
+    g.start[i] = (int)total;
+    total += ((p[i].N + 31) / 32) * ((p[i].M + 32 * MB - 1) / (32 * MB));
+  }
+  for (int i = count; i <= kMaxGroup; ++i) g.start[i] = (int)total;
+  if constexpr (STAGED)
+    hipLaunchKernelGGL((gemm_skinny_staged_grouped_kernel<MODE, MB, NW>), dim3((unsigned)total), dim3(64 * NW), 0, s,
+                       g);
+  else
+    hipLaunchKernelGGL((gemm_skinny_grouped_kernel<MODE, MB, NW>), dim3((unsigned)total), dim3(64 * NW), 0, s, g);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_skinny_grouped(DecMode mode, const DecArgs* p, int count, hipStream_t s) {
+  int64_t mmax = 0, grid64 = 0;
+  for (int i = 0; i < count; ++i) {
+    mmax = p[i].M > mmax ? p[i].M : mmax;
+    grid64 += ((p[i].N + 31) / 32) * ((p[i].M + 63) / 64);
+  }
+  if (mode == kW4A4) {
+    if (mmax > 64) return run_grouped<kW4A4, 2, kSkStagedWaves, true>(p, count, s);
+    return run_grouped<kW4A4, 1, kSkStagedWaves, true>(p, count, s);
+  }
+  const bool short_grid = grid64 < 256;
+  if (mmax <= 8) return run_grouped<kW8A8, 1, 8, false>(p, count, s);
+  if (mmax <= 32 || short_grid) return run_grouped<kW8A8, 1, 4, false>(p, count, s);
+  return run_grouped<kW8A8, 2, 4, false>(p, count, s);
 }
 
 }  // namespace bsq

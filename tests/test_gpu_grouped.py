@@ -138,3 +138,36 @@ def test_grouped_joint_block_16384(fmt):
         probs.append(_problem(fmt, xa if K == 3072 else xb, _weights(fmt, N, K, block * 4 + gi)))
         xbs.append(xb_a if K == 3072 else xb_b)
     _check_group(fmt, probs, xbs, sample=4)
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+@pytest.mark.parametrize("M", [1, 16])
+def test_grouped_few_tokens_joint_block(fmt, M):
+    """The joint block's four linears for a few tokens: every problem on the few-token route, so the
+    group runs as one grid of the few-token kernels (a workgroup per 32 weight rows)."""
+    xb_a, xa = _acts(fmt, M, 3072, 6)
+    xb_b, xb = _acts(fmt, M, 12288, 7)
+    probs, xbs = [], []
+    for gi, (name, N, K) in enumerate(syn.JOINT_GEMMS):
+        probs.append(_problem(fmt, xa if K == 3072 else xb, _weights(fmt, N, K, 50 + gi)))
+        xbs.append(xb_a if K == 3072 else xb_b)
+    _check_group(fmt, probs, xbs, sample=min(M, 6))
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+@pytest.mark.parametrize("M,shapes", [
+    (100, [(4096, 1024), (2048, 1024), (3072, 2048), (2000, 1024)]),  # two activation blocks a workgroup
+    (4, [(1024, 1024), (512, 1024), (2048, 1024)]),                   # a handful of tokens on a small grid
+    (40, [(3072, 3072), (12288, 3072)]),                              # routes differ: one launch per problem
+])
+def test_grouped_few_token_variants(fmt, M, shapes):
+    """Few-token groups on each workgroup variant the grouped launch picks, ragged N included,
+    and a group whose problems take different routes."""
+    xbs, probs, acts = [], [], {}
+    for b, (N, K) in enumerate(shapes):
+        if K not in acts:
+            acts[K] = _acts(fmt, M, K, 60 + len(acts))
+        xb, x = acts[K]
+        probs.append(_problem(fmt, x, _weights(fmt, N, K, 70 + b)))
+        xbs.append(xb)
+    _check_group(fmt, probs, xbs, sample=min(M, 6))

@@ -502,10 +502,12 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
                     "hbm_frac = (weights + activations + Y bytes) / time / 8 TB/s"}
 
 
-def few_token_block(L, syn, dev, Ms=(1, 16)):
-    """A joint block's four linears (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288) for
-    a few tokens, with cold weights: four launches back to back against one grouped launch
-    (bsq_gemm_grouped_q, one grid of the few-token kernels), per scheme and token count.
+def block_launches(L, syn, dev, Ms=(1, 16, 512, 2048)):
+    """A joint block's four linears (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288) with
+    cold weights: four launches back to back against one grouped launch (bsq_gemm_grouped_q), per
+    scheme and token count. At 1 and 16 tokens the group runs as one grid of the few-token kernels;
+    at 512 tokens (under two rounds of large tiles) as one launch per problem, so both columns
+    time the same kernels; at 2048 tokens as one grid of the tiled kernels.
 
     The block's weights are copied until the copies exceed 600 MB and the timed calls rotate over
     them, so that no call finds its weights in the 256 MB Infinity Cache; activations are
@@ -522,7 +524,7 @@ def few_token_block(L, syn, dev, Ms=(1, 16)):
 
     def check(st):
         if st != 0:
-            raise L.BsqError("few-token block", st)
+            raise L.BsqError("block launches", st)
 
     def timed(calls, iters=24):
         it = iter(range(1 << 30))
@@ -589,7 +591,7 @@ def few_token_block(L, syn, dev, Ms=(1, 16)):
                    "hbm_frac_grouped": round(nbytes / (us_grouped * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                    "block_mb": round(nbytes / 1e6, 2)}
             out["rows"].append(row)
-            log("few-token block %s M=%d: four launches %.1f us, one grouped launch %.1f us" %
+            log("joint block %s M=%d: four launches %.1f us, one grouped launch %.1f us" %
                 (scheme, Mi, us_four, us_grouped))
             del ys, singles, groups
         del copies, block
@@ -921,8 +923,8 @@ def main():
         log("few-token sweep")
         result["small_m"] = small_m_sweep(L, syn, dev)
     if not args.no_small_m:
-        log("few-token joint block")
-        result["few_token_block"] = few_token_block(L, syn, dev)
+        log("joint block: four launches vs one grouped launch")
+        result["block_launches"] = block_launches(L, syn, dev)
     if not args.no_joint:
         log("joint-block shapes")
         result["joint_block_4mp"] = joint_block_sweep(L, syn, dev)

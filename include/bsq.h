@@ -202,10 +202,13 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
  * bsq_gemm_nvfp4_q (BSQ_FMT_NVFP4) returns for its operands: one grid holds
  * every problem's output tiles, longest K first, so one problem's last round
  * of tiles overlaps the next problem's first instead of leaving compute
- * units idle between launches. Groups the grouped kernels do not cover (fp8r
- * with K % 128 != 0, nvfp4 with K % 256 != 0, or fewer output tiles in all
- * than one round of 256 x 192 tiles on the 256 compute units) run as one
- * launch per problem, in the order given, with the same results.
+ * units idle between launches. A group whose problems all take the
+ * few-token route (a few dozen tokens or fewer) runs as one grid of the
+ * few-token kernels. Groups the grouped kernels do not cover (fp8r with
+ * K % 128 != 0, nvfp4 with K % 256 != 0, fewer output tiles in all than two
+ * rounds of 256 x 192 tiles on the 256 compute units, or problems on
+ * different routes) run as one launch per problem, in the order given, with
+ * the same results.
  *   problems : host array of `count` descriptors (read during the call only);
  *              count 0 is a no-op, 1 <= count <= BSQ_MAX_GROUP otherwise
  *   per problem, with the layouts and alignment of the two entry points:

@@ -93,8 +93,8 @@ def _check_group(fmt, probs, xbs, sample=12, seed=0):
 
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
 def test_grouped_kernel_mixed_shapes(fmt):
-    """296 tiles of 256 x 192 in all (the grouped kernel), ragged M and N, the longest K last."""
-    M = 2000
+    """592 tiles of 256 x 192 in all (the grouped kernel), ragged M and N, the longest K last."""
+    M = 4000
     xb1, x1 = _acts(fmt, M, 1024, 0)
     xb2, x2 = _acts(fmt, M, 2048, 1)
     shapes = [(2304, 1024), (776, 1024), (3072, 1024), (760, 2048)]
@@ -108,7 +108,8 @@ def test_grouped_kernel_mixed_shapes(fmt):
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
 def test_grouped_fallback_paths(fmt):
     """Groups the grouped kernels do not take run one launch per problem, with the same bits:
-    too few tiles, a K that is not a whole number of the grouped kernels' stages, empty problems."""
+    too few tiles (300 and 2000 tokens: less than two rounds of 256 x 192 tiles), a K that is not
+    a whole number of the grouped kernels' stages, empty problems."""
     xb, x = _acts(fmt, 300, 512, 2)
     small = [_problem(fmt, x, _weights(fmt, N, 512, 20 + i)) for i, N in enumerate((520, 264))]
     _check_group(fmt, small, [xb, xb])

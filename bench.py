@@ -502,10 +502,10 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
                     "hbm_frac = (weights + activations + Y bytes) / time / 8 TB/s"}
 
 
-def block_launches(L, syn, dev, Ms=(1, 16, 512, 2048)):
+def block_launches(L, syn, dev, Ms=(1, 16, 32, 512, 2048)):
     """A joint block's four linears (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288) with
     cold weights: four launches back to back against one grouped launch (bsq_gemm_grouped_q), per
-    scheme and token count. At 1 and 16 tokens the group runs as one grid of the few-token kernels;
+    scheme and token count. At 1, 16 and 32 tokens the group runs as one grid of the few-token kernels;
     at 512 tokens (under two rounds of large tiles) as one launch per problem, so both columns
     time the same kernels; at 2048 tokens as one grid of the tiled kernels.
 

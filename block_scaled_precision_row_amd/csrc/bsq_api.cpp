@@ -406,7 +406,13 @@ bsq_status bsq_gemm_grouped_q(bsq_format format, const bsq_gemm_problem* problem
   // one grid when every problem takes the same route and the grouped kernels cover the group
   hipError_t e = hipSuccess;
   bool done = false;
-  if (few == n && bsq::gemm_skinny_grouped_supported(mode, q, n)) {
+  // Up to 64 tokens the few-token grid also serves a group whose larger problems alone would take
+  // the tiled kernels: a joint block's four linears (cold weights) at 32 / 64 tokens as one
+  // few-token grid against four launches, nvfp4 33.0 / 50.0 vs 71.8 / 60.2 us, fp8r 32.6 / 46.8
+  // vs 49.3 / 50.4 us (at 96 and 128 tokens the launches win: 83 / 85 vs 96 / 106 us nvfp4).
+  int64_t mmax = 0;
+  for (int i = 0; i < n; ++i) mmax = q[i].M > mmax ? q[i].M : mmax;
+  if ((few == n || (few > 0 && mmax <= 64)) && bsq::gemm_skinny_grouped_supported(mode, q, n)) {
     e = bsq::launch_gemm_skinny_grouped(mode, q, n, stream);
     done = true;
   } else if (few == 0 && fp8) {

@@ -197,18 +197,24 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
  * one kernel launch (the four linears of a joint transformer block -- qkv,
  * proj, MLP up and down -- whose 28 blocks the FLUX 3 Image Klein release
  * page, section one, describes; each linear's arithmetic is that of the
- * "BFL (fp8r / nvfp4)" scheme list and "Kernels" table, as above). Problem i's
- * y is, bit for bit, what bsq_gemm_fp8r_q (format BSQ_FMT_FP8R) or
- * bsq_gemm_nvfp4_q (BSQ_FMT_NVFP4) returns for its operands: one grid holds
- * every problem's output tiles, longest K first, so one problem's last round
- * of tiles overlaps the next problem's first instead of leaving compute
- * units idle between launches. A group whose problems all take the
- * few-token route (a few dozen tokens or fewer) runs as one grid of the
- * few-token kernels. Groups the grouped kernels do not cover (fp8r with
- * K % 128 != 0, nvfp4 with K % 256 != 0, fewer output tiles in all than two
- * rounds of 256 x 192 tiles on the 256 compute units, or problems on
- * different routes) run as one launch per problem, in the order given, with
- * the same results.
+ * "BFL (fp8r / nvfp4)" scheme list and "Kernels" table, as above). One grid
+ * holds every problem's work, longest K first, so one problem's last round
+ * overlaps the next problem's first instead of leaving compute units idle
+ * between launches, and each launch's fixed cost is paid once:
+ *  - problems that alone would run on the tiled kernels (several hundred
+ *    tokens and more) share one grid of them when the group holds at least
+ *    two rounds of 256 x 192 output tiles on the 256 compute units; each y is
+ *    then, bit for bit, what bsq_gemm_fp8r_q (format BSQ_FMT_FP8R) or
+ *    bsq_gemm_nvfp4_q (BSQ_FMT_NVFP4) returns for its operands;
+ *  - a group of at most 64 tokens in which some problem alone would take the
+ *    few-token kernels runs as one grid of the few-token kernels: the y of a
+ *    problem that alone takes them is bit for bit the single call's, the y of
+ *    one that alone would take the tiled kernels is the few-token kernels'
+ *    result (the same products, summed over K in another order: within the
+ *    GEMM tolerance of the single call's, and deterministic);
+ *  - anything else (fp8r with K % 128 != 0, nvfp4 with K % 256 != 0, fewer
+ *    tiles, 65 or more tokens on mixed routes) runs one launch per problem,
+ *    in the order given, with the single calls' results.
  *   problems : host array of `count` descriptors (read during the call only);
  *              count 0 is a no-op, 1 <= count <= BSQ_MAX_GROUP otherwise
  *   per problem, with the layouts and alignment of the two entry points:

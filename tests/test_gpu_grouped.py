@@ -76,14 +76,19 @@ def _oracle_rows(fmt, p, xb, rows):
     return gemm.gemm_nvfp4(xq, xs, np.float32(gx[0]), wq, ws, np.float32(gw[0]))
 
 
-def _check_group(fmt, probs, xbs, sample=12, seed=0):
+def _check_group(fmt, probs, xbs, sample=12, seed=0, exact=None):
+    """`exact`: the problems whose output must equal the single call's bit for bit (all by default);
+    every sampled row of every problem is checked against the oracle."""
     ys = L.bsq_gemm_grouped_q(_fmt(fmt), probs)
+    again = L.bsq_gemm_grouped_q(_fmt(fmt), probs)
     singles = [_single(fmt, p) for p in probs]
     torch.cuda.synchronize()
     rng = np.random.default_rng(seed)
     for i, (y, s) in enumerate(zip(ys, singles)):
         yb, sb = host(y), host(s)
-        assert np.array_equal(yb, sb), "problem %d differs from its single launch" % i
+        assert np.array_equal(yb, host(again[i])), "problem %d: two grouped calls differ" % i
+        if exact is None or i in exact:
+            assert np.array_equal(yb, sb), "problem %d differs from its single launch" % i
         if sample:
             M = yb.shape[0]
             rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, sample, replace=False)]))
@@ -142,28 +147,32 @@ def test_grouped_joint_block_16384(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 16, 48])
 def test_grouped_few_tokens_joint_block(fmt, M):
-    """The joint block's four linears for a few tokens: every problem on the few-token route, so the
-    group runs as one grid of the few-token kernels (a workgroup per 32 weight rows)."""
+    """The joint block's four linears for a few tokens as one grid of the few-token kernels (a
+    workgroup per 32 weight rows). At 48 tokens qkv and up alone would take the tiled kernels, so
+    only proj and down must match their single calls bit for bit."""
     xb_a, xa = _acts(fmt, M, 3072, 6)
     xb_b, xb = _acts(fmt, M, 12288, 7)
     probs, xbs = [], []
     for gi, (name, N, K) in enumerate(syn.JOINT_GEMMS):
         probs.append(_problem(fmt, xa if K == 3072 else xb, _weights(fmt, N, K, 50 + gi)))
         xbs.append(xb_a if K == 3072 else xb_b)
-    _check_group(fmt, probs, xbs, sample=min(M, 6))
+    _check_group(fmt, probs, xbs, sample=min(M, 6), exact=None if M <= 16 else (1, 3))
 
 
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
-@pytest.mark.parametrize("M,shapes", [
-    (100, [(4096, 1024), (2048, 1024), (3072, 2048), (2000, 1024)]),  # two activation blocks a workgroup
-    (4, [(1024, 1024), (512, 1024), (2048, 1024)]),                   # a handful of tokens on a small grid
-    (40, [(3072, 3072), (12288, 3072)]),                              # routes differ: one launch per problem
+@pytest.mark.parametrize("M,shapes,exact", [
+    (100, [(4096, 1024), (2048, 1024), (3072, 2048), (2000, 1024)], None),  # two activation blocks a workgroup
+    (4, [(1024, 1024), (512, 1024), (2048, 1024)], None),                   # a handful of tokens, small grid
+    (40, [(3072, 3072), (12288, 3072)], (0,)),    # alone, N = 12288 would take the tiled kernels
+    (80, [(3072, 3072), (12288, 3072)], None),    # the same past 64 tokens: one launch per problem
 ])
-def test_grouped_few_token_variants(fmt, M, shapes):
-    """Few-token groups on each workgroup variant the grouped launch picks, ragged N included,
-    and a group whose problems take different routes."""
+def test_grouped_few_token_variants(fmt, M, shapes, exact):
+    """Few-token groups on each workgroup variant the grouped launch picks, ragged N included, and
+    groups whose problems alone take different routes: up to 64 tokens all of them run on the
+    few-token kernels (bit for bit the single call where that is the problem's own route, within
+    the tolerance of the oracle everywhere), beyond that one launch per problem."""
     xbs, probs, acts = [], [], {}
     for b, (N, K) in enumerate(shapes):
         if K not in acts:
@@ -171,4 +180,4 @@ def test_grouped_few_token_variants(fmt, M, shapes):
         xb, x = acts[K]
         probs.append(_problem(fmt, x, _weights(fmt, N, K, 70 + b)))
         xbs.append(xb)
-    _check_group(fmt, probs, xbs, sample=min(M, 6))
+    _check_group(fmt, probs, xbs, sample=min(M, 6), exact=exact)

@@ -580,7 +580,7 @@ bool gemm_fp8_grouped_supported(const Fp8Problem* p, int count) {
     if (p[i].K % kStageK != 0) return false;
     tiles += ((int64_t)(p[i].M + 255) / 256) * ((p[i].N + 191) / 192);
   }
-  return tiles >= 512;
+  return tiles >= 512 && tiles < ((int64_t)1 << 31);  // the grid's workgroup ids are 32-bit
 }
 
 // One grid over every problem's tiles, the tile shape chosen for the whole group as for one

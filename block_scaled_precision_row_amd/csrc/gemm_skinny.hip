@@ -744,9 +744,12 @@ hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s) {
 // 27.9 us with four waves and 30.0 us with eight, but 25.8 -> 24.8 us with eight at one token.
 bool gemm_skinny_grouped_supported(DecMode mode, const DecArgs* p, int count) {
   if ((mode != kW4A4 && mode != kW8A8) || count < 2 || count > kMaxGroup) return false;
-  for (int i = 0; i < count; ++i)
+  int64_t blocks = 0;  // at one activation block a workgroup, the most the grid can hold
+  for (int i = 0; i < count; ++i) {
     if (p[i].lt || p[i].yq || p[i].ypmax || !p[i].y || !gemm_skinny_supported(mode, p[i])) return false;
-  return true;
+    blocks += ((p[i].N + 31) / 32) * ((p[i].M + 31) / 32);
+  }
+  return blocks < ((int64_t)1 << 31);  // the grid's workgroup ids are 32-bit
 }
 
 namespace {

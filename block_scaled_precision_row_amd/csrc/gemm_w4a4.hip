@@ -378,7 +378,7 @@ bool gemm_w4a4_grouped_supported(const DecArgs* p, int count) {
     if (p[i].K % kStageK != 0 || p[i].lt || p[i].yq || p[i].ypmax || !p[i].y) return false;
     tiles += ((p[i].M + 255) / 256) * ((p[i].N + 191) / 192);
   }
-  return tiles >= 512;
+  return tiles >= 512 && tiles < ((int64_t)1 << 31);  // the grid's workgroup ids are 32-bit
 }
 
 // One grid over every problem's tiles, the tile shape chosen for the whole group as for one

@@ -1,14 +1,17 @@
 """GPU parity of the grouped launch (bsq_gemm_grouped_q).
 
-Every problem of a group must come out bit for bit as the single pre-quantized
-entry point (bsq_gemm_fp8r_q / bsq_gemm_nvfp4_q) computes it -- the grouped
-kernels run the same tile code, only the workgroup -> (problem, tile) mapping
-differs -- and sampled rows must match the oracle's fp64 product within the
-GEMM tolerance. Groups cover the grouped kernels (ragged M and N, mixed K,
-longest K not first), the per-problem fallback (too few tiles, a K the grouped
-kernels do not take, empty problems) and the four joint-block linears at
-16384 tokens ("FLUX 3 Image Klein" release page, section one: 28 joint blocks
-of qkv, proj, MLP up and down).
+Every problem that keeps its own route in a group must come out bit for bit as
+the single pre-quantized entry point (bsq_gemm_fp8r_q / bsq_gemm_nvfp4_q)
+computes it -- the grouped kernels run the same tile code, only the workgroup
+-> (problem, tile) mapping differs; a problem that a group of at most 64 tokens
+moves onto the few-token kernels is checked against the oracle only. Every
+grouped call must repeat its own bits, and sampled rows of every problem must
+match the oracle's fp64 product within the GEMM tolerance. Groups cover the
+grouped tiled kernels (ragged M and N, mixed K, longest K not first), every
+few-token variant, mixed routes, the per-problem fallback (too few tiles, a K
+the grouped kernels do not take, empty problems) and the four joint-block
+linears at 1, 16, 48 and 16384 tokens ("FLUX 3 Image Klein" release page,
+section one: 28 joint blocks of qkv, proj, MLP up and down).
 """
 import numpy as np
 import pytest

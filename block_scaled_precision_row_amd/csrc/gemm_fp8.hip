@@ -486,8 +486,8 @@ struct Fp8Group {
   int start[kMaxGroup + 1];
   int count;
 };
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_fp8_grouped_kernel(Fp8Group g) {
   const int bid = blockIdx.x;
   const int p = group_problem(g.start, g.count, bid);
@@ -566,34 +566,55 @@ hipError_t run(const uint8_t* xq, const float* sx, const uint8_t* w, const float
 
 }  // namespace
 
-// Grouped W8A8: every problem on the hand-ordered loop (K % 128 == 0), and at least two rounds
-// of 256 x 192 tiles in all. Below that one launch per
-// problem does better, its smaller tiles filling the compute units; above it one grid removes
-// each launch's partly empty last round. A joint block's four linears (qkv, proj, up, down) as
-// one grid against four launches: 512 tokens (288 tiles) nvfp4 196 vs 171 us, fp8r 145 vs
-// 130 us; 1024 tokens nvfp4 214 vs 281 us, fp8r 146 vs 154 us; 2048 tokens nvfp4 362 vs 447 us,
-// fp8r 225 vs 290 us; 4096 tokens nvfp4 682 vs 719 us, fp8r 413 vs 441 us.
-bool gemm_fp8_grouped_supported(const Fp8Problem* p, int count) {
-  if (count < 2 || count > kMaxGroup) return false;
-  int64_t tiles = 0;
-  for (int i = 0; i < count; ++i) {
-    if (p[i].K % kStageK != 0) return false;
-    tiles += ((int64_t)(p[i].M + 255) / 256) * ((p[i].N + 191) / 192);
-  }
-  return tiles >= 512 && tiles < ((int64_t)1 << 31);  // the grid's workgroup ids are 32-bit
-}
-
-// One grid over every problem's tiles, the tile shape chosen for the whole group as for one
-// GEMM (whole rounds of 256 x 256 or 256 x 192 tiles, each tile's time in proportion to its K).
-hipError_t launch_gemm_fp8_grouped(const Fp8Problem* p, int count, hipStream_t s) {
-  auto cost = [&](int BM, int BN, int per_tile) {
-    double work = 0;  // tiles times K / 3072
-    for (int i = 0; i < count; ++i)
-      work += (double)(((int64_t)(p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN)) * p[i].K / 3072.0;
-    return std::ceil(work / 256.0 - 1e-9) * per_tile;
+// Grouped W8A8: every problem on the hand-ordered loop (K % 128 == 0). Below three rounds of
+// 256 x 192 tiles the group runs on 128 x 128 tiles two to a compute unit, once those fill one
+// round of pairs (512 tiles); beyond, on the 256 x 256 or 256 x 192 tile of least expected time
+// over whole rounds (each tile's time in proportion to its K; round times as for one GEMM, at
+// K = 3072) when it fills two rounds. Smaller groups run one launch per problem, whose own tile
+// choice fills the compute units. A joint block's four linears (qkv, proj, up, down; cold
+// weights) as one grid against four launches, fp8r / nvfp4 (us): 384 tokens 96 / 102 vs 114 /
+// 150, 512 tokens 104 / 111 vs 129 / 171, 768 tokens 104 / 158 vs 145 / 218, 1024 tokens 144 /
+// 200 vs 156 / 242 (all on 128 x 128 pairs), 2048 tokens 221 / 356 vs 290 / 443 (256 x 192),
+// 4096 tokens 410 / 672 vs 440 / 716 (256 x 256). On 128 x 128 pairs 2048 and 4096 tokens took
+// 262 / 406 and 505 / 803 us; on 256-row tiles 512 tokens (288 tiles) took 145 / 196 us.
+namespace {
+struct GroupTile {
+  int bm, bn, per_round, round_us;
+};
+constexpr GroupTile kFp8GroupTiles[3] = {{256, 256, 256, 92}, {256, 192, 256, 72}, {128, 128, 512, 52}};
+// the group's tile (index into kFp8GroupTiles), or -1 when no tile fills two rounds
+int fp8_group_tile(const Fp8Problem* p, int count) {
+  auto tiles_of = [&](const GroupTile& c, double* work) {
+    int64_t tiles = 0;
+    double w = 0;  // tiles times K / 3072
+    for (int i = 0; i < count; ++i) {
+      const int64_t n = ((int64_t)(p[i].M + c.bm - 1) / c.bm) * ((p[i].N + c.bn - 1) / c.bn);
+      tiles += n;
+      w += (double)n * (double)p[i].K / 3072.0;
+    }
+    if (work) *work = w;
+    return tiles;
   };
-  const bool square = cost(256, 256, 92) <= cost(256, 192, 72);
-  const int BM = 256, BN = square ? 256 : 192;
+  // under three rounds of 256 x 192 tiles, 128 x 128 tiles two to a compute unit once they fill a
+  // round of pairs (measured below); otherwise the 256-row tile of fewer whole rounds
+  if (tiles_of(kFp8GroupTiles[1], nullptr) < 3 * 256) {
+    const int64_t t = tiles_of(kFp8GroupTiles[2], nullptr);
+    return t >= 512 && t < ((int64_t)1 << 31) ? 2 : -1;
+  }
+  int best = -1;
+  double best_cost = 0;
+  for (int t = 0; t < 2; ++t) {
+    const GroupTile& c = kFp8GroupTiles[t];
+    double work = 0;
+    const int64_t tiles = tiles_of(c, &work);
+    if (tiles < 2 * (int64_t)c.per_round || tiles >= ((int64_t)1 << 31)) continue;  // 32-bit workgroup ids
+    const double cost = std::ceil(work / c.per_round - 1e-9) * c.round_us;
+    if (best < 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  return best;
+}
+template <int BM, int BN, int WPE>
+hipError_t run_fp8_group(const Fp8Problem* p, int count, hipStream_t s) {
   Fp8Group g{};
   g.count = count;
   int64_t total = 0;
@@ -604,11 +625,24 @@ hipError_t launch_gemm_fp8_grouped(const Fp8Problem* p, int count, hipStream_t s
     total += ((int64_t)(p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN);
   }
   for (int i = count; i <= kMaxGroup; ++i) g.start[i] = (int)total;
-  if (square)
-    hipLaunchKernelGGL((gemm_fp8_grouped_kernel<256, 256>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_fp8_grouped_kernel<256, 192>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((gemm_fp8_grouped_kernel<BM, BN, WPE>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
   return hipGetLastError();
+}
+}  // namespace
+
+bool gemm_fp8_grouped_supported(const Fp8Problem* p, int count) {
+  if (count < 2 || count > kMaxGroup) return false;
+  for (int i = 0; i < count; ++i)
+    if (p[i].K % kStageK != 0) return false;
+  return fp8_group_tile(p, count) >= 0;
+}
+
+hipError_t launch_gemm_fp8_grouped(const Fp8Problem* p, int count, hipStream_t s) {
+  switch (fp8_group_tile(p, count)) {
+    case 0: return run_fp8_group<256, 256, 1>(p, count, s);
+    case 1: return run_fp8_group<256, 192, 1>(p, count, s);
+    default: return run_fp8_group<128, 128, 2>(p, count, s);
+  }
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* xq, const float* sx, const uint8_t* w, const float* sw,

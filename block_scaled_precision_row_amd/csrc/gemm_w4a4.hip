@@ -338,8 +338,8 @@ struct W4Group {
   int start[kMaxGroup + 1];
   int count;
 };
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gemm_w4a4_grouped_kernel(W4Group g) {
   const int bid = blockIdx.x;
   const int p = group_problem(g.start, g.count, bid);
@@ -364,34 +364,48 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
 
 bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kStageK == 0; }
 
-// Grouped W4A4: every problem with K % 256 == 0, plain bf16 output (no adapter, no quantized
-// output), and at least two rounds of 256 x 192 tiles in all. Below that one launch per
-// problem does better, its smaller tiles filling the compute units; above it one grid removes
-// each launch's partly empty last round. A joint block's four linears (qkv, proj, up, down) as
-// one grid against four launches: 512 tokens (288 tiles) nvfp4 196 vs 171 us, fp8r 145 vs
-// 130 us; 1024 tokens nvfp4 214 vs 281 us, fp8r 146 vs 154 us; 2048 tokens nvfp4 362 vs 447 us,
-// fp8r 225 vs 290 us; 4096 tokens nvfp4 682 vs 719 us, fp8r 413 vs 441 us.
-bool gemm_w4a4_grouped_supported(const DecArgs* p, int count) {
-  if (count < 2 || count > kMaxGroup) return false;
-  int64_t tiles = 0;
-  for (int i = 0; i < count; ++i) {
-    if (p[i].K % kStageK != 0 || p[i].lt || p[i].yq || p[i].ypmax || !p[i].y) return false;
-    tiles += ((p[i].M + 255) / 256) * ((p[i].N + 191) / 192);
-  }
-  return tiles >= 512 && tiles < ((int64_t)1 << 31);  // the grid's workgroup ids are 32-bit
-}
-
-// One grid over every problem's tiles, the tile shape chosen for the whole group as for one
-// GEMM (whole rounds of 256 x 256 or 256 x 192 tiles, each tile's time in proportion to its K).
-hipError_t launch_gemm_w4a4_grouped(const DecArgs* p, int count, hipStream_t s) {
-  auto cost = [&](int BM, int BN, int per_tile) {
-    double work = 0;  // tiles times K / 3072
-    for (int i = 0; i < count; ++i)
-      work += (double)(((p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN)) * (double)p[i].K / 3072.0;
-    return std::ceil(work / 256.0 - 1e-9) * per_tile;
+// Grouped W4A4: every problem with K % 256 == 0 and plain bf16 output (no adapter, no quantized
+// output). The tile rule and its measurements are those of the grouped fp8r launch: 128 x 128
+// tiles two to a compute unit below three rounds of 256 x 192 tiles (from one round of pairs),
+// else the 256 x 256 or 256 x 192 tile of least expected time over whole rounds.
+namespace {
+struct GroupTile {
+  int bm, bn, per_round, round_us;
+};
+constexpr GroupTile kW4GroupTiles[3] = {{256, 256, 256, 76}, {256, 192, 256, 60}, {128, 128, 512, 49}};
+// the group's tile (index into kW4GroupTiles), or -1 when no tile fills two rounds
+int w4a4_group_tile(const DecArgs* p, int count) {
+  auto tiles_of = [&](const GroupTile& c, double* work) {
+    int64_t tiles = 0;
+    double w = 0;  // tiles times K / 3072
+    for (int i = 0; i < count; ++i) {
+      const int64_t n = ((int64_t)(p[i].M + c.bm - 1) / c.bm) * ((p[i].N + c.bn - 1) / c.bn);
+      tiles += n;
+      w += (double)n * (double)p[i].K / 3072.0;
+    }
+    if (work) *work = w;
+    return tiles;
   };
-  const bool square = cost(256, 256, 76) <= cost(256, 192, 60);
-  const int BM = 256, BN = square ? 256 : 192;
+  // under three rounds of 256 x 192 tiles, 128 x 128 tiles two to a compute unit once they fill a
+  // round of pairs (measured below); otherwise the 256-row tile of fewer whole rounds
+  if (tiles_of(kW4GroupTiles[1], nullptr) < 3 * 256) {
+    const int64_t t = tiles_of(kW4GroupTiles[2], nullptr);
+    return t >= 512 && t < ((int64_t)1 << 31) ? 2 : -1;
+  }
+  int best = -1;
+  double best_cost = 0;
+  for (int t = 0; t < 2; ++t) {
+    const GroupTile& c = kW4GroupTiles[t];
+    double work = 0;
+    const int64_t tiles = tiles_of(c, &work);
+    if (tiles < 2 * (int64_t)c.per_round || tiles >= ((int64_t)1 << 31)) continue;  // 32-bit workgroup ids
+    const double cost = std::ceil(work / c.per_round - 1e-9) * c.round_us;
+    if (best < 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  return best;
+}
+template <int BM, int BN, int WPE>
+hipError_t run_w4a4_group(const DecArgs* p, int count, hipStream_t s) {
   W4Group g{};
   g.count = count;
   int64_t total = 0;
@@ -402,12 +416,26 @@ hipError_t launch_gemm_w4a4_grouped(const DecArgs* p, int count, hipStream_t s) 
     total += ((p[i].M + BM - 1) / BM) * ((p[i].N + BN - 1) / BN);
   }
   for (int i = count; i <= kMaxGroup; ++i) g.start[i] = (int)total;
-  if (square)
-    hipLaunchKernelGGL((gemm_w4a4_grouped_kernel<256, 256>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_w4a4_grouped_kernel<256, 192>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((gemm_w4a4_grouped_kernel<BM, BN, WPE>), dim3((unsigned)total), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
+}  // namespace
+
+bool gemm_w4a4_grouped_supported(const DecArgs* p, int count) {
+  if (count < 2 || count > kMaxGroup) return false;
+  for (int i = 0; i < count; ++i)
+    if (p[i].K % kStageK != 0 || p[i].lt || p[i].yq || p[i].ypmax || !p[i].y) return false;
+  return w4a4_group_tile(p, count) >= 0;
+}
+
+hipError_t launch_gemm_w4a4_grouped(const DecArgs* p, int count, hipStream_t s) {
+  switch (w4a4_group_tile(p, count)) {
+    case 0: return run_w4a4_group<256, 256, 1>(p, count, s);
+    case 1: return run_w4a4_group<256, 192, 1>(p, count, s);
+    default: return run_w4a4_group<128, 128, 2>(p, count, s);
+  }
+}
+
 bool lora_pre_scaled_w4a4(const DecArgs& a) { return gemm_w4a4_supported(a); }
 
 hipError_t launch_gemm_w4a4(const DecArgs& args, hipStream_t s) {

@@ -101,7 +101,8 @@ def _check_group(fmt, probs, xbs, sample=12, seed=0, exact=None):
 
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
 def test_grouped_kernel_mixed_shapes(fmt):
-    """592 tiles of 256 x 192 in all (the grouped kernel), ragged M and N, the longest K last."""
+    """A grouped tiled grid (592 tiles of 256 x 192: 128 x 128 tiles two to a compute unit), ragged
+    M and N, the longest K last."""
     M = 4000
     xb1, x1 = _acts(fmt, M, 1024, 0)
     xb2, x2 = _acts(fmt, M, 2048, 1)
@@ -137,11 +138,14 @@ def test_grouped_fallback_paths(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
-def test_grouped_joint_block_16384(fmt):
-    """The joint block's four linears at 16384 tokens in one launch, as the benchmark times them."""
+@pytest.mark.parametrize("M", [syn.JOINT_TOKENS, 2048, 600])
+def test_grouped_joint_block(fmt, M):
+    """The joint block's four linears in one launch, as the benchmark times them: at 16384 tokens
+    on 256 x 256 tiles, at 2048 on 256 x 192 tiles, at 600 (ragged) on 128 x 128 tiles two to a
+    compute unit."""
     block = 0 if fmt == "nvfp4" else 1
-    xb_a, xa = _acts(fmt, syn.JOINT_TOKENS, 3072, 0)
-    xb_b, xb = _acts(fmt, syn.JOINT_TOKENS, 12288, 1)
+    xb_a, xa = _acts(fmt, M, 3072, 0)
+    xb_b, xb = _acts(fmt, M, 12288, 1)
     probs, xbs = [], []
     for gi, (name, N, K) in enumerate(syn.JOINT_GEMMS):
         probs.append(_problem(fmt, xa if K == 3072 else xb, _weights(fmt, N, K, block * 4 + gi)))

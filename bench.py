@@ -505,9 +505,9 @@ def small_m_sweep(L, syn, dev, Ms=(16, 32, 64, 128, 256, 512), Ns=(N_FP8, N_FP4)
 def block_launches(L, syn, dev, Ms=(1, 16, 32, 512, 2048)):
     """A joint block's four linears (qkv 9216x3072, proj 3072x3072, up 12288x3072, down 3072x12288) with
     cold weights: four launches back to back against one grouped launch (bsq_gemm_grouped_q), per
-    scheme and token count. At 1, 16 and 32 tokens the group runs as one grid of the few-token kernels;
-    at 512 tokens (under two rounds of large tiles) as one launch per problem, so both columns
-    time the same kernels; at 2048 tokens as one grid of the tiled kernels.
+    scheme and token count. At 1, 16 and 32 tokens the group runs as one grid of the few-token kernels,
+    at 512 tokens as one grid of 128 x 128 tiles two to a compute unit, at 2048 tokens as one grid of
+    256 x 192 tiles.
 
     The block's weights are copied until the copies exceed 600 MB and the timed calls rotate over
     them, so that no call finds its weights in the 256 MB Infinity Cache; activations are

@@ -365,9 +365,12 @@ hipError_t run(const DecArgs& a, hipStream_t s) {
 bool gemm_w4a4_supported(const DecArgs& a) { return a.K % kStageK == 0; }
 
 // Grouped W4A4: every problem with K % 256 == 0 and plain bf16 output (no adapter, no quantized
-// output). The tile rule and its measurements are those of the grouped fp8r launch: 128 x 128
-// tiles two to a compute unit below three rounds of 256 x 192 tiles (from one round of pairs),
-// else the 256 x 256 or 256 x 192 tile of least expected time over whole rounds.
+// output). The tile rule and its measurements are those of the grouped fp8r launch (128 x 128
+// tiles two to a compute unit below three rounds of 256 x 192 tiles, else the 256 x 256 or
+// 256 x 192 tile of least expected time over whole rounds), except that the decode-heavier W4A4
+// tile already pays from 256 pair tiles (half a round): a joint block at 192 / 256 / 320 tokens
+// as one grid 91.3 / 91.1 / 94.2 us against four launches 99.2 / 106.0 / 121.3 us, where the fp8r
+// block lost (93.3 / 100.9 / 91.8 vs 76.6 / 83.3 / 86.7 us) and keeps the full round.
 namespace {
 struct GroupTile {
   int bm, bn, per_round, round_us;
@@ -390,7 +393,7 @@ int w4a4_group_tile(const DecArgs* p, int count) {
   // round of pairs (measured below); otherwise the 256-row tile of fewer whole rounds
   if (tiles_of(kW4GroupTiles[1], nullptr) < 3 * 256) {
     const int64_t t = tiles_of(kW4GroupTiles[2], nullptr);
-    return t >= 512 && t < ((int64_t)1 << 31) ? 2 : -1;
+    return t >= 256 && t < ((int64_t)1 << 31) ? 2 : -1;  // half a round of pairs already pays
   }
   int best = -1;
   double best_cost = 0;

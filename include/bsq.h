@@ -203,8 +203,9 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
  * between launches, and each launch's fixed cost is paid once:
  *  - problems that alone would run on the tiled kernels (several hundred
  *    tokens and more) share one grid of them when the group fills the 256
- *    compute units (at least one round of 128 x 128 tiles two to a unit, or
- *    two rounds of 256 x 192 / 256 x 256 tiles); each y is
+ *    compute units (at least one round of 128 x 128 tiles two to a unit --
+ *    half a round for nvfp4 -- or two rounds of 256 x 192 / 256 x 256
+ *    tiles); each y is
  *    then, bit for bit, what bsq_gemm_fp8r_q (format BSQ_FMT_FP8R) or
  *    bsq_gemm_nvfp4_q (BSQ_FMT_NVFP4) returns for its operands;
  *  - a group of at most 64 tokens in which some problem alone would take the

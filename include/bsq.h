@@ -209,14 +209,16 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
  *    then, bit for bit, what bsq_gemm_fp8r_q (format BSQ_FMT_FP8R) or
  *    bsq_gemm_nvfp4_q (BSQ_FMT_NVFP4) returns for its operands;
  *  - a group of at most 64 tokens in which some problem alone would take the
- *    few-token kernels runs as one grid of the few-token kernels: the y of a
- *    problem that alone takes them is bit for bit the single call's, the y of
- *    one that alone would take the tiled kernels is the few-token kernels'
- *    result (the same products, summed over K in another order: within the
- *    GEMM tolerance of the single call's, and deterministic);
+ *    few-token kernels runs as one grid of the few-token kernels, with one
+ *    workgroup shape (waves splitting K, activation blocks) for the whole
+ *    group: each y holds the same products summed over K in that shape's
+ *    order -- bit for bit the single call's where the single call runs the
+ *    same shape on the few-token kernels, otherwise (another shape, or the
+ *    tiled kernels alone) within the GEMM tolerance of it;
  *  - anything else (fp8r with K % 128 != 0, nvfp4 with K % 256 != 0, fewer
  *    tiles, 65 or more tokens on mixed routes) runs one launch per problem,
  *    in the order given, with the single calls' results.
+ * Every grouped call is deterministic: the same group gives the same bits.
  *   problems : host array of `count` descriptors (read during the call only);
  *              count 0 is a no-op, 1 <= count <= BSQ_MAX_GROUP otherwise
  *   per problem, with the layouts and alignment of the two entry points:

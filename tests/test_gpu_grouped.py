@@ -1,10 +1,12 @@
 """GPU parity of the grouped launch (bsq_gemm_grouped_q).
 
-Every problem that keeps its own route in a group must come out bit for bit as
+On the tiled kernels every problem of a group must come out bit for bit as
 the single pre-quantized entry point (bsq_gemm_fp8r_q / bsq_gemm_nvfp4_q)
 computes it -- the grouped kernels run the same tile code, only the workgroup
--> (problem, tile) mapping differs; a problem that a group of at most 64 tokens
-moves onto the few-token kernels is checked against the oracle only. Every
+-> (problem, tile) mapping differs. On the few-token kernels bit equality is
+asserted only for problems whose single call runs the group's workgroup shape
+(waves splitting K, activation blocks per workgroup); the others sum the same
+products in another order and are held to the oracle's tolerance. Every
 grouped call must repeat its own bits, and sampled rows of every problem must
 match the oracle's fp64 product within the GEMM tolerance. Groups cover the
 grouped tiled kernels (ragged M and N, mixed K, longest K not first), every
@@ -158,29 +160,41 @@ def test_grouped_joint_block(fmt, M):
 @pytest.mark.parametrize("M", [1, 16, 48])
 def test_grouped_few_tokens_joint_block(fmt, M):
     """The joint block's four linears for a few tokens as one grid of the few-token kernels (a
-    workgroup per 32 weight rows). At 48 tokens qkv and up alone would take the tiled kernels, so
-    only proj and down must match their single calls bit for bit."""
+    workgroup per 32 weight rows). The group's workgroups split K over eight waves (nvfp4) or
+    four (fp8r; eight at one token, and two activation blocks a workgroup at 48 tokens); alone,
+    qkv and up (grids of 256 or more weight blocks) take four waves at 16 tokens (nvfp4) and at
+    one token (fp8r), and the tiled kernels at 48 tokens, and fp8r's proj and down one block a
+    workgroup at 48 tokens. Bit equality is asserted where the shapes agree."""
     xb_a, xa = _acts(fmt, M, 3072, 6)
     xb_b, xb = _acts(fmt, M, 12288, 7)
     probs, xbs = [], []
     for gi, (name, N, K) in enumerate(syn.JOINT_GEMMS):
         probs.append(_problem(fmt, xa if K == 3072 else xb, _weights(fmt, N, K, 50 + gi)))
         xbs.append(xb_a if K == 3072 else xb_b)
-    _check_group(fmt, probs, xbs, sample=min(M, 6), exact=None if M <= 16 else (1, 3))
+    exact = {("nvfp4", 1): None, ("nvfp4", 16): (1, 3), ("nvfp4", 48): (1, 3),
+             ("fp8r", 1): (1, 3), ("fp8r", 16): None, ("fp8r", 48): ()}[(fmt, M)]
+    _check_group(fmt, probs, xbs, sample=min(M, 6), exact=exact)
 
 
 @pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+# `exact`, per scheme: the problems whose single call runs the group's workgroup shape (waves and
+# activation blocks per workgroup), so that their bits must match; None = all of them
 @pytest.mark.parametrize("M,shapes,exact", [
-    (100, [(4096, 1024), (2048, 1024), (3072, 2048), (2000, 1024)], None),  # two activation blocks a workgroup
-    (4, [(1024, 1024), (512, 1024), (2048, 1024)], None),                   # a handful of tokens, small grid
-    (40, [(3072, 3072), (12288, 3072)], (0,)),    # alone, N = 12288 would take the tiled kernels
-    (80, [(3072, 3072), (12288, 3072)], None),    # the same past 64 tokens: one launch per problem
+    # two activation blocks a workgroup; alone, fp8r's smaller grids take one block a workgroup
+    (100, [(4096, 1024), (2048, 1024), (3072, 2048), (2000, 1024)], {"nvfp4": None, "fp8r": (0,)}),
+    # a handful of tokens on a small grid (eight waves a workgroup for both schemes)
+    (4, [(1024, 1024), (512, 1024), (2048, 1024)], {"nvfp4": None, "fp8r": None}),
+    # alone, N = 12288 would take the tiled kernels, and fp8r's N = 3072 one block a workgroup
+    (40, [(3072, 3072), (12288, 3072)], {"nvfp4": (0,), "fp8r": ()}),
+    # the same past 64 tokens: one launch per problem
+    (80, [(3072, 3072), (12288, 3072)], {"nvfp4": None, "fp8r": None}),
 ])
 def test_grouped_few_token_variants(fmt, M, shapes, exact):
     """Few-token groups on each workgroup variant the grouped launch picks, ragged N included, and
     groups whose problems alone take different routes: up to 64 tokens all of them run on the
-    few-token kernels (bit for bit the single call where that is the problem's own route, within
+    few-token kernels (bit for bit the single call where it runs the same workgroup shape, within
     the tolerance of the oracle everywhere), beyond that one launch per problem."""
+    exact = exact[fmt]
     xbs, probs, acts = [], [], {}
     for b, (N, K) in enumerate(shapes):
         if K not in acts:

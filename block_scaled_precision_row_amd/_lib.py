@@ -36,6 +36,12 @@ class GemmProblem(ctypes.Structure):
                 ("y", _p), ("ldy", _i64), ("M", _i64), ("N", _i64), ("K", _i64)]
 
 
+class WeightOnlyProblem(ctypes.Structure):
+    """bsq_weight_only_problem: one weight-only linear of a grouped launch (device pointers as integers)."""
+    _fields_ = [("x", _p), ("ldx", _i64), ("w", _p), ("w_scale", _p), ("w_scale2", _p), ("y", _p), ("ldy", _i64),
+                ("M", _i64), ("N", _i64), ("K", _i64)]
+
+
 # symbol -> (restype, argtypes); mirrors include/bsq.h
 SIGNATURES = {
     "bsq_abi_version": (_int, []),
@@ -53,6 +59,7 @@ SIGNATURES = {
     "bsq_gemm_fp8r_q": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "bsq_gemm_nvfp4_q": (_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p]),
     "bsq_gemm_grouped_q": (_int, [_int, ctypes.POINTER(GemmProblem), _int, _p]),
+    "bsq_gemm_grouped_weight_only": (_int, [_int, ctypes.POINTER(WeightOnlyProblem), _int, _p]),
     "bsq_gemm_nvfp4_quantize_y_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "bsq_gemm_nvfp4_q_quantize_y": (_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _sz,
                                            _p]),
@@ -373,6 +380,41 @@ def bsq_gemm_grouped_q(fmt, problems, ys=None):
                              ws.data_ptr(), None if gw is None else gw.data_ptr(), y.data_ptr(), ldy, M, N, K)
         out.append(y)
     _check("bsq_gemm_grouped_q", lib.bsq_gemm_grouped_q(fmt, arr, len(problems), _stream()))
+    return out
+
+
+def bsq_gemm_grouped_weight_only(fmt, problems, ys=None):
+    """Several weight-only linears (bf16 activations) of one scheme in one launch
+    (bsq_gemm_grouped_weight_only). fmt BSQ_FMT_FP8R: each problem is (x [M, K] bf16, w [N, K] E4M3,
+    w_scale [N] fp32); fmt BSQ_FMT_NVFP4: (x, w [N, K/2] packed E2M1, w_bscale [N, K/16] E4M3,
+    w_scale2 [1]). Returns the bf16 outputs [M, N]."""
+    if fmt not in (BSQ_FMT_FP8R, BSQ_FMT_NVFP4):
+        raise ValueError("fmt must be BSQ_FMT_FP8R or BSQ_FMT_NVFP4")
+    if len(problems) > BSQ_MAX_GROUP:
+        raise ValueError("at most %d problems per group" % BSQ_MAX_GROUP)
+    arr = (WeightOnlyProblem * max(len(problems), 1))()
+    out = []
+    for i, p in enumerate(problems):
+        x = p[0]
+        M, K, ldx = _rows(x, torch.bfloat16, "x")
+        if fmt == BSQ_FMT_FP8R:
+            _, w, ws = p
+            N = w.shape[0]
+            _dense(w, torch.uint8, (N, K), "w")
+            _dense(ws, torch.float32, (N,), "w_scale")
+            g2 = None
+        else:
+            _, w, ws, g2 = p
+            N = w.shape[0]
+            _dense(w, torch.uint8, (N, K // 2), "w")
+            _dense(ws, torch.uint8, (N, K // 16), "w_bscale")
+            _scalar(g2, "w_scale2")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if ys is None else ys[i]
+        _, _, ldy = _rows(y, torch.bfloat16, "y")
+        arr[i] = WeightOnlyProblem(x.data_ptr(), ldx, w.data_ptr(), ws.data_ptr(),
+                                   None if g2 is None else g2.data_ptr(), y.data_ptr(), ldy, M, N, K)
+        out.append(y)
+    _check("bsq_gemm_grouped_weight_only", lib.bsq_gemm_grouped_weight_only(fmt, arr, len(problems), _stream()))
     return out
 
 

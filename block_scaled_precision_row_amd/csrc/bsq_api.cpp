@@ -356,6 +356,57 @@ bsq_status bsq_gemm_nvfp4_q(const uint8_t* xq, const uint8_t* x_bscale, const fl
 
 static_assert(BSQ_MAX_GROUP == bsq::kMaxGroup, "the header states the group limit");
 
+bsq_status bsq_gemm_grouped_weight_only(bsq_format format, const bsq_weight_only_problem* problems, int count,
+                                        hipStream_t stream) {
+  if (format != BSQ_FMT_FP8R && format != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;
+  if (count < 0 || count > BSQ_MAX_GROUP) return BSQ_ERR_ARG;
+  if (count == 0) return BSQ_OK;
+  if (!problems) return BSQ_ERR_NULL;
+  const bool fp8 = format == BSQ_FMT_FP8R;
+  // every problem is checked (as the single weight-only calls check it) before anything is enqueued
+  int order[BSQ_MAX_GROUP], n = 0;
+  for (int i = 0; i < count; ++i) {
+    const bsq_weight_only_problem& p = problems[i];
+    if (fp8 && p.w_scale2) return BSQ_ERR_ARG;
+    bsq_status st = check_gemm_common(p.x, p.ldx, p.w, p.y, p.ldy, p.M, p.N, p.K, BSQ_WEIGHT_ONLY);
+    if (st != BSQ_OK) return st;
+    if (p.M == 0 || p.N == 0) continue;
+    if (!p.w_scale || (!fp8 && !p.w_scale2)) return BSQ_ERR_NULL;
+    if (!aligned(p.w_scale, 4) || (p.w_scale2 && !aligned(p.w_scale2, 4))) return BSQ_ERR_ALIGN;
+    order[n++] = i;
+  }
+  if (n == 0) return BSQ_OK;
+  bsq_status st = check_device();
+  if (st != BSQ_OK) return st;
+  for (int i = 1; i < n; ++i)  // longest K first (stable)
+    for (int j = i; j > 0 && problems[order[j]].K > problems[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
+  const bsq::DecMode mode = fp8 ? bsq::kW8A16 : bsq::kW4A16;
+  auto args = [&](const bsq_weight_only_problem& p) {
+    bsq::DecArgs a{};
+    a.x = p.x; a.ldx = p.ldx; a.w = p.w; a.y = p.y; a.ldy = p.ldy; a.M = p.M; a.N = p.N; a.K = p.K;
+    if (fp8) {
+      a.sw = static_cast<const float*>(p.w_scale);
+    } else {
+      a.ws = static_cast<const uint8_t*>(p.w_scale); a.gw = p.w_scale2;
+    }
+    return a;
+  };
+  bsq::DecArgs q[BSQ_MAX_GROUP];
+  int few = 0;
+  for (int i = 0; i < n; ++i) {
+    q[i] = args(problems[order[i]]);
+    few += route_skinny(mode, q[i]) ? 1 : 0;
+  }
+  hipError_t e = hipSuccess;
+  if (few == n && bsq::gemm_skinny_grouped_supported(mode, q, n)) {
+    e = bsq::launch_gemm_skinny_grouped(mode, q, n, stream);
+  } else {
+    for (int i = 0; i < count && e == hipSuccess; ++i)
+      if (problems[i].M > 0 && problems[i].N > 0) e = launch_dec_or_skinny(mode, args(problems[i]), stream);
+  }
+  return e == hipSuccess ? BSQ_OK : hip_fail(e);
+}
+
 bsq_status bsq_gemm_grouped_q(bsq_format format, const bsq_gemm_problem* problems, int count, hipStream_t stream) {
   if (format != BSQ_FMT_FP8R && format != BSQ_FMT_NVFP4) return BSQ_ERR_ARG;
   if (count < 0 || count > BSQ_MAX_GROUP) return BSQ_ERR_ARG;

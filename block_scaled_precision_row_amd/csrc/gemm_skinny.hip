@@ -735,7 +735,7 @@ hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s) {
   }
 }
 
-// Grouped few-token launch (W4A4, W8A8; no adapter): one grid over every problem's workgroups,
+// Grouped few-token launch (any scheme; no adapter): one grid over every problem's workgroups,
 // the variant (activation blocks and waves per workgroup) picked for the whole group from the
 // largest token count and the group's total grid. A group's grid holds several problems' worth
 // of workgroups, which favours more waves per workgroup than one launch of the same token count
@@ -743,7 +743,7 @@ hipError_t launch_gemm_skinny(DecMode mode, const DecArgs& a, hipStream_t s) {
 // took 34.5 us as one grid of four-wave W4A4 workgroups and 27.0 us with eight waves; W8A8 took
 // 27.9 us with four waves and 30.0 us with eight, but 25.8 -> 24.8 us with eight at one token.
 bool gemm_skinny_grouped_supported(DecMode mode, const DecArgs* p, int count) {
-  if ((mode != kW4A4 && mode != kW8A8) || count < 2 || count > kMaxGroup) return false;
+  if (count < 2 || count > kMaxGroup) return false;
   int64_t blocks = 0;  // at one activation block a workgroup, the most the grid can hold
   for (int i = 0; i < count; ++i) {
     if (p[i].lt || p[i].yq || p[i].ypmax || !p[i].y || !gemm_skinny_supported(mode, p[i])) return false;
@@ -779,6 +779,10 @@ hipError_t launch_gemm_skinny_grouped(DecMode mode, const DecArgs* p, int count,
     mmax = p[i].M > mmax ? p[i].M : mmax;
     grid64 += ((p[i].N + 31) / 32) * ((p[i].M + 63) / 64);
   }
+  // weight-only linears: one activation block a workgroup, eight waves (W4A16) or four (W8A16),
+  // the shapes one launch of a short grid takes
+  if (mode == kW4A16) return run_grouped<kW4A16, 1, kSkStagedWaves, true>(p, count, s);
+  if (mode == kW8A16) return run_grouped<kW8A16, 1, 4, false>(p, count, s);
   if (mode == kW4A4) {
     if (mmax > 64) return run_grouped<kW4A4, 2, kSkStagedWaves, true>(p, count, s);
     return run_grouped<kW4A4, 1, kSkStagedWaves, true>(p, count, s);

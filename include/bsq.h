@@ -249,6 +249,40 @@ typedef struct {
 bsq_status bsq_gemm_grouped_q(bsq_format format, const bsq_gemm_problem* problems, int count, hipStream_t stream);
 
 /*
+ * Grouped launch of weight-only linears (BSQ_WEIGHT_ONLY: bf16 activations
+ * times the dequantized weights, the fallback's arithmetic of the "BFL (fp8r /
+ * nvfp4)" page, last paragraph of "Kernels"). Problem i's y is what
+ * bsq_gemm_fp8r (format BSQ_FMT_FP8R) or bsq_gemm_nvfp4 (BSQ_FMT_NVFP4) with
+ * BSQ_WEIGHT_ONLY returns for it. A group whose problems all take the
+ * few-token route alone runs as one grid of the few-token kernels, with one
+ * workgroup shape for the group (bit for bit the single call's where that call
+ * runs the same shape, otherwise within the GEMM tolerance of it); any other
+ * group runs one launch per problem, in the order given, with the single
+ * calls' results. Deterministic.
+ *   problems : host array of `count` descriptors (read during the call only);
+ *              count 0 is a no-op, 1 <= count <= BSQ_MAX_GROUP otherwise
+ *   per problem: x [M][ldx] bf16 (ldx >= K, ldx % 8 == 0); w, w_scale as
+ *     bsq_gemm_fp8r (E4M3 [N][K], fp32 [N]; w_scale2 NULL) or bsq_gemm_nvfp4
+ *     (packed E2M1 [N][K/2], E4M3 [N][K/16], w_scale2 [1] fp32); y [M][ldy];
+ *     problems with M == 0 or N == 0 are skipped.
+ * Errors: BSQ_ERR_ARG for an unknown format, count < 0 or count >
+ * BSQ_MAX_GROUP, or a non-NULL w_scale2 with fp8r; otherwise the statuses of
+ * the two entry points. Every problem is validated before anything is enqueued.
+ */
+typedef struct {
+  const uint16_t* x;
+  int64_t ldx;
+  const uint8_t* w;
+  const void* w_scale;
+  const float* w_scale2;
+  uint16_t* y;
+  int64_t ldy;
+  int64_t M, N, K;
+} bsq_weight_only_problem;
+bsq_status bsq_gemm_grouped_weight_only(bsq_format format, const bsq_weight_only_problem* problems, int count,
+                                        hipStream_t stream);
+
+/*
  * W4A4 linear whose output is also handed to the next quantized linear in
  * nvfp4 ("BFL (fp8r / nvfp4)": every quantized linear quantizes its input at
  * run time; here the producing GEMM does it in its epilogue, where the

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound():
     syms = declared_symbols()
-    assert len(syms) == 26
+    assert len(syms) == 27
     so = ctypes.CDLL(_lib.LIB_PATH)
     for s in syms:
         assert hasattr(so, s), s
@@ -100,6 +100,37 @@ def test_grouped_validation():
         assert g(fp8, probs(f8, f8), 2, None) == DEV
     with pytest.raises(ValueError):
         _lib.bsq_gemm_grouped_q(fp8, [None] * 9)
+
+
+def test_grouped_weight_only_validation():
+    fp8, nv = _lib.BSQ_FMT_FP8R, _lib.BSQ_FMT_NVFP4
+    g = L.bsq_gemm_grouped_weight_only
+    WP = _lib.WeightOnlyProblem
+
+    def probs(*ps):
+        arr = (WP * len(ps))()
+        for i, p in enumerate(ps):
+            arr[i] = p
+        return arr
+
+    # x, ldx, w, w_scale, w_scale2, y, ldy, M, N, K
+    f8 = WP(A.value, 128, B.value, C.value, None, D.value, 64, 16, 64, 128)
+    n4 = WP(A.value, 256, B.value, C.value, D.value, A.value, 64, 16, 64, 256)
+    assert g(3, probs(f8), 1, None) == ARG                                   # format
+    assert g(fp8, probs(f8), 9, None) == ARG                                 # more than BSQ_MAX_GROUP
+    assert g(fp8, probs(f8), -1, None) == ARG
+    assert g(fp8, None, 0, None) == OK and g(fp8, None, 1, None) == NULL
+    assert g(fp8, probs(f8, WP(A.value, 128, B.value, C.value, D.value, D.value, 64, 16, 64, 128)), 2, None) == ARG
+    assert g(nv, probs(n4, WP(A.value, 256, B.value, C.value, None, A.value, 64, 16, 64, 256)), 2, None) == NULL
+    assert g(fp8, probs(f8, WP(A.value, 120, B.value, C.value, None, D.value, 64, 16, 64, 128)), 2, None) == SHAPE
+    assert g(fp8, probs(f8, WP(ODD.value, 128, B.value, C.value, None, D.value, 64, 16, 64, 128)), 2, None) == ALIGN
+    assert g(nv, probs(n4, WP(A.value, 256, B.value, ODD.value, D.value, A.value, 64, 16, 64, 256)), 2, None) == ALIGN
+    empty = WP(None, 128, None, None, None, None, 64, 0, 64, 128)  # M = 0: skipped unread
+    assert g(fp8, probs(empty, empty), 2, None) == OK
+    if not torch.cuda.is_available():
+        assert g(fp8, probs(f8, f8), 2, None) == DEV
+    with pytest.raises(ValueError):
+        _lib.bsq_gemm_grouped_weight_only(fp8, [None] * 9)
 
 
 def test_workspace_sizes():

@@ -203,3 +203,40 @@ def test_grouped_few_token_variants(fmt, M, shapes, exact):
         probs.append(_problem(fmt, x, _weights(fmt, N, K, 70 + b)))
         xbs.append(xb)
     _check_group(fmt, probs, xbs, sample=min(M, 6), exact=exact)
+
+
+@pytest.mark.parametrize("fmt", ["fp8r", "nvfp4"])
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_grouped_weight_only_joint_block(fmt, M):
+    """Weight-only linears (bf16 activations, the fallback's arithmetic) grouped: the joint block's
+    four linears. At 1 and 16 tokens every problem is on the few-token route and the group runs as
+    one grid of eight-wave (nvfp4) or four-wave (fp8r) workgroups, the shape proj and down take
+    alone (qkv and up, with grids of 256 or more weight blocks, take four or two waves alone); at
+    40 tokens qkv and up alone take the tiled kernels, so the group runs one launch per problem."""
+    xs = {K: syn.activations(syn.JOINT_4MP, M, K, block=8 + (K > 3072)) for K in (3072, 12288)}
+    xd = {K: dev_bf16(v) for K, v in xs.items()}
+    probs, host_w = [], []
+    for gi, (name, N, K) in enumerate(syn.JOINT_GEMMS):
+        w = _weights(fmt, N, K, 80 + gi)
+        probs.append((xd[K],) + tuple(w))
+        host_w.append(tuple(host(t) for t in w))
+    ys = L.bsq_gemm_grouped_weight_only(_fmt(fmt), probs)
+    again = L.bsq_gemm_grouped_weight_only(_fmt(fmt), probs)
+    if fmt == "fp8r":
+        singles = [L.bsq_gemm_fp8r(p[0], p[1], p[2], flags=L.BSQ_WEIGHT_ONLY) for p in probs]
+    else:
+        singles = [L.bsq_gemm_nvfp4(p[0], p[1], p[2], p[3], None, flags=L.BSQ_WEIGHT_ONLY) for p in probs]
+    torch.cuda.synchronize()
+    exact = None if M == 40 else (1, 3)
+    rng = np.random.default_rng(M)
+    for i, (name, N, K) in enumerate(syn.JOINT_GEMMS):
+        yb = host(ys[i])
+        assert np.array_equal(yb, host(again[i])), "problem %d: two grouped calls differ" % i
+        if exact is None or i in exact:
+            assert np.array_equal(yb, host(singles[i])), "problem %d differs from its single launch" % i
+        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 6), replace=False)]))
+        if fmt == "fp8r":
+            ref = gemm.gemm_fp8r_weight_only(xs[K][rows], host_w[i][0], host_w[i][1])
+        else:
+            ref = gemm.gemm_nvfp4_weight_only(xs[K][rows], host_w[i][0], host_w[i][1], np.float32(host_w[i][2][0]))
+        assert_gemm_close(yb[rows], ref, "%s weight-only grouped problem %d" % (fmt, i))

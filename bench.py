@@ -539,7 +539,7 @@ def block_launches(L, syn, dev, Ms=(1, 16, 32, 512, 2048)):
         return e0.elapsed_time(e1) / iters * 1e3  # us per block
 
     gemms = syn.JOINT_GEMMS
-    out = {"gemms": [{"gemm": n, "N": N, "K": K} for n, N, K in gemms], "rows": []}
+    out = {"gemms": [{"gemm": n, "N": N, "K": K} for n, N, K in gemms], "rows": [], "weight_only_rows": []}
     for scheme in ("nvfp4", "fp8r"):
         block = []
         for gi, (name, N, K) in enumerate(gemms):
@@ -594,11 +594,42 @@ def block_launches(L, syn, dev, Ms=(1, 16, 32, 512, 2048)):
             log("joint block %s M=%d: four launches %.1f us, one grouped launch %.1f us" %
                 (scheme, Mi, us_four, us_grouped))
             del ys, singles, groups
+        # the same weights as weight-only linears (bf16 activations): bsq_gemm_grouped_weight_only
+        for Mi in (1, 16):
+            xb = {K: up_bf16(syn.activations(syn.JOINT_4MP, Mi, K, block=0 if K == 3072 else 1))
+                  for K in sorted({K for _, _, K in gemms})}
+            ys = [torch.empty((Mi, N), dtype=torch.bfloat16, device=dev) for _, N, _ in gemms]
+            singles, groups = [], []
+            fmt = L.BSQ_FMT_NVFP4 if scheme == "nvfp4" else L.BSQ_FMT_FP8R
+            for cp in copies:
+                probs = (L.WeightOnlyProblem * len(gemms))()
+                one = []
+                for gi, (name, N, K) in enumerate(gemms):
+                    x, w, y = xb[K], cp[gi], ys[gi]
+                    if scheme == "nvfp4":
+                        probs[gi] = L.WeightOnlyProblem(P(x), K, P(w[0]), P(w[1]), P(w[2]), P(y), N, Mi, N, K)
+                        one.append(lambda x=x, w=w, y=y, N=N, K=K: check(lib.bsq_gemm_nvfp4(
+                            P(x), K, P(w[0]), P(w[1]), P(w[2]), None, P(y), N, Mi, N, K, L.BSQ_WEIGHT_ONLY, None, 0,
+                            stream)))
+                    else:
+                        probs[gi] = L.WeightOnlyProblem(P(x), K, P(w[0]), P(w[1]), None, P(y), N, Mi, N, K)
+                        one.append(lambda x=x, w=w, y=y, N=N, K=K: check(lib.bsq_gemm_fp8r(
+                            P(x), K, P(w[0]), P(w[1]), P(y), N, Mi, N, K, L.BSQ_WEIGHT_ONLY, None, 0, stream)))
+                singles.append(lambda one=one: [c() for c in one])
+                groups.append(lambda probs=probs, fmt=fmt: check(lib.bsq_gemm_grouped_weight_only(
+                    fmt, probs, len(gemms), stream)))
+            us_four, us_grouped = timed(singles), timed(groups)
+            out["weight_only_rows"].append({"scheme": scheme, "M": Mi, "four_launches_us": round(us_four, 2),
+                                            "grouped_us": round(us_grouped, 2)})
+            log("weight-only joint block %s M=%d: four launches %.1f us, one grouped launch %.1f us" %
+                (scheme, Mi, us_four, us_grouped))
+            del ys, singles, groups
         del copies, block
         torch.cuda.empty_cache()
     out["note"] = ("us per block (the four GEMMs) from events around 24 back-to-back blocks rotated over > 600 MB of "
                    "weight copies (cold weights), queued behind other GPU work; hbm_frac = (weights + activations + "
-                   "Y bytes) / time / 8 TB/s")
+                   "Y bytes) / time / 8 TB/s; weight_only_rows: the same weights as weight-only linears (bf16 "
+                   "activations, bsq_gemm_grouped_weight_only)")
     return out
 
 
